@@ -13,7 +13,9 @@ Readings (the design notes list them):
   added in K order with float32 round-to-nearest-even ('sequential'). For B=32 a group
   has two blocks and this equals one rounding of the exact group sum. The alternative
   reading, one rounding of the exact 64-product sum, is available as reading='single'.
-- The first group initialises the accumulator; canonicalisation, when enabled, acts on
+- An exact zero block partial is +0. The first group initialises the accumulator
+  (equivalently: the accumulator starts at +0 and every group is added toward zero, since
+  +0 + G = G exactly and x + (-x) = +0 under round-toward-zero); canonicalisation, when enabled, acts on
   the accumulator before the output scale; the output scale is
   alpha = float32(g_a * g_b) [times 1/n for Hadamard-rotated weight-gradient operands],
   and y = float32(acc * alpha).
@@ -126,7 +128,7 @@ def gemm_model(qa: np.ndarray, sa: np.ndarray, qb: np.ndarray, sb: np.ndarray, b
             ks = slice(b * block, (b + 1) * block)
             I = qa[:, ks] @ qb[:, ks].T          # multiples of 1/4, |I| <= 36*block: exact
             Tb = I * sa[:, b][:, None] * sb[:, b][None, :]   # exact (<= 21 significant bits)
-            T.append(Tb)
+            T.append(Tb + 0.0)        # an exact zero partial is +0 (no signed zero from the BLAS order)
         if reading == "sequential":
             for Tb in T:
                 if not _f32_exact(Tb):

@@ -111,22 +111,25 @@ def sr_e2m1(r: np.ndarray, u16: np.ndarray) -> np.ndarray:
     return (mag | (np.signbit(r).astype(np.int64) << 3)).astype(np.uint8)
 
 
-def _payload(xb: np.ndarray, mult: np.ndarray, rounding: str, seed: int, offset: int, K: int) -> np.ndarray:
-    """Quantize block-shaped values xb [R, nb, B] with per-block multipliers [R, nb]."""
+def _payload(xb: np.ndarray, mult: np.ndarray, rounding: str, seed: int, offset: int, K: int,
+             row0: int = 0) -> np.ndarray:
+    """Quantize block-shaped values xb [R, nb, B] with per-block multipliers [R, nb].
+    ``row0``: logical row of xb[0] in the full operand (stochastic-rounding index base)."""
     r = (xb * mult[..., None]).astype(np.float32)     # float32 multiply, RNE
     R, nb, B = xb.shape
     if rounding == "rne":
         return F.encode_e2m1(r).reshape(R, nb * B)
     if rounding == "sr":
-        idx = np.arange(R * K, dtype=np.uint64)
+        idx = np.arange(R * K, dtype=np.uint64) + np.uint64(row0 * K)
         u = sr_uniform16(seed, offset, idx).reshape(R, nb, B)
         return sr_e2m1(r, u).reshape(R, nb * B)
     raise ValueError(rounding)
 
 
 def quantize_1d(x: np.ndarray, fmt: int, block: int, amax=None, T: float = 448.0,
-                rounding: str = "rne", seed: int = 0, offset: int = 0) -> QuantResult:
-    """Quantize x [rows, K] with 1D blocks of ``block`` consecutive elements along K."""
+                rounding: str = "rne", seed: int = 0, offset: int = 0, row0: int = 0) -> QuantResult:
+    """Quantize x [rows, K] with 1D blocks of ``block`` consecutive elements along K.
+    ``row0`` is the logical row of x[0] when x is a row slice of a larger operand."""
     x = np.asarray(x, dtype=np.float32)
     R, K = x.shape
     if K % block:
@@ -137,11 +140,11 @@ def quantize_1d(x: np.ndarray, fmt: int, block: int, amax=None, T: float = 448.0
     amax_b = np.max(np.abs(xb), axis=2)
     if fmt == F.E8M0:
         codes, mult = e8m0_block(amax_b)
-        q = _payload(xb, mult, rounding, seed, offset, K)
+        q = _payload(xb, mult, rounding, seed, offset, K, row0)
         return QuantResult(q, codes, np.float32(1.0), fmt, block)
     s_enc, s_blk, g = tensor_scales(amax, T)
     codes, mult, n_sat, n_zero = _block_scales(amax_b, s_enc, s_blk, fmt)
-    q = _payload(xb, mult, rounding, seed, offset, K)
+    q = _payload(xb, mult, rounding, seed, offset, K, row0)
     return QuantResult(q, codes, g, fmt, block, n_sat, n_zero)
 
 
