@@ -1,0 +1,229 @@
+"""Benchmark of the block-scaled FP4 hot path on one MI355X.
+
+One step = one full FP4 training pass of a linear layer at the up-projection shape
+(8192 tokens, 4096 -> 14336): amax sampling on sample steps (per-operand D=50 caches),
+quantize X (row view) and W, fprop Y = X W^T, stochastic-rounded dY in the row view and
+dgrad dX = dY W, the wgrad views dY^T (T = 2048) and X^T (optionally H16-rotated) and
+wgrad dW = dY^T X. Inputs are seeded synthetic tensors already resident in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--fmt mxfp4|ue5m3|e4m3] [--hadamard 0|16|32]
+
+Prints one JSON line. ``value`` = FP4 GEMM FLOPs of the step / step wall time (TFLOP/s);
+``roofline`` is the fprop GEMM kernel's achieved FLOP rate (HIP events around each
+launch on the launch stream) against the FP4 MFMA peak; ``quantizer`` is the row-view
+activation quantizer's algorithmic GB/s against HBM peak; ``cpu_baseline`` times the CPU
+oracle on a bounded slice of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+M_TOK, K_IN, N_OUT = 8192, 4096, 14336
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense FP4/FP6 MFMA
+BF16_PEAK_TFLOPS = 2500.0
+HBM_PEAK_GBS = 8000.0
+METRIC = "FP4 GEMM TFLOPS + quantize GB/s at 8192x4096x14336, % of MI355X peak"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--fmt", default="mxfp4", choices=["mxfp4", "ue5m3", "e4m3"])
+    p.add_argument("--hadamard", type=int, default=0, choices=[0, 16, 32])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=32, help="output rows of the oracle GEMM sample")
+    return p.parse_args()
+
+
+class LinearStep:
+    """Buffers and per-operand amax caches of one FP4 linear layer (fprop + dgrad + wgrad)."""
+
+    def __init__(self, fp4, torch, X, W, dY, fmt_name, hadamard):
+        self.fp4, self.torch = fp4, torch
+        self.X, self.W, self.dY = X, W, dY
+        self.hn = hadamard
+        self.fmt = {"mxfp4": fp4.E8M0, "ue5m3": fp4.UE5M3, "e4m3": fp4.E4M3}[fmt_name]
+        self.block = 32 if self.fmt == fp4.E8M0 else 16
+        D = 1 if self.fmt == fp4.E4M3 else 50          # E4M3 recipe: current scaling
+        mk = lambda: fp4.AmaxCache(D)
+        self.c_x, self.c_w, self.c_dy = mk(), mk(), mk()
+        self.c_xh, self.c_dyh = (mk(), mk()) if hadamard else (self.c_x, self.c_dy)
+        self.obs = torch.empty(1, dtype=torch.float32, device="cuda")
+        dev = "cuda"
+        self.Y = torch.empty((M_TOK, N_OUT), dtype=torch.float32, device=dev)
+        self.dX = torch.empty((M_TOK, K_IN), dtype=torch.float32, device=dev)
+        self.dW = torch.empty((N_OUT, K_IN), dtype=torch.float32, device=dev)
+        self.ev = []          # (start, end) events around each fprop GEMM
+        self.evq = []         # around each activation row-view quantization
+
+    def _sample(self, cache, x, step, hn=0):
+        if self.fmt == self.fp4.E8M0:
+            return
+        if cache.needs_sample(step):
+            self.fp4.tensor_amax(x, hn, out=self.obs)
+            cache.update(step, self.obs)
+
+    def run(self, step, timed=False):
+        fp4, torch = self.fp4, self.torch
+        E8 = self.fmt == fp4.E8M0
+        B = self.block
+        # forward
+        self._sample(self.c_x, self.X, step)
+        self._sample(self.c_w, self.W, step)
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        qx = fp4.quantize(self.X, self.fmt, B, fp4.ROW, amax=self.c_x.amax, T=448)
+        if timed:
+            e1.record()
+            self.evq.append((e0, e1))
+        if E8:
+            qw = fp4.quantize(self.W, self.fmt, B, fp4.ROW)
+            qwt = fp4.quantize(self.W, self.fmt, B, fp4.COL)          # W^T, blocks along out-features
+        else:
+            qw, qwt = fp4.quantize(self.W, self.fmt, 16, fp4.TILE2D, amax=self.c_w.amax, T=448)
+        if timed:
+            g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g0.record()
+        fp4.gemm_fprop(qx, qw, out=self.Y)
+        if timed:
+            g1.record()
+            self.ev.append((g0, g1))
+        # backward: dgrad
+        self._sample(self.c_dy, self.dY, step)
+        qdy = fp4.quantize(self.dY, self.fmt, B, fp4.ROW, amax=self.c_dy.amax, T=448, stochastic=True, seed=42,
+                           offset=step * 8 + 0)
+        fp4.gemm_dgrad(qdy, qwt, out=self.dX)
+        # backward: wgrad (dY^T with T = 2048, X^T with T = 448, optional Hadamard)
+        self._sample(self.c_dyh, self.dY, step, self.hn)
+        self._sample(self.c_xh, self.X, step, self.hn)
+        qdyt = fp4.quantize(self.dY, self.fmt, B, fp4.COL, amax=self.c_dyh.amax, T=2048, stochastic=True, seed=42,
+                            offset=step * 8 + 1, hadamard_n=self.hn)
+        qxt = fp4.quantize(self.X, self.fmt, B, fp4.COL, amax=self.c_xh.amax, T=448, hadamard_n=self.hn)
+        fp4.gemm_wgrad(qdyt, qxt, hadamard_n=self.hn, out=self.dW)
+
+
+def bf16_device(torch, synth, x):
+    bits = synth.f32_to_bf16_bits(x)
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def cpu_baseline(args, fmt_name, synth):
+    """The oracle as it stands, on the host: quantize a row slice of X and W and run the
+    group-model GEMM for args.cpu_rows output rows across all 14336 columns."""
+    import oracle
+    from oracle import formats as OF
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    fmt = {"mxfp4": OF.E8M0, "ue5m3": OF.UE5M3, "e4m3": OF.E4M3}[fmt_name]
+    block = 32 if fmt == OF.E8M0 else 16
+    rows = args.cpu_rows
+    Xs = synth.student_t((rows, K_IN), 3.0, 301)
+    W = synth.normal((N_OUT, K_IN), 0.02, 303)
+    t0 = time.perf_counter()
+    qx = oracle.quantize_1d(Xs, fmt, block, amax=float(np.max(np.abs(Xs))), T=448)
+    tq = time.perf_counter() - t0
+    if fmt == OF.E8M0:
+        qw = oracle.quantize_1d(W, fmt, block)
+        a, sa = oracle.operand_from_quant(qx)
+        b, sb = oracle.operand_from_quant(qw)
+    else:
+        qw = oracle.quantize_2d(W, fmt, amax=float(np.max(np.abs(W))), T=448)
+        a, sa = oracle.operand_from_quant(qx)
+        b, sb = oracle.operand_from_quant(qw, "2d")
+    t1 = time.perf_counter()
+    oracle.gemm_model(a, sa, b, sb, block, alpha=oracle.output_scale(qx.g, qw.g))
+    tg = time.perf_counter() - t1
+    flops = 2.0 * rows * N_OUT * K_IN
+    qbytes = rows * K_IN * (2 + 0.5 + 1.0 / block)
+    return {"value": flops / tg / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"group-model GEMM of {rows} output rows x {N_OUT} x K={K_IN} ({fmt_name}), "
+                      f"{tg:.1f} s; quantizer on {rows}x{K_IN}: {qbytes / tq / 1e9:.4f} GB/s",
+            "quantizer_GBps": qbytes / tq / 1e9, "seconds": tg + tq}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build targets the single-GPU FP4 hot path; "
+              "multi-GPU runs are not supported.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import fp4_block_scaled_tensor_amd as fp4
+    fp4.library()                     # fails loudly if the HIP library is missing
+    torch.manual_seed(0)
+    # synthetic inputs: the up-projection activation (Student-t nu=3, 4 outlier channels x100),
+    # weight N(0, 0.02), upstream gradient N(0, 1e-3)
+    X = synth.student_t((M_TOK, K_IN), 3.0, 301)
+    X, _ = synth.scale_channels(X, 4, 100.0, 302)
+    Xd = bf16_device(torch, synth, X)
+    Wd = bf16_device(torch, synth, synth.normal((N_OUT, K_IN), 0.02, 303))
+    dYd = bf16_device(torch, synth, synth.normal((M_TOK, N_OUT), 1e-3, 304))
+    del X
+    step_obj = LinearStep(fp4, torch, Xd, Wd, dYd, args.fmt, args.hadamard)
+    for s in range(args.warmup):
+        step_obj.run(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s in range(args.warmup, args.warmup + args.steps):
+        step_obj.run(s, timed=True)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(stop) / args.steps
+    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in step_obj.ev]))
+    quant_ms = float(np.mean([a.elapsed_time(b) for a, b in step_obj.evq]))
+    flop_gemm = 2.0 * M_TOK * N_OUT * K_IN
+    step_flops = 3 * flop_gemm
+    value = step_flops / (ms_step * 1e-3) / 1e12
+    achieved = flop_gemm / (gemm_ms * 1e-3) / 1e12
+    bpe = 2 + 0.5 + 1.0 / step_obj.block
+    q_gbs = M_TOK * K_IN * bpe / (quant_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4-e2m1 (" + args.fmt + " scales), fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": f"FP4 linear training step 8192 tok x 4096 -> 14336 ({args.fmt}, H{args.hadamard})",
+                   "tokens": M_TOK, "in_features": K_IN, "out_features": N_OUT, "gemms_per_step": 3,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "fprop GEMM " + ("k_gemm_mx" if args.fmt == "mxfp4" else "k_gemm_dec16"),
+                     "achieved": round(achieved, 2),
+                     "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP4_PEAK_TFLOPS, 4),
+                     "traffic": None, "avg_ms": round(gemm_ms, 4),
+                     "frac_of_bf16_peak": None if args.fmt == "mxfp4" else round(achieved / BF16_PEAK_TFLOPS, 4)},
+        "quantizer": {"kernel": "k_quant_row (activation 8192x4096 bf16)", "achieved": round(q_gbs, 1),
+                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(q_gbs / HBM_PEAK_GBS, 4),
+                      "bytes_per_elem": bpe, "avg_ms": round(quant_ms, 4)},
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args, args.fmt, synth)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

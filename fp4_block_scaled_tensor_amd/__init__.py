@@ -1,0 +1,191 @@
+"""Block-scaled FP4 quantization and FP4 GEMMs for MI355X (gfx950).
+
+Python binding of libfp4bs.so (include/fp4bs.h). PyTorch provides device memory and the
+current HIP stream; every step of the path runs in the library's HIP kernels. There is no
+CPU or PyTorch fallback: importing works without the library, the first call raises if it
+is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import (FP4_UE5M3, FP4_E4M3, FP4_E8M0, FP4_VIEW_ROW, FP4_VIEW_COL, FP4_VIEW_TILE2D,
+                   FP4_SCALES_1D, FP4_SCALES_2D, FP4_SCALES_2D_T, FP4Error)
+
+UE5M3, E4M3, E8M0 = FP4_UE5M3, FP4_E4M3, FP4_E8M0
+ROW, COL, TILE2D = FP4_VIEW_ROW, FP4_VIEW_COL, FP4_VIEW_TILE2D
+
+__all__ = ["UE5M3", "E4M3", "E8M0", "ROW", "COL", "TILE2D", "QTensor", "AmaxCache", "quantize", "tensor_amax",
+           "gemm_fprop", "gemm_dgrad", "gemm_wgrad", "debug_encode", "FP4Error", "library"]
+
+
+def library() -> ctypes.CDLL:
+    return _lib.load()
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev_check(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("FP4 kernels take device tensors (the path has no CPU implementation)")
+
+
+@dataclass
+class QTensor:
+    """A quantized GEMM operand [rows x k]: packed E2M1 payload, scale codes, decode scale g."""
+    q: torch.Tensor          # uint8 [rows, k // 2]
+    s: torch.Tensor          # uint8 scale codes
+    g: torch.Tensor          # float32 [1]
+    fmt: int
+    block: int
+    layout: int              # FP4_SCALES_*
+    rows: int
+    k: int
+
+    def operand(self) -> _lib.Operand:
+        return _lib.Operand(self.q.data_ptr(), self.s.data_ptr(), self.g.data_ptr(), self.fmt, self.block,
+                            self.layout, 0, self.rows, self.k)
+
+
+def _cfg(fmt, block, view, stochastic, hadamard_n, T, seed, offset) -> _lib.QuantCfg:
+    return _lib.QuantCfg(int(fmt), int(block), int(view), int(bool(stochastic)), int(hadamard_n), float(T),
+                         int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 64 - 1))
+
+
+def quantize(x: torch.Tensor, fmt: int = UE5M3, block: int = 16, view: int = ROW, amax: torch.Tensor | None = None,
+             T: float = 448.0, stochastic: bool = False, seed: int = 0, offset: int = 0, hadamard_n: int = 0,
+             amax_obs: torch.Tensor | None = None):
+    """fp4_quantize. x: bf16 or fp32 [rows, cols] on the GPU (row stride x.stride(0)).
+
+    Returns a QTensor; for TILE2D a pair (forward operand [rows x cols], dgrad operand
+    [cols x rows]) sharing the 2D scale grid and g."""
+    lib = _lib.load()
+    _dev_check(x, amax, amax_obs)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    if x.dtype == torch.bfloat16:
+        dt = _lib.FP4_IN_BF16
+    elif x.dtype == torch.float32:
+        dt = _lib.FP4_IN_FP32
+    else:
+        raise ValueError("x must be bfloat16 or float32")
+    rows, cols = x.shape
+    cfg = _cfg(fmt, block, view, stochastic, hadamard_n, T, seed, offset)
+    qb, sb, qtb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _lib.check(lib.fp4_quantize_sizes(rows, cols, ctypes.byref(cfg), ctypes.byref(qb), ctypes.byref(sb),
+                                      ctypes.byref(qtb)))
+    dev = x.device
+    if view == COL:
+        q = torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev)
+        s = torch.empty((cols, rows // block), dtype=torch.uint8, device=dev)
+    elif view == TILE2D:
+        q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        s = torch.empty((rows // 16, cols // 16), dtype=torch.uint8, device=dev)
+    else:
+        q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        s = torch.empty((rows, cols // block), dtype=torch.uint8, device=dev)
+    qt = torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev) if view == TILE2D else None
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    _lib.check(lib.fp4_quantize(_ptr(x), dt, rows, cols, x.stride(0), ctypes.byref(cfg), _ptr(amax), _ptr(q), _ptr(s),
+                                _ptr(qt), _ptr(g), _ptr(amax_obs), _stream()))
+    if view == ROW:
+        return QTensor(q, s, g, fmt, block, FP4_SCALES_1D, rows, cols)
+    if view == COL:
+        return QTensor(q, s, g, fmt, block, FP4_SCALES_1D, cols, rows)
+    return (QTensor(q, s, g, fmt, 16, FP4_SCALES_2D, rows, cols),
+            QTensor(qt, s, g, fmt, 16, FP4_SCALES_2D_T, cols, rows))
+
+
+def tensor_amax(x: torch.Tensor, hadamard_n: int = 0, out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp4_tensor_amax: max|x| (after the blockwise FWHT along rows if hadamard_n) into a [1] float32 tensor."""
+    lib = _lib.load()
+    _dev_check(x)
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    dt = _lib.FP4_IN_FP32 if x.dtype == torch.float32 else _lib.FP4_IN_BF16
+    if x.dtype not in (torch.float32, torch.bfloat16) or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16/fp32 tensor with unit column stride")
+    _lib.check(lib.fp4_tensor_amax(_ptr(x), dt, x.shape[0], x.shape[1], x.stride(0), int(hadamard_n), _ptr(out),
+                                   _stream()))
+    return out
+
+
+class AmaxCache:
+    """Device-resident sample-and-hold amax cache (amax_cache_update / amax_cache_reset)."""
+
+    def __init__(self, D: int = 50, device: str | torch.device = "cuda"):
+        self.D = int(D)
+        self.amax = torch.zeros(1, dtype=torch.float32, device=device)
+        self.valid = torch.zeros(1, dtype=torch.int32, device=device)
+        self._host_valid = False   # mirror of the device flag, kept by this object
+
+    def _c(self) -> _lib.AmaxCacheC:
+        return _lib.AmaxCacheC(self.amax.data_ptr(), self.valid.data_ptr(), self.D)
+
+    def needs_sample(self, step: int) -> bool:
+        return (not self._host_valid) or step % self.D == 0
+
+    def update(self, step: int, amax_obs: torch.Tensor) -> None:
+        lib = _lib.load()
+        c = self._c()
+        _lib.check(lib.amax_cache_update(ctypes.byref(c), int(step), _ptr(amax_obs), _stream()))
+        self._host_valid = True
+
+    def reset(self) -> None:
+        lib = _lib.load()
+        c = self._c()
+        _lib.check(lib.amax_cache_reset(ctypes.byref(c), _stream()))
+        self._host_valid = False
+
+
+def _gemm(name: str, a: QTensor, b: QTensor, canon: bool, hadamard_n: int | None, out: torch.Tensor | None):
+    lib = _lib.load()
+    if out is None:
+        out = torch.empty((a.rows, b.rows), dtype=torch.float32, device=a.q.device)
+    if out.shape != (a.rows, b.rows) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [M, N] tensor")
+    oa, ob = a.operand(), b.operand()
+    fn = getattr(lib, name)
+    if hadamard_n is None:
+        st = fn(ctypes.byref(oa), ctypes.byref(ob), _ptr(out), int(bool(canon)), _stream())
+    else:
+        st = fn(ctypes.byref(oa), ctypes.byref(ob), _ptr(out), int(hadamard_n), int(bool(canon)), _stream())
+    _lib.check(st)
+    return out
+
+
+def gemm_fprop(x: QTensor, w: QTensor, canon: bool = False, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X . W^T (fp4_gemm_fprop)."""
+    return _gemm("fp4_gemm_fprop", x, w, canon, None, out)
+
+
+def gemm_dgrad(dy: QTensor, wt: QTensor, canon: bool = False, out: torch.Tensor | None = None) -> torch.Tensor:
+    """dX = dY . W (fp4_gemm_dgrad); wt is the weight's transposed operand."""
+    return _gemm("fp4_gemm_dgrad", dy, wt, canon, None, out)
+
+
+def gemm_wgrad(dyt: QTensor, xt: QTensor, hadamard_n: int = 0, canon: bool = False,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """dW = dY^T . X (fp4_gemm_wgrad) from the two COL-view operands."""
+    return _gemm("fp4_gemm_wgrad", dyt, xt, canon, hadamard_n, out)
+
+
+def debug_encode(x: torch.Tensor, which: int, u16: torch.Tensor | None = None) -> torch.Tensor:
+    """fp4_debug_encode: device encoder codes for float32 inputs (parity tests)."""
+    lib = _lib.load()
+    _dev_check(x, u16)
+    x = x.contiguous()
+    out = torch.empty(x.numel(), dtype=torch.uint8, device=x.device)
+    _lib.check(lib.fp4_debug_encode(_ptr(x), _ptr(u16), x.numel(), int(which), _ptr(out), _stream()))
+    return out

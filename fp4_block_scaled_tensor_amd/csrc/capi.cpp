@@ -1,0 +1,262 @@
+// C ABI of the block-scaled FP4 library: argument validation and dispatch. Every check
+// runs before anything is enqueued; errors set a thread-local message.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/fp4bs.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fp4_status fail(fp4_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+fp4_status ok() {
+  g_err[0] = '\0';
+  return FP4_OK;
+}
+
+fp4_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FP4_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+fp4_status check_fmt_block(int32_t fmt, int32_t block) {
+  if (fmt != FP4_UE5M3 && fmt != FP4_E4M3 && fmt != FP4_E8M0) return fail(FP4_EINVAL, "unknown scale format %d", fmt);
+  if (block != 16 && block != 32) return fail(FP4_EUNSUPPORTED, "block must be 16 or 32 (got %d)", block);
+  if (fmt == FP4_E8M0 && block != 32) return fail(FP4_EUNSUPPORTED, "E8M0 (MXFP4) scales require block 32");
+  return FP4_OK;
+}
+
+fp4_status check_cfg(const fp4_quant_cfg* c) {
+  if (!c) return fail(FP4_EINVAL, "cfg is NULL");
+  fp4_status st = check_fmt_block(c->fmt, c->block);
+  if (st != FP4_OK) return st;
+  if (c->view < FP4_VIEW_ROW || c->view > FP4_VIEW_TILE2D) return fail(FP4_EINVAL, "unknown view %d", c->view);
+  if (c->stochastic != 0 && c->stochastic != 1) return fail(FP4_EINVAL, "stochastic must be 0 or 1");
+  if (c->hadamard_n != 0 && c->hadamard_n != 16 && c->hadamard_n != 32)
+    return fail(FP4_EINVAL, "hadamard_n must be 0, 16 or 32");
+  if (c->hadamard_n != 0 && c->view != FP4_VIEW_COL)
+    return fail(FP4_EUNSUPPORTED, "the Hadamard rotation applies to the COL (wgrad) view only");
+  if (c->view == FP4_VIEW_TILE2D) {
+    if (c->fmt == FP4_E8M0) return fail(FP4_EUNSUPPORTED, "TILE2D needs UE5M3 or E4M3 scales");
+    if (c->block != 16) return fail(FP4_EUNSUPPORTED, "TILE2D uses 16x16 tiles (block 16)");
+    if (c->stochastic) return fail(FP4_EUNSUPPORTED, "weights are rounded to nearest-even only");
+  }
+  if (c->fmt != FP4_E8M0 && !(c->T > 0.0f && c->T < 3.0e38f)) return fail(FP4_EINVAL, "T must be positive and finite");
+  return FP4_OK;
+}
+
+fp4_status check_shape(int64_t rows, int64_t cols, const fp4_quant_cfg* c) {
+  if (rows < 0 || cols < 0) return fail(FP4_EINVAL, "negative size");
+  if (rows > (int64_t(1) << 40) || cols > (int64_t(1) << 40)) return fail(FP4_EINVAL, "size too large");
+  const int B = c->block;
+  if (c->view == FP4_VIEW_ROW && cols % B) return fail(FP4_EINVAL, "ROW view: cols %% block != 0");
+  if (c->view == FP4_VIEW_COL) {
+    if (rows % B) return fail(FP4_EINVAL, "COL view: rows (tokens) %% block != 0");
+    if (c->hadamard_n && rows % c->hadamard_n) return fail(FP4_EINVAL, "COL view: rows %% hadamard_n != 0");
+    if (cols % 8) return fail(FP4_EINVAL, "COL view: cols must be a multiple of 8");
+  }
+  if (c->view == FP4_VIEW_TILE2D && (rows % 16 || cols % 16))
+    return fail(FP4_EINVAL, "TILE2D: rows and cols must be multiples of 16");
+  return FP4_OK;
+}
+
+void sizes(int64_t rows, int64_t cols, const fp4_quant_cfg* c, size_t* q, size_t* s, size_t* qt) {
+  const int64_t B = c->block;
+  *q = (size_t)(rows * cols / 2);
+  *qt = 0;
+  if (c->view == FP4_VIEW_ROW) *s = (size_t)(rows * (cols / B));
+  else if (c->view == FP4_VIEW_COL) *s = (size_t)(cols * (rows / B));
+  else {
+    *s = (size_t)((rows / 16) * (cols / 16));
+    *qt = *q;
+  }
+}
+
+fp4_status check_operand(const fp4_operand* o, const char* name) {
+  if (!o) return fail(FP4_EINVAL, "%s is NULL", name);
+  if (o->rows < 0 || o->k < 0) return fail(FP4_EINVAL, "%s: negative size", name);
+  if (o->k % 64) return fail(FP4_EINVAL, "%s: K must be a multiple of 64 (got %lld)", name, (long long)o->k);
+  fp4_status st = check_fmt_block(o->fmt, o->block);
+  if (st != FP4_OK) return st;
+  if (o->scale_layout < FP4_SCALES_1D || o->scale_layout > FP4_SCALES_2D_T)
+    return fail(FP4_EINVAL, "%s: unknown scale layout", name);
+  if (o->scale_layout != FP4_SCALES_1D) {
+    if (o->fmt == FP4_E8M0 || o->block != 16) return fail(FP4_EUNSUPPORTED, "%s: 2D scales need UE5M3/E4M3 block 16", name);
+    if (o->rows % 16) return fail(FP4_EINVAL, "%s: 2D-scaled operand rows must be a multiple of 16", name);
+  }
+  if (o->rows > 0 && o->k > 0) {
+    if (!o->q || !o->s) return fail(FP4_EINVAL, "%s: NULL payload or scales", name);
+    if (!aligned(o->q, 16)) return fail(FP4_EALIGN, "%s: payload not 16-byte aligned", name);
+    if (!aligned(o->s, 2)) return fail(FP4_EALIGN, "%s: scales not 2-byte aligned", name);
+  }
+  if (o->g && !aligned(o->g, 4)) return fail(FP4_EALIGN, "%s: g not 4-byte aligned", name);
+  return FP4_OK;
+}
+
+fp4_status gemm_common(const fp4_operand* a, const fp4_operand* b, float* c, int32_t canon, int32_t hadamard_n,
+                       void* stream, const char* what) {
+  fp4_status st;
+  if ((st = check_operand(a, "A")) != FP4_OK) return st;
+  if ((st = check_operand(b, "B")) != FP4_OK) return st;
+  if (a->k != b->k) return fail(FP4_EINVAL, "%s: operands have different K (%lld vs %lld)", what, (long long)a->k,
+                                (long long)b->k);
+  if (a->fmt != b->fmt || a->block != b->block) return fail(FP4_EUNSUPPORTED, "%s: operands differ in format/block", what);
+  if (canon != 0 && canon != 1) return fail(FP4_EINVAL, "canon must be 0 or 1");
+  if (a->rows > 0 && b->rows > 0) {
+    if (!c) return fail(FP4_EINVAL, "%s: output is NULL", what);
+    if (!aligned(c, 16)) return fail(FP4_EALIGN, "%s: output not 16-byte aligned", what);
+  }
+  fp4k::GemmArgs g;
+  g.a = fp4k::GemmOperand{a->q, a->s, a->g, a->scale_layout, a->rows};
+  g.b = fp4k::GemmOperand{b->q, b->s, b->g, b->scale_layout, b->rows};
+  g.fmt = a->fmt;
+  g.block = a->block;
+  g.M = a->rows;
+  g.N = b->rows;
+  g.K = a->k;
+  g.c = c;
+  g.canon = canon;
+  g.hadamard_n = hadamard_n;
+  g.stream = (hipStream_t)stream;
+  if (g.M == 0 || g.N == 0) return ok();
+  const hipError_t e = (g.fmt == FP4_E8M0) ? fp4k::run_gemm_mx(g) : fp4k::run_gemm_dec16(g);
+  return hip_status(e, what);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fp4_abi_version(void) { return FP4BS_ABI_VERSION; }
+
+const char* fp4_last_error(void) { return g_err; }
+
+fp4_status fp4_quantize_sizes(int64_t rows, int64_t cols, const fp4_quant_cfg* cfg, size_t* q_bytes, size_t* s_bytes,
+                              size_t* qt_bytes) {
+  fp4_status st;
+  if ((st = check_cfg(cfg)) != FP4_OK) return st;
+  if ((st = check_shape(rows, cols, cfg)) != FP4_OK) return st;
+  if (!q_bytes || !s_bytes || !qt_bytes) return fail(FP4_EINVAL, "NULL size output");
+  sizes(rows, cols, cfg, q_bytes, s_bytes, qt_bytes);
+  return ok();
+}
+
+fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld,
+                        const fp4_quant_cfg* cfg, const float* d_amax, uint8_t* q, uint8_t* s, uint8_t* q_t,
+                        float* d_g, float* d_amax_obs, void* stream) {
+  fp4_status st;
+  if ((st = check_cfg(cfg)) != FP4_OK) return st;
+  if ((st = check_shape(rows, cols, cfg)) != FP4_OK) return st;
+  if (x_dtype != FP4_IN_BF16 && x_dtype != FP4_IN_FP32) return fail(FP4_EINVAL, "unknown input dtype %d", x_dtype);
+  const int64_t esz = x_dtype == FP4_IN_FP32 ? 4 : 2;
+  if (ld < cols) return fail(FP4_EINVAL, "ld (%lld) < cols (%lld)", (long long)ld, (long long)cols);
+  const bool nonempty = rows > 0 && cols > 0;
+  if (nonempty) {
+    if (!x || !q || !s) return fail(FP4_EINVAL, "NULL x, q or s");
+    if (cfg->view == FP4_VIEW_TILE2D && !q_t) return fail(FP4_EINVAL, "TILE2D requires q_t");
+    if (!aligned(x, 16) || !aligned(q, 16) || (q_t && !aligned(q_t, 16)))
+      return fail(FP4_EALIGN, "x, q and q_t must be 16-byte aligned");
+    if ((ld * esz) % 16) return fail(FP4_EALIGN, "row stride must be a multiple of 16 bytes");
+  }
+  if (cfg->view != FP4_VIEW_TILE2D && q_t) return fail(FP4_EINVAL, "q_t is only written by TILE2D");
+  if (cfg->fmt != FP4_E8M0 && !d_amax) return fail(FP4_EINVAL, "UE5M3/E4M3 need the cached amax d_amax");
+  if ((d_amax && !aligned(d_amax, 4)) || (d_g && !aligned(d_g, 4)) || (d_amax_obs && !aligned(d_amax_obs, 4)))
+    return fail(FP4_EALIGN, "amax / g pointers must be 4-byte aligned");
+  fp4k::QuantArgs a;
+  a.x = x;
+  a.f32 = x_dtype == FP4_IN_FP32;
+  a.rows = rows;
+  a.cols = cols;
+  a.ld = ld;
+  a.fmt = cfg->fmt;
+  a.block = cfg->block;
+  a.view = cfg->view;
+  a.stochastic = cfg->stochastic;
+  a.hadamard_n = cfg->hadamard_n;
+  a.T = cfg->T;
+  a.seed = cfg->seed;
+  a.offset = cfg->offset;
+  a.d_amax = d_amax;
+  a.q = q;
+  a.s = s;
+  a.qt = q_t;
+  a.d_g = d_g;
+  a.d_amax_obs = d_amax_obs;
+  a.stream = (hipStream_t)stream;
+  return hip_status(fp4k::run_quantize(a), "fp4_quantize");
+}
+
+fp4_status fp4_tensor_amax(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld, int32_t hadamard_n,
+                           float* d_amax_out, void* stream) {
+  if (x_dtype != FP4_IN_BF16 && x_dtype != FP4_IN_FP32) return fail(FP4_EINVAL, "unknown input dtype %d", x_dtype);
+  if (rows < 0 || cols < 0 || ld < cols) return fail(FP4_EINVAL, "bad sizes");
+  if (hadamard_n != 0 && hadamard_n != 16 && hadamard_n != 32) return fail(FP4_EINVAL, "hadamard_n must be 0, 16, 32");
+  if (hadamard_n && rows % hadamard_n) return fail(FP4_EINVAL, "rows %% hadamard_n != 0");
+  if (cols % 8) return fail(FP4_EINVAL, "cols must be a multiple of 8");
+  if (!d_amax_out || !aligned(d_amax_out, 4)) return fail(FP4_EINVAL, "d_amax_out must be a 4-byte aligned pointer");
+  const int64_t esz = x_dtype == FP4_IN_FP32 ? 4 : 2;
+  if (rows > 0 && cols > 0) {
+    if (!x || !aligned(x, 16)) return fail(FP4_EALIGN, "x must be non-NULL and 16-byte aligned");
+    if ((ld * esz) % 16) return fail(FP4_EALIGN, "row stride must be a multiple of 16 bytes");
+  }
+  return hip_status(fp4k::run_amax(x, x_dtype == FP4_IN_FP32, rows, cols, ld, hadamard_n, d_amax_out,
+                                   (hipStream_t)stream),
+                    "fp4_tensor_amax");
+}
+
+fp4_status amax_cache_update(const fp4_amax_cache* cache, int64_t step, const float* d_amax_obs, void* stream) {
+  if (!cache || !cache->amax || !cache->valid || !d_amax_obs) return fail(FP4_EINVAL, "NULL cache field or amax");
+  if (cache->D < 1) return fail(FP4_EINVAL, "cache period D must be >= 1");
+  if (step < 0) return fail(FP4_EINVAL, "step must be >= 0");
+  return hip_status(fp4k::run_cache_update(cache->amax, cache->valid, cache->D, step, d_amax_obs, (hipStream_t)stream),
+                    "amax_cache_update");
+}
+
+fp4_status amax_cache_reset(const fp4_amax_cache* cache, void* stream) {
+  if (!cache || !cache->valid) return fail(FP4_EINVAL, "NULL cache");
+  return hip_status(fp4k::run_cache_reset(cache->valid, (hipStream_t)stream), "amax_cache_reset");
+}
+
+fp4_status fp4_gemm_fprop(const fp4_operand* x, const fp4_operand* w, float* y, int32_t canon, void* stream) {
+  if (x && x->scale_layout != FP4_SCALES_1D) return fail(FP4_EUNSUPPORTED, "fprop: activation needs 1D scales");
+  if (w && w->scale_layout == FP4_SCALES_2D_T)
+    return fail(FP4_EUNSUPPORTED, "fprop: the weight's transposed (dgrad) view is not the forward operand");
+  return gemm_common(x, w, y, canon, 0, stream, "fp4_gemm_fprop");
+}
+
+fp4_status fp4_gemm_dgrad(const fp4_operand* dy, const fp4_operand* wt, float* dx, int32_t canon, void* stream) {
+  if (dy && dy->scale_layout != FP4_SCALES_1D) return fail(FP4_EUNSUPPORTED, "dgrad: dY needs 1D scales");
+  if (wt && wt->scale_layout == FP4_SCALES_2D)
+    return fail(FP4_EUNSUPPORTED, "dgrad: pass the weight's transposed payload with FP4_SCALES_2D_T");
+  return gemm_common(dy, wt, dx, canon, 0, stream, "fp4_gemm_dgrad");
+}
+
+fp4_status fp4_gemm_wgrad(const fp4_operand* dyt, const fp4_operand* xt, float* dw, int32_t hadamard_n, int32_t canon,
+                          void* stream) {
+  if (hadamard_n != 0 && hadamard_n != 16 && hadamard_n != 32) return fail(FP4_EINVAL, "hadamard_n must be 0, 16, 32");
+  if ((dyt && dyt->scale_layout != FP4_SCALES_1D) || (xt && xt->scale_layout != FP4_SCALES_1D))
+    return fail(FP4_EUNSUPPORTED, "wgrad: both operands need 1D scales along tokens");
+  return gemm_common(dyt, xt, dw, canon, hadamard_n, stream, "fp4_gemm_wgrad");
+}
+
+fp4_status fp4_debug_encode(const float* x, const uint16_t* u16, int64_t n, int32_t which, uint8_t* out, void* stream) {
+  if (n < 0 || which < 0 || which > 4) return fail(FP4_EINVAL, "bad n or which");
+  if (n > 0 && (!x || !out || (which == 4 && !u16))) return fail(FP4_EINVAL, "NULL input/output");
+  return hip_status(fp4k::run_debug_encode(x, u16, n, which, out, (hipStream_t)stream), "fp4_debug_encode");
+}
+
+}  // extern "C"

@@ -1,0 +1,184 @@
+// Device helpers for the block-scaled FP4 kernels on gfx950: scale-format encoders and
+// decoders, E2M1 payload rounding, Philox-4x32-10, and the FP32 round-mode switch.
+//
+// Sources (page title, section):
+//  - "UE5M3 FP4 Block Scaling for Stable Language Model Pretraining", approach (접근 방법):
+//    E2M1 payload; unsigned E5M3 block scales (max 61,440); nearest-even for activations,
+//    weights and block scales; stochastic rounding of dY only; zero block scale -> 1.
+//  - "Practical FP4 Training for Large-Scale MoE Models on Hopper GPUs", methodology (방법론):
+//    MXFP4 = E2M1 payload with a power-of-two scale per 32 elements.
+// Bit layouts: UE5M3 eeeeemmm (bias 15, subnormals, exponent 31 unused);
+// E4M3 0eeeemmm (bias 7, 0x7F is NaN and never produced); E8M0 2^(code-127).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4k {
+
+enum : int { FMT_UE5M3 = 0, FMT_E4M3 = 1, FMT_E8M0 = 2 };
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ---- block-scale formats with 3 mantissa bits (UE5M3: bias 15, E4M3: bias 7) ----
+template <int FMT> struct ScaleFmt;
+template <> struct ScaleFmt<FMT_UE5M3> {
+  static constexpr int BIAS = 15;
+  static constexpr uint32_t MAXCODE = 0xF7;      // 2^15 * 1.875 = 61440
+  static constexpr float MAXV = 61440.0f;
+  static constexpr uint32_t ONE = 0x78;          // 1.0
+  static constexpr float SUB_SCALE = 131072.0f;  // 2^17: subnormal quantum 2^-17
+  static constexpr float MIN_NORMAL = 6.103515625e-05f;  // 2^-14
+};
+template <> struct ScaleFmt<FMT_E4M3> {
+  static constexpr int BIAS = 7;
+  static constexpr uint32_t MAXCODE = 0x7E;      // 2^8 * 1.75 = 448
+  static constexpr float MAXV = 448.0f;
+  static constexpr uint32_t ONE = 0x38;
+  static constexpr float SUB_SCALE = 512.0f;     // 2^9
+  static constexpr float MIN_NORMAL = 0.015625f; // 2^-6
+};
+
+// Nearest-even, saturating code of v >= 0 (v may be +inf). Subnormal codes 0..7 continue
+// into the first normal code 8, so below the normal range the code is simply
+// rint(v / quantum); above it the 23-bit FP32 mantissa is rounded to 3 bits with
+// ties-to-even and a carry that propagates into the exponent.
+template <int FMT>
+__device__ __forceinline__ uint32_t enc_scale3(float v) {
+  using S = ScaleFmt<FMT>;
+  if (!(v < S::MAXV)) return S::MAXCODE;
+  if (v < S::MIN_NORMAL) return (uint32_t)__builtin_rintf(v * S::SUB_SCALE);
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
+  return (r >> 20) - ((uint32_t)(127 - S::BIAS) << 3);
+}
+
+template <int FMT>
+__device__ __forceinline__ float dec_scale3(uint32_t c) {
+  using S = ScaleFmt<FMT>;
+  const uint32_t e = c >> 3, m = c & 7u;
+  if (e == 0) return (float)m * (1.0f / S::SUB_SCALE);
+  return __uint_as_float(((e - S::BIAS + 127u) << 23) | (m << 20));
+}
+
+// E8M0 block exponent for a block maximum a >= 0: floor(log2 a) - 2 clamped to [-127, 127],
+// 0 for a == 0. Returns the code E + 127.
+__device__ __forceinline__ uint32_t e8m0_code(float a) {
+  const uint32_t b = __float_as_uint(a);
+  if (b == 0) return 127;
+  int fl;
+  const uint32_t ex = b >> 23;
+  if (ex != 0) fl = (int)ex - 127;
+  else fl = (31 - __builtin_clz(b)) - 149;      // subnormal maximum
+  int E = fl - 2;
+  E = E < -127 ? -127 : (E > 127 ? 127 : E);
+  return (uint32_t)(E + 127);
+}
+
+// 2^-E for the E8M0 code c = E + 127 (exact; 2^-127 is subnormal).
+__device__ __forceinline__ float e8m0_inv(uint32_t c) {
+  const int negE = 127 - (int)c;                 // -E in [-127, 127]
+  if (negE >= -126) return __uint_as_float((uint32_t)(negE + 127) << 23);
+  return __uint_as_float(1u << 22);              // 2^-127
+}
+
+// ---- E2M1 payload, nearest-even with saturation at 6 ----
+// v_cvt_scalef32_pk_fp4_f32 with scale 1.0 converts two floats to two E2M1 codes with
+// nearest-even, saturation and the input sign kept (checked against a compare-based
+// encoder on all 2^32 float32 inputs). src0 lands in the low nibble of the selected byte.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pack2(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// 8 floats -> one dword of 8 codes (element 0 in the low nibble)
+__device__ __forceinline__ uint32_t e2m1_pack8(const float* r) {
+  uint32_t w = 0;
+  w = e2m1_pack2<0>(w, r[0], r[1]);
+  w = e2m1_pack2<1>(w, r[2], r[3]);
+  w = e2m1_pack2<2>(w, r[4], r[5]);
+  w = e2m1_pack2<3>(w, r[6], r[7]);
+  return w;
+}
+
+// ---- stochastic E2M1 ----
+// With a = |r| < 6, let lo <= a < hi be the neighbouring codebook values (grid step 0.5
+// below 2, 1 below 4, 2 below 6); round up iff u16 < 65536 * (a - lo) / (hi - lo). All
+// quantities are exact in float32 (Sterbenz subtraction, power-of-two scaling).
+__device__ __forceinline__ uint32_t e2m1_sr(float r, uint32_t u16) {
+  const float a = fabsf(r);
+  const uint32_t sign = (__float_as_uint(r) >> 28) & 8u;
+  if (!(a < 6.0f)) return sign | 7u;
+  float t;
+  uint32_t base;
+  if (a < 2.0f) { t = a * 2.0f; base = 0; }
+  else if (a < 4.0f) { t = a - 2.0f; base = 4; }
+  else { t = (a - 4.0f) * 0.5f; base = 6; }
+  const float fl = __builtin_floorf(t);
+  const float frac = t - fl;
+  const uint32_t up = ((float)u16 < frac * 65536.0f) ? 1u : 0u;
+  return sign | (base + (uint32_t)fl + up);
+}
+
+// ---- Philox-4x32-10 (Salmon et al., SC'11) ----
+struct u4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ u4 philox4x32_10(u4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    c = u4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+  }
+  return c;
+}
+
+// 16-bit draws for the 8 logical elements 8*blk8 .. 8*blk8+7 of an operand: element j
+// takes word j>>1, low half for even j.
+__device__ __forceinline__ void philox_u16x8(uint64_t blk8, uint64_t seed, uint64_t offset, uint32_t* u) {
+  const u4 o = philox4x32_10(u4{(uint32_t)blk8, (uint32_t)(blk8 >> 32), (uint32_t)offset, (uint32_t)(offset >> 32)},
+                             (uint32_t)seed, (uint32_t)(seed >> 32));
+  u[0] = o.x & 0xFFFFu; u[1] = o.x >> 16;
+  u[2] = o.y & 0xFFFFu; u[3] = o.y >> 16;
+  u[4] = o.z & 0xFFFFu; u[5] = o.z >> 16;
+  u[6] = o.w & 0xFFFFu; u[7] = o.w >> 16;
+}
+
+// ---- tensor scales from the cached amax (float32, nearest-even) ----
+struct TensorScales { float s_enc, s_blk, g; };
+
+__device__ __forceinline__ TensorScales tensor_scales(const float* d_amax, float T) {
+  const float A = d_amax ? *d_amax : 0.0f;
+  TensorScales ts{1.0f, 1.0f, 1.0f};
+  if (A > 0.0f && A <= 3.4028234663852886e38f) {
+    const float se = (6.0f * T) / A;
+    if (se <= 3.4028234663852886e38f) {
+      ts.s_enc = se;
+      ts.s_blk = T / A;
+      ts.g = 1.0f / se;
+    }
+  }
+  return ts;
+}
+
+// ---- FP32 round-mode control (MODE register bits [1:0]; [3:2] = f64/f16 stay nearest) ----
+// Inline asm with a memory clobber orders these against the volatile adds that depend on them.
+__device__ __forceinline__ void mode_f32_rtz() {
+  asm volatile("s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 3\n\ts_nop 3" ::: "memory");
+}
+__device__ __forceinline__ void mode_f32_rne() {
+  asm volatile("s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 0\n\ts_nop 3" ::: "memory");
+}
+
+// a + b with whatever FP32 round mode is current; volatile so it cannot move across a
+// mode switch.
+__device__ __forceinline__ float add_in_mode(float a, float b) {
+  float r;
+  asm volatile("v_add_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+}  // namespace fp4k

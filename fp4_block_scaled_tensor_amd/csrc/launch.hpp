@@ -1,0 +1,52 @@
+// Internal launcher interface between the C ABI (capi.cpp) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4k {
+
+struct QuantArgs {
+  const void* x;
+  bool f32;
+  int64_t rows, cols, ld;
+  int fmt, block, view, stochastic, hadamard_n;
+  float T;
+  uint64_t seed, offset;
+  const float* d_amax;
+  uint8_t* q;
+  uint8_t* s;
+  uint8_t* qt;
+  float* d_g;
+  float* d_amax_obs;
+  hipStream_t stream;
+};
+
+struct GemmOperand {
+  const uint8_t* q;
+  const uint8_t* s;
+  const float* g;
+  int layout;        // 0: 1D, 1: 2D forward view, 2: 2D transposed view
+  int64_t rows;
+};
+
+struct GemmArgs {
+  GemmOperand a, b;
+  int fmt, block;
+  int64_t M, N, K;
+  float* c;
+  int canon;
+  int hadamard_n;
+  hipStream_t stream;
+};
+
+hipError_t run_quantize(const QuantArgs& a);
+hipError_t run_amax(const void* x, bool f32, int64_t rows, int64_t cols, int64_t ld, int hadamard_n, float* out,
+                    hipStream_t stream);
+hipError_t run_cache_update(float* amax, int32_t* valid, int32_t D, int64_t step, const float* obs, hipStream_t stream);
+hipError_t run_cache_reset(int32_t* valid, hipStream_t stream);
+hipError_t run_debug_encode(const float* x, const uint16_t* u16, int64_t n, int which, uint8_t* out,
+                            hipStream_t stream);
+hipError_t run_gemm_mx(const GemmArgs& g);      // E8M0, block 32
+hipError_t run_gemm_dec16(const GemmArgs& g);   // UE5M3 / E4M3, block 16 or 32
+
+}  // namespace fp4k

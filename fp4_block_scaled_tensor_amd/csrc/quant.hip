@@ -1,0 +1,465 @@
+// Block-scaled FP4 quantizer kernels for gfx950 (HBM-bound).
+//
+// "UE5M3 FP4 Block Scaling for Stable Language Model Pretraining", approach (접근 방법):
+// per-operand cached amax and scale target T set the tensor scale; block scales are
+// nearest-even and saturating, a zero scale becomes one; the E2M1 payload is nearest-even
+// (stochastic for dY); weights use 2D 16x16 blocks shared by the forward and backward views.
+// "Practical FP4 Training for Large-Scale MoE Models on Hopper GPUs", methodology (방법론):
+// transposed layouts are produced by a fused transpose + quantize pass through on-chip
+// memory instead of a separate transpose in HBM.
+// "技術概要：MXFP4 による大規模言語モデルの事前学習", method (手法): deterministic H16/H32
+// Hadamard rotation of the weight-gradient operands, fused here into the transposed pass.
+//
+// Kernels:
+//   k_quant_row   ROW view: one thread per B-element block along the row; 16-byte loads.
+//   k_quant_col   COL view: a 256-token x 64-feature tile staged in LDS; each thread owns a
+//                 16/32-token run of one feature (optionally rotated by the FWHT), writes its
+//                 payload to an LDS output tile, which is stored row-contiguously.
+//   k_quant_2d    TILE2D: a 64x64 tile in LDS; tile amaxes by lane shuffles; both the forward
+//                 payload (row segments) and the transposed payload (column segments).
+//   k_amax_*      max|x| (plain, or along-token FWHT for Hadamard views) by atomicMax on the
+//                 float bits (non-negative floats order like unsigned integers).
+#include "fp4_device.hpp"
+#include "launch.hpp"
+
+namespace fp4k {
+
+constexpr int NT = 256;
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ void atomic_max_nonneg(float* p, float v) {
+  atomicMax(reinterpret_cast<unsigned int*>(p), __float_as_uint(v));
+}
+
+// Load 8 consecutive input elements (bf16 or fp32) as floats.
+template <bool F32>
+__device__ __forceinline__ void load8(const void* base, int64_t elem, float* v) {
+  if constexpr (F32) {
+    const uint4 a = *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(base) + elem);
+    const uint4 b = *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(base) + elem + 4);
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+  } else {
+    const uint4 a = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
+    v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+    v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+  }
+}
+
+// Scale code and payload multiplier of one block with maximum amax_b.
+template <int FMT>
+__device__ __forceinline__ void block_scale(float amax_b, const TensorScales& ts, uint32_t& code, float& mult) {
+  if constexpr (FMT == FMT_E8M0) {
+    code = e8m0_code(amax_b);
+    mult = e8m0_inv(code);
+  } else {
+    code = enc_scale3<FMT>(amax_b * ts.s_blk);
+    if (code == 0) code = ScaleFmt<FMT>::ONE;          // zero-scale rule
+    mult = ts.s_enc / dec_scale3<FMT>(code);           // correctly rounded division
+  }
+}
+
+// Quantize n (multiple of 8) values with multiplier mult into n/8 dwords of codes.
+// SR: logical index of v[0] is i0 (multiple of 8).
+template <int N, bool SR>
+__device__ __forceinline__ void payload(const float* v, float mult, uint64_t i0, uint64_t seed, uint64_t offset,
+                                        uint32_t* words) {
+#pragma unroll
+  for (int w = 0; w < N / 8; ++w) {
+    float r[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = v[8 * w + j] * mult;
+    if constexpr (SR) {
+      uint32_t u[8];
+      philox_u16x8((i0 >> 3) + w, seed, offset, u);
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) word |= e2m1_sr(r[j], u[j]) << (4 * j);
+      words[w] = word;
+    } else {
+      words[w] = e2m1_pack8(r);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- ROW view
+template <int FMT, int B, bool SR, bool F32>
+__global__ __launch_bounds__(NT) void k_quant_row(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+                                                  const float* __restrict__ d_amax, float T, uint64_t seed,
+                                                  uint64_t offset, uint8_t* __restrict__ q, uint8_t* __restrict__ s,
+                                                  float* __restrict__ d_amax_obs) {
+  const int64_t nbr = cols / B;
+  const int64_t b = (int64_t)blockIdx.x * NT + threadIdx.x;
+  TensorScales ts{1.0f, 1.0f, 1.0f};
+  if constexpr (FMT != FMT_E8M0) ts = tensor_scales(d_amax, T);
+  float obs = 0.0f;
+  if (b < nbr) {
+    for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+      float v[B];
+#pragma unroll
+      for (int j = 0; j < B / 8; ++j) load8<F32>(x, r * ld + b * B + 8 * j, v + 8 * j);
+      float amax_b = 0.0f;
+#pragma unroll
+      for (int j = 0; j < B; ++j) amax_b = fmaxf(amax_b, fabsf(v[j]));
+      obs = fmaxf(obs, amax_b);
+      uint32_t code;
+      float mult;
+      block_scale<FMT>(amax_b, ts, code, mult);
+      uint32_t words[B / 8];
+      payload<B, SR>(v, mult, (uint64_t)(r * cols + b * B), seed, offset, words);
+      uint8_t* qp = q + r * (cols / 2) + b * (B / 2);
+      if constexpr (B == 16) *reinterpret_cast<uint2*>(qp) = make_uint2(words[0], words[1]);
+      else *reinterpret_cast<uint4*>(qp) = make_uint4(words[0], words[1], words[2], words[3]);
+      s[r * nbr + b] = (uint8_t)code;
+    }
+  }
+  if (d_amax_obs) {
+    obs = wave_max(obs);
+    if ((threadIdx.x & 63) == 0) atomic_max_nonneg(d_amax_obs, obs);
+  }
+}
+
+// ---------------------------------------------------------------- COL view (wgrad operands)
+constexpr int CT = 256;   // tokens per tile
+constexpr int CF = 64;    // features per tile
+
+template <int HN>
+__device__ __forceinline__ void fwht_inplace(float* v) {
+#pragma unroll
+  for (int h = 1; h < HN; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < HN; ++i) {
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+}
+
+// Stage a CT x CF tile of x (rows = tokens, cols = features) into LDS as float.
+template <bool F32>
+__device__ __forceinline__ void stage_tile(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+                                           int64_t t0, int64_t f0, float (*tile)[CF + 1]) {
+  // 8-element chunks: CT rows x (CF/8) chunks
+  for (int c = threadIdx.x; c < CT * (CF / 8); c += NT) {
+    const int rr = c / (CF / 8), cc = (c % (CF / 8)) * 8;
+    float v[8];
+    if (t0 + rr < rows && f0 + cc < cols) {
+      load8<F32>(x, (t0 + rr) * ld + f0 + cc, v);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[rr][cc + j] = v[j];
+  }
+}
+
+template <int FMT, int B, bool SR, bool F32, int HN>
+__global__ __launch_bounds__(NT) void k_quant_col(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+                                                  const float* __restrict__ d_amax, float T, uint64_t seed,
+                                                  uint64_t offset, uint8_t* __restrict__ q, uint8_t* __restrict__ s,
+                                                  float* __restrict__ d_amax_obs) {
+  constexpr int U = (HN > B) ? HN : B;          // tokens per thread unit
+  constexpr int UNITS = CT / U;                 // units per feature in a tile
+  __shared__ float tile[CT][CF + 1];
+  __shared__ uint32_t qout[CF][CT / 8 + 1];     // 8 codes per dword
+  __shared__ uint8_t sout[CF][CT / B];
+  const int64_t t0 = (int64_t)blockIdx.x * CT;
+  const int64_t f0 = (int64_t)blockIdx.y * CF;
+  stage_tile<F32>(x, rows, cols, ld, t0, f0, tile);
+  __syncthreads();
+  TensorScales ts{1.0f, 1.0f, 1.0f};
+  if constexpr (FMT != FMT_E8M0) ts = tensor_scales(d_amax, T);
+  const int f = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  float obs = 0.0f;
+  for (int u = w; u < UNITS; u += NT / 64) {
+    if (t0 + (int64_t)u * U >= rows) break;
+    float v[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) v[i] = tile[u * U + i][f];
+    if constexpr (HN > 0) {
+#pragma unroll
+      for (int h0 = 0; h0 < U; h0 += HN) fwht_inplace<HN>(v + h0);   // every HN-token run of the unit
+    }
+#pragma unroll
+    for (int bb = 0; bb < U / B; ++bb) {
+      float amax_b = 0.0f;
+#pragma unroll
+      for (int i = 0; i < B; ++i) amax_b = fmaxf(amax_b, fabsf(v[bb * B + i]));
+      obs = fmaxf(obs, amax_b);
+      uint32_t code;
+      float mult;
+      block_scale<FMT>(amax_b, ts, code, mult);
+      uint32_t words[B / 8];
+      const int tok = u * U + bb * B;           // token offset inside the tile
+      payload<B, SR>(v + bb * B, mult, (uint64_t)((f0 + f) * rows + t0 + tok), seed, offset, words);
+#pragma unroll
+      for (int j = 0; j < B / 8; ++j) qout[f][tok / 8 + j] = words[j];
+      sout[f][tok / B] = (uint8_t)code;
+    }
+  }
+  __syncthreads();
+  // store payload rows: feature f0+ff, bytes [t0/2, t0/2 + CT/2) in 8-byte pieces
+  const int64_t qrow = rows / 2;
+  for (int c = threadIdx.x; c < CF * (CT / 16); c += NT) {
+    const int ff = c / (CT / 16), piece = c % (CT / 16);
+    const int64_t tok = t0 + piece * 16;
+    if (f0 + ff < cols && tok < rows) {
+      *reinterpret_cast<uint2*>(q + (f0 + ff) * qrow + tok / 2) = make_uint2(qout[ff][2 * piece], qout[ff][2 * piece + 1]);
+    }
+  }
+  const int64_t srow = rows / B;
+  for (int c = threadIdx.x; c < CF * (CT / B); c += NT) {
+    const int ff = c / (CT / B), j = c % (CT / B);
+    if (f0 + ff < cols && t0 + (int64_t)j * B < rows) s[(f0 + ff) * srow + t0 / B + j] = sout[ff][j];
+  }
+  if (d_amax_obs) {
+    obs = wave_max(obs);
+    if ((threadIdx.x & 63) == 0) atomic_max_nonneg(d_amax_obs, obs);
+  }
+}
+
+// ---------------------------------------------------------------- TILE2D (weights)
+constexpr int WT = 64;   // 64x64 weight tile per workgroup
+
+template <int FMT, bool F32>
+__global__ __launch_bounds__(NT) void k_quant_2d(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+                                                 const float* __restrict__ d_amax, float T, uint8_t* __restrict__ q,
+                                                 uint8_t* __restrict__ qt, uint8_t* __restrict__ s,
+                                                 float* __restrict__ d_amax_obs) {
+  __shared__ float tile[WT][WT + 1];
+  __shared__ float mults[WT / 16][WT / 16];
+  const int64_t r0 = (int64_t)blockIdx.y * WT, c0 = (int64_t)blockIdx.x * WT;
+  for (int c = threadIdx.x; c < WT * (WT / 8); c += NT) {
+    const int rr = c / (WT / 8), cc = (c % (WT / 8)) * 8;
+    float v[8];
+    if (r0 + rr < rows && c0 + cc < cols) {
+      load8<F32>(x, (r0 + rr) * ld + c0 + cc, v);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[rr][cc + j] = v[j];
+  }
+  __syncthreads();
+  TensorScales ts = tensor_scales(d_amax, T);
+  // forward view: thread = (row r, 16-col segment sg); lanes 4k+sg of a wave share a 16x16 tile
+  const int r = threadIdx.x >> 2, sg = threadIdx.x & 3;
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = tile[r][sg * 16 + i];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+  m = fmaxf(m, __shfl_xor(m, 4, 64));
+  m = fmaxf(m, __shfl_xor(m, 8, 64));
+  m = fmaxf(m, __shfl_xor(m, 16, 64));
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  uint32_t code;
+  float mult;
+  block_scale<FMT>(m, ts, code, mult);
+  const bool rvalid = (r0 + r) < rows && (c0 + sg * 16) < cols;
+  if ((r & 15) == 0) {
+    mults[r >> 4][sg] = mult;
+    if (rvalid) s[((r0 + r) >> 4) * (cols / 16) + ((c0 >> 4) + sg)] = (uint8_t)code;
+  }
+  uint32_t words[2];
+  payload<16, false>(v, mult, 0, 0, 0, words);
+  if (rvalid) *reinterpret_cast<uint2*>(q + (r0 + r) * (cols / 2) + (c0 + sg * 16) / 2) = make_uint2(words[0], words[1]);
+  __syncthreads();
+  // transposed view: thread = (column cc, 16-row segment rs)
+  const int cc = threadIdx.x >> 2, rs = threadIdx.x & 3;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = tile[rs * 16 + i][cc];
+  payload<16, false>(v, mults[rs][cc >> 4], 0, 0, 0, words);
+  if ((c0 + cc) < cols && (r0 + rs * 16) < rows)
+    *reinterpret_cast<uint2*>(qt + (c0 + cc) * (rows / 2) + (r0 + rs * 16) / 2) = make_uint2(words[0], words[1]);
+  if (d_amax_obs) {
+    float o = wave_max(m);
+    if ((threadIdx.x & 63) == 0) atomic_max_nonneg(d_amax_obs, o);
+  }
+}
+
+// ---------------------------------------------------------------- amax
+template <bool F32>
+__global__ __launch_bounds__(NT) void k_amax_plain(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+                                                   float* __restrict__ out) {
+  float m = 0.0f;
+  const int64_t chunks = cols / 8;            // cols % 8 == 0 (validated)
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+    for (int64_t c = (int64_t)blockIdx.x * NT + threadIdx.x; c < chunks; c += (int64_t)gridDim.x * NT) {
+      float v[8];
+      load8<F32>(x, r * ld + c * 8, v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+    }
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) atomic_max_nonneg(out, m);
+}
+
+template <bool F32, int HN>
+__global__ __launch_bounds__(NT) void k_amax_hadamard(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                      int64_t ld, float* __restrict__ out) {
+  __shared__ float tile[CT][CF + 1];
+  const int64_t t0 = (int64_t)blockIdx.x * CT, f0 = (int64_t)blockIdx.y * CF;
+  stage_tile<F32>(x, rows, cols, ld, t0, f0, tile);
+  __syncthreads();
+  const int f = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float m = 0.0f;
+  for (int u = w; u < CT / HN; u += NT / 64) {
+    float v[HN];
+#pragma unroll
+    for (int i = 0; i < HN; ++i) v[i] = tile[u * HN + i][f];
+    fwht_inplace<HN>(v);
+#pragma unroll
+    for (int i = 0; i < HN; ++i) m = fmaxf(m, fabsf(v[i]));   // padded rows/cols are zero
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) atomic_max_nonneg(out, m);
+}
+
+__global__ void k_fill_f32(float* p, float v) { *p = v; }
+
+__global__ void k_write_g(const float* __restrict__ d_amax, float T, int fmt, float* __restrict__ d_g) {
+  *d_g = (fmt == FMT_E8M0) ? 1.0f : tensor_scales(d_amax, T).g;
+}
+
+__global__ void k_cache_update(float* amax, int32_t* valid, int32_t D, int64_t step, const float* obs) {
+  if (*valid == 0 || (step % D) == 0) {
+    *amax = *obs;
+    *valid = 1;
+  }
+}
+
+__global__ void k_cache_reset(int32_t* valid) { *valid = 0; }
+
+__global__ void k_debug_encode(const float* __restrict__ x, const uint16_t* __restrict__ u16, int64_t n, int which,
+                               uint8_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (i >= n) return;
+  const float v = x[i];
+  uint32_t c = 0;
+  if (which == 0) c = e2m1_pack2<0>(0u, v, 0.0f) & 15u;
+  else if (which == 1) c = enc_scale3<FMT_UE5M3>(v);
+  else if (which == 2) c = enc_scale3<FMT_E4M3>(v);
+  else if (which == 3) c = e8m0_code(v);
+  else c = e2m1_sr(v, u16[i]);
+  out[i] = (uint8_t)c;
+}
+
+// ---------------------------------------------------------------- launchers
+static inline unsigned grid_rows(int64_t rows) { return (unsigned)(rows < 65535 ? (rows > 0 ? rows : 1) : 65535); }
+
+template <int FMT, int B, bool SR, bool F32>
+static hipError_t launch_row(const QuantArgs& a) {
+  const int64_t nbr = a.cols / B;
+  dim3 grid((unsigned)((nbr + NT - 1) / NT), grid_rows(a.rows));
+  hipLaunchKernelGGL((k_quant_row<FMT, B, SR, F32>), grid, dim3(NT), 0, a.stream, a.x, a.rows, a.cols, a.ld, a.d_amax,
+                     a.T, a.seed, a.offset, a.q, a.s, a.d_amax_obs);
+  return hipGetLastError();
+}
+
+template <int FMT, int B, bool SR, bool F32, int HN>
+static hipError_t launch_col(const QuantArgs& a) {
+  dim3 grid((unsigned)((a.rows + CT - 1) / CT), (unsigned)((a.cols + CF - 1) / CF));
+  hipLaunchKernelGGL((k_quant_col<FMT, B, SR, F32, HN>), grid, dim3(NT), 0, a.stream, a.x, a.rows, a.cols, a.ld,
+                     a.d_amax, a.T, a.seed, a.offset, a.q, a.s, a.d_amax_obs);
+  return hipGetLastError();
+}
+
+template <int FMT, bool F32>
+static hipError_t launch_2d(const QuantArgs& a) {
+  dim3 grid((unsigned)((a.cols + WT - 1) / WT), (unsigned)((a.rows + WT - 1) / WT));
+  hipLaunchKernelGGL((k_quant_2d<FMT, F32>), grid, dim3(NT), 0, a.stream, a.x, a.rows, a.cols, a.ld, a.d_amax, a.T, a.q,
+                     a.qt, a.s, a.d_amax_obs);
+  return hipGetLastError();
+}
+
+template <int FMT, int B, bool SR, bool F32>
+static hipError_t dispatch_col_h(const QuantArgs& a) {
+  if (a.hadamard_n == 16) return launch_col<FMT, B, SR, F32, 16>(a);
+  if (a.hadamard_n == 32) return launch_col<FMT, B, SR, F32, 32>(a);
+  return launch_col<FMT, B, SR, F32, 0>(a);
+}
+
+template <int FMT, int B, bool F32>
+static hipError_t dispatch_view(const QuantArgs& a) {
+  if (a.view == 0) return a.stochastic ? launch_row<FMT, B, true, F32>(a) : launch_row<FMT, B, false, F32>(a);
+  if (a.view == 1) return a.stochastic ? dispatch_col_h<FMT, B, true, F32>(a) : dispatch_col_h<FMT, B, false, F32>(a);
+  if constexpr (FMT != FMT_E8M0 && B == 16) return launch_2d<FMT, F32>(a);
+  return hipErrorInvalidValue;
+}
+
+template <bool F32>
+static hipError_t dispatch_fmt(const QuantArgs& a) {
+  if (a.fmt == FMT_E8M0) return dispatch_view<FMT_E8M0, 32, F32>(a);
+  if (a.fmt == FMT_UE5M3) return a.block == 16 ? dispatch_view<FMT_UE5M3, 16, F32>(a) : dispatch_view<FMT_UE5M3, 32, F32>(a);
+  return a.block == 16 ? dispatch_view<FMT_E4M3, 16, F32>(a) : dispatch_view<FMT_E4M3, 32, F32>(a);
+}
+
+hipError_t run_quantize(const QuantArgs& a) {
+  hipError_t e;
+  if (a.d_amax_obs) {
+    hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, a.stream, a.d_amax_obs, 0.0f);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (a.d_g) {
+    hipLaunchKernelGGL(k_write_g, dim3(1), dim3(1), 0, a.stream, a.d_amax, a.T, a.fmt, a.d_g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (a.rows == 0 || a.cols == 0) return hipSuccess;
+  return a.f32 ? dispatch_fmt<true>(a) : dispatch_fmt<false>(a);
+}
+
+hipError_t run_amax(const void* x, bool f32, int64_t rows, int64_t cols, int64_t ld, int hadamard_n, float* out,
+                    hipStream_t stream) {
+  hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, stream, out, 0.0f);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || rows == 0 || cols == 0) return e;
+  if (hadamard_n == 0) {
+    const int64_t chunks = cols / 8;
+    const unsigned gx = (unsigned)((chunks + NT - 1) / NT > 16 ? 16 : (chunks + NT - 1) / NT);
+    const unsigned gy = (unsigned)(rows < 4096 ? rows : 4096);
+    if (f32) hipLaunchKernelGGL(k_amax_plain<true>, dim3(gx, gy), dim3(NT), 0, stream, x, rows, cols, ld, out);
+    else hipLaunchKernelGGL(k_amax_plain<false>, dim3(gx, gy), dim3(NT), 0, stream, x, rows, cols, ld, out);
+    return hipGetLastError();
+  }
+  dim3 grid((unsigned)((rows + CT - 1) / CT), (unsigned)((cols + CF - 1) / CF));
+  if (hadamard_n == 16) {
+    if (f32) hipLaunchKernelGGL((k_amax_hadamard<true, 16>), grid, dim3(NT), 0, stream, x, rows, cols, ld, out);
+    else hipLaunchKernelGGL((k_amax_hadamard<false, 16>), grid, dim3(NT), 0, stream, x, rows, cols, ld, out);
+  } else {
+    if (f32) hipLaunchKernelGGL((k_amax_hadamard<true, 32>), grid, dim3(NT), 0, stream, x, rows, cols, ld, out);
+    else hipLaunchKernelGGL((k_amax_hadamard<false, 32>), grid, dim3(NT), 0, stream, x, rows, cols, ld, out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t run_cache_update(float* amax, int32_t* valid, int32_t D, int64_t step, const float* obs, hipStream_t stream) {
+  hipLaunchKernelGGL(k_cache_update, dim3(1), dim3(1), 0, stream, amax, valid, D, step, obs);
+  return hipGetLastError();
+}
+
+hipError_t run_cache_reset(int32_t* valid, hipStream_t stream) {
+  hipLaunchKernelGGL(k_cache_reset, dim3(1), dim3(1), 0, stream, valid);
+  return hipGetLastError();
+}
+
+hipError_t run_debug_encode(const float* x, const uint16_t* u16, int64_t n, int which, uint8_t* out, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_debug_encode, dim3((unsigned)((n + NT - 1) / NT)), dim3(NT), 0, stream, x, u16, n, which, out);
+  return hipGetLastError();
+}
+
+}  // namespace fp4k

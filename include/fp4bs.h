@@ -1,0 +1,209 @@
+/*
+ * fp4bs.h - C ABI of the block-scaled FP4 quantize + GEMM library for MI355X (gfx950).
+ *
+ * The library implements the data-parallel hot path of FP4 linear layers in LLM
+ * pretraining: block-scaled E2M1 quantization of activations, weights and upstream
+ * gradients, and the three block-scaled FP4 GEMMs (fprop, dgrad, wgrad) under the
+ * probe-matched accumulation model.
+ *
+ * Sources (page title, section):
+ *  [UE5M3]  "UE5M3 FP4 Block Scaling for Stable Language Model Pretraining": approach
+ *           (접근 방법) for formats, amax cache, T, rounding, zero-scale rule, 2D weights and
+ *           the GEMM model; key contributions (핵심 기여) for the 137x / 30x headroom.
+ *  [MXFP4]  "技術概要：MXFP4 による大規模言語モデルの事前学習": method (手法) for the
+ *           fprop / dgrad / wgrad GEMMs and the deterministic H16 / H32 Hadamard rotation.
+ *  [HOPPER] "Practical FP4 Training for Large-Scale MoE Models on Hopper GPUs":
+ *           methodology (방법론) for MXFP4 (E2M1, block 32) and fused transposed quantization.
+ *  [FUSION] "Format-Aware Fusion for Fast FP4 Pretraining": abstract, for producers that
+ *           write the consumer's layout and for fixed-sign 32-value Hadamard wgrad
+ *           preconditioning.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are device pointers owned by the caller; the library allocates
+ *    and frees nothing and keeps no state between calls.
+ *  - Work is enqueued on ``stream`` (a hipStream_t; NULL = the null stream) and ordered on
+ *    it; no call synchronises the host or copies device data to the host.
+ *  - Arguments are validated before anything is enqueued; an invalid call returns a
+ *    non-zero fp4_status, enqueues nothing, and sets a thread-local message readable with
+ *    fp4_last_error(). A failed launch returns FP4_EHIP.
+ *  - Matrices are row-major. Packed E2M1 payloads store element 2j of a row in the low
+ *    nibble and 2j+1 in the high nibble of byte j (sign in bit 3 of each nibble).
+ *  - Device pointers must be 16-byte aligned, except amax/g scalars (4-byte).
+ *  - Calls are thread-safe; concurrent calls on different streams that write the same
+ *    buffers race, as with any stream-ordered API.
+ */
+#ifndef FP4BS_H
+#define FP4BS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP4BS_ABI_VERSION 1
+
+typedef enum {
+  FP4_OK = 0,
+  FP4_EINVAL = 1,        /* null pointer, bad size, bad enum value */
+  FP4_EUNSUPPORTED = 2,  /* valid but unsupported combination (e.g. E8M0 with block 16) */
+  FP4_EALIGN = 3,        /* misaligned pointer or leading dimension */
+  FP4_EHIP = 4           /* a HIP runtime call or kernel launch failed */
+} fp4_status;
+
+/* Block-scale formats [UE5M3 approach; HOPPER methodology]. */
+typedef enum {
+  FP4_UE5M3 = 0,  /* unsigned E5M3, bias 15, max 61440; block 16 (main recipe) or 32 */
+  FP4_E4M3 = 1,   /* E4M3 (bias 7, max 448) with an FP32 tensor scale; block 16 or 32 */
+  FP4_E8M0 = 2    /* power-of-two MX scale, block 32, no tensor scale (MXFP4) */
+} fp4_scale_fmt;
+
+/* Which operand view a quantization produces. */
+typedef enum {
+  FP4_VIEW_ROW = 0,    /* x [rows x cols] -> operand [rows x cols], blocks along cols (fprop X, dgrad dY) */
+  FP4_VIEW_COL = 1,    /* x [rows x cols] -> operand x^T [cols x rows], blocks along rows = tokens
+                          (wgrad operands dY^T and X^T), optional Hadamard along rows */
+  FP4_VIEW_TILE2D = 2  /* weight w [rows x cols] -> 16x16-tile scales shared by the forward
+                          operand w [rows x cols] and the dgrad operand w^T [cols x rows] */
+} fp4_view;
+
+typedef enum { FP4_IN_BF16 = 0, FP4_IN_FP32 = 1 } fp4_in_dtype;
+
+/* How an operand's scale codes map to its (row, K-block) pairs. */
+typedef enum {
+  FP4_SCALES_1D = 0,    /* s[row * (k/block) + kb] */
+  FP4_SCALES_2D = 1,    /* forward weight view: s[(row/16) * (k/16) + kb] */
+  FP4_SCALES_2D_T = 2   /* transposed weight view: s[kb * (rows/16) + row/16] */
+} fp4_scale_layout;
+
+/* Per-call quantization recipe. */
+typedef struct {
+  int32_t fmt;         /* fp4_scale_fmt */
+  int32_t block;       /* 16 or 32 (E8M0 requires 32; TILE2D requires 16) */
+  int32_t view;        /* fp4_view */
+  int32_t stochastic;  /* 0: nearest-even payload; 1: stochastic rounding (ROW/COL only;
+                          the recipe uses it for the upstream gradient dY only) */
+  int32_t hadamard_n;  /* 0, 16 or 32: unnormalised Sylvester FWHT along tokens before
+                          quantizing; COL view only [MXFP4 method; FUSION abstract] */
+  float T;             /* scale target: the cached amax maps to block-scale value T
+                          (448 default, 2048 override); ignored for E8M0 */
+  uint64_t seed;       /* stochastic rounding: Philox-4x32-10 key */
+  uint64_t offset;     /* stochastic rounding: counter words 2-3 (e.g. step*8 + view id) */
+} fp4_quant_cfg;
+
+/* A quantized GEMM operand: K-contiguous payload [rows x k/2] plus scale codes. */
+typedef struct {
+  const uint8_t* q;    /* device, packed E2M1 [rows x k/2] */
+  const uint8_t* s;    /* device, scale codes, layout per scale_layout */
+  const float* g;      /* device, tensor decode scale (1 float); NULL means 1.0 */
+  int32_t fmt;         /* fp4_scale_fmt */
+  int32_t block;       /* 16 or 32 */
+  int32_t scale_layout;/* fp4_scale_layout */
+  int32_t reserved;
+  int64_t rows;        /* M (or N) */
+  int64_t k;           /* contraction length; multiple of 64 */
+} fp4_operand;
+
+/* Per-operand sample-and-hold amax cache; both fields live in device memory. */
+typedef struct {
+  float* amax;         /* cached amax A */
+  int32_t* valid;      /* 0 = empty (start or resume: the cache is not checkpointed) */
+  int32_t D;           /* sample period (50 delayed, 1 current) */
+} fp4_amax_cache;
+
+/*
+ * fp4_quantize - block-scaled FP4 quantization of one tensor [UE5M3 approach].
+ *
+ *   x        device, rows x cols elements of x_dtype, row stride ld (elements, >= cols,
+ *            ld*elem_size multiple of 16 bytes)
+ *   d_amax   device float: the cached amax A used for the scales (UE5M3/E4M3; may be NULL
+ *            for E8M0)
+ *   q        ROW/TILE2D: [rows x cols/2] bytes; COL: [cols x rows/2] bytes
+ *   s        ROW: [rows x cols/B]; COL: [cols x rows/B]; TILE2D: [rows/16 x cols/16] codes
+ *   q_t      TILE2D only: the transposed (dgrad) payload [cols x rows/2]; NULL otherwise
+ *   d_g      device float receiving the tensor decode scale g = 1/s_enc (1 for E8M0); may be NULL
+ *   d_amax_obs  optional device float receiving the observed max|x| of this tensor (after
+ *            the Hadamard rotation when enabled); overwritten
+ * Arithmetic (float32, nearest-even): s_enc = 6T/A, s_blk = T/A, g = 1/s_enc (all 1 when A
+ * is 0 or not finite or 6T/A overflows); block scale S = enc(amax_b*s_blk) saturating,
+ * replaced by 1 if it encodes to 0; payload E2M1(x * (s_enc/S)). E8M0: exponent
+ * floor(log2 amax_b) - 2 clamped to [-127, 127], 0 for a zero block; payload E2M1(x * 2^-E).
+ * Stochastic rounding draws 16 bits per element from Philox-4x32-10 with counter
+ * (i>>3, offset) for logical operand index i, word (i>>1)&3, half i&1.
+ * Requires: cols % B == 0 (ROW), rows % B == 0 and rows % hadamard_n == 0 (COL),
+ * rows % 16 == 0 and cols % 16 == 0 (TILE2D). Empty tensors are a no-op (g is still written).
+ */
+fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld,
+                        const fp4_quant_cfg* cfg, const float* d_amax,
+                        uint8_t* q, uint8_t* s, uint8_t* q_t, float* d_g, float* d_amax_obs,
+                        void* stream);
+
+/* fp4_quantize_sizes - byte sizes of q, s and q_t for a call with these arguments (host only). */
+fp4_status fp4_quantize_sizes(int64_t rows, int64_t cols, const fp4_quant_cfg* cfg,
+                              size_t* q_bytes, size_t* s_bytes, size_t* qt_bytes);
+
+/*
+ * fp4_tensor_amax - d_amax_out = max|x| over rows x cols, after the blockwise FWHT along rows
+ * when hadamard_n is 16 or 32 (the amax that a COL-view quantization with that rotation
+ * sees). Overwrites *d_amax_out. [UE5M3 approach: per-operand amax sampled every D steps]
+ */
+fp4_status fp4_tensor_amax(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld,
+                           int32_t hadamard_n, float* d_amax_out, void* stream);
+
+/*
+ * amax_cache_update - sample-and-hold [UE5M3 approach]: if the cache is empty or
+ * step % D == 0, A <- *d_amax_obs and the cache becomes valid; otherwise A is held.
+ * The decision is taken on the device (the host need not know the valid flag).
+ */
+fp4_status amax_cache_update(const fp4_amax_cache* cache, int64_t step, const float* d_amax_obs, void* stream);
+
+/* amax_cache_reset - mark the cache empty (a resumed run samples on first use). */
+fp4_status amax_cache_reset(const fp4_amax_cache* cache, void* stream);
+
+/*
+ * The three GEMMs [UE5M3 approach, GEMM model; MXFP4 method]. Each computes
+ * C[M x N] = A[M x K] . B[N x K]^T into row-major float32 c (ldc = N) from two operands
+ * with the same fmt and block, K % 64 == 0:
+ *   for every 64-product group: block partials T_b = S_a S_b sum(q_a q_b) are exact; the
+ *   group's partials are added in K order in float32 with round-to-nearest-even; groups
+ *   are accumulated in K order with float32 round-toward-zero; optionally the result is
+ *   canonicalised to round_half_even(1024 c)/1024 (canon != 0); finally
+ *   c = acc * float32(g_a * g_b) [* 1/hadamard_n for wgrad], rounded to nearest-even.
+ * Exact results require every block partial and group sum to stay inside the float32
+ * normal range (always true for UE5M3/E4M3; for E8M0, combined block exponents within
+ * about +-100).
+ *
+ * fp4_gemm_fprop: Y = X . W^T. x: ROW-view activation (1D scales); w: weight forward view
+ *                 (TILE2D q with FP4_SCALES_2D, or a ROW-view weight with 1D scales).
+ * fp4_gemm_dgrad: dX = dY . W. dy: ROW-view upstream gradient; wt: the weight's transposed
+ *                 payload q_t with FP4_SCALES_2D_T (or any 1D-scaled [N x K] operand).
+ * fp4_gemm_wgrad: dW = dY^T . X. dyt, xt: COL-view operands (1D scales along tokens);
+ *                 hadamard_n (0/16/32) must match the rotation used to quantize both.
+ */
+fp4_status fp4_gemm_fprop(const fp4_operand* x, const fp4_operand* w, float* y, int32_t canon, void* stream);
+fp4_status fp4_gemm_dgrad(const fp4_operand* dy, const fp4_operand* wt, float* dx, int32_t canon, void* stream);
+fp4_status fp4_gemm_wgrad(const fp4_operand* dyt, const fp4_operand* xt, float* dw, int32_t hadamard_n,
+                          int32_t canon, void* stream);
+
+/*
+ * fp4_debug_encode - runs the device encoders on n float32 inputs, for parity tests only.
+ *   which 0: E2M1 nearest-even payload code of x (one byte per input, sign in bit 3)
+ *   which 1: UE5M3 scale code of x (x >= 0), nearest-even, saturating (no zero rule)
+ *   which 2: E4M3 scale code of x (x >= 0), nearest-even, saturating (no zero rule)
+ *   which 3: E8M0 block exponent code of x (x >= 0) as used for a block maximum
+ *   which 4: stochastic E2M1 code of x with 16-bit draw u16[i] (u16 required)
+ */
+fp4_status fp4_debug_encode(const float* x, const uint16_t* u16, int64_t n, int32_t which, uint8_t* out,
+                            void* stream);
+
+/* Thread-local description of the last error on this thread ("" if none). */
+const char* fp4_last_error(void);
+
+/* FP4BS_ABI_VERSION of the loaded library. */
+int32_t fp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP4BS_H */

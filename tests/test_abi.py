@@ -1,0 +1,142 @@
+"""The C ABI on the host: the library loads, exports every function include/fp4bs.h declares,
+and rejects invalid arguments before enqueuing anything (no GPU needed for these paths)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from fp4_block_scaled_tensor_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4bs.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libfp4bs.so is not built; run `python -m fp4_block_scaled_tensor_amd.build`")
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:fp4_status|const char\*|int32_t)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_and_binding_agree():
+    decl = declared_functions()
+    assert set(decl) == set(_lib.EXPORTED), decl
+    assert len(decl) == 11
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_abi_version(lib):
+    assert lib.fp4_abi_version() == _lib.ABI_VERSION
+
+
+def cfg(fmt=0, block=16, view=0, sr=0, hn=0, T=448.0):
+    return _lib.QuantCfg(fmt, block, view, sr, hn, T, 0, 0)
+
+
+def test_quantize_sizes(lib):
+    q, s, qt = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    c = cfg()
+    assert lib.fp4_quantize_sizes(8192, 4096, ctypes.byref(c), ctypes.byref(q), ctypes.byref(s), ctypes.byref(qt)) == 0
+    assert (q.value, s.value, qt.value) == (8192 * 2048, 8192 * 256, 0)
+    c = cfg(view=2)
+    assert lib.fp4_quantize_sizes(14336, 4096, ctypes.byref(c), ctypes.byref(q), ctypes.byref(s), ctypes.byref(qt)) == 0
+    assert (q.value, s.value, qt.value) == (14336 * 2048, 896 * 256, 14336 * 2048)
+    c = cfg(fmt=2, block=32, view=1)
+    assert lib.fp4_quantize_sizes(8192, 4096, ctypes.byref(c), ctypes.byref(q), ctypes.byref(s), ctypes.byref(qt)) == 0
+    assert (q.value, s.value) == (4096 * 4096, 4096 * 256)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fmt=2, block=16), _lib.FP4_EUNSUPPORTED),      # E8M0 needs block 32
+    (dict(block=8), _lib.FP4_EUNSUPPORTED),
+    (dict(fmt=7), _lib.FP4_EINVAL),
+    (dict(view=2, block=32), _lib.FP4_EUNSUPPORTED),     # 2D tiles are 16x16
+    (dict(view=2, sr=1), _lib.FP4_EUNSUPPORTED),         # weights: nearest-even only
+    (dict(hn=16), _lib.FP4_EUNSUPPORTED),                # Hadamard only on the COL view
+    (dict(view=1, hn=8), _lib.FP4_EINVAL),
+    (dict(T=-1.0), _lib.FP4_EINVAL),
+])
+def test_quantize_rejects_bad_config(lib, kw, status):
+    c = cfg(**kw)
+    st = lib.fp4_quantize(ctypes.c_void_p(16), 0, 64, 64, 64, ctypes.byref(c), ctypes.c_void_p(16),
+                          ctypes.c_void_p(16), ctypes.c_void_p(16), None, None, None, None)
+    assert st == status
+    assert lib.fp4_last_error().decode()
+
+
+def test_quantize_rejects_bad_shapes_and_pointers(lib):
+    c = cfg()
+    P = ctypes.c_void_p(4096)
+    assert lib.fp4_quantize(P, 0, 64, 40, 40, ctypes.byref(c), P, P, P, None, None, None, None) == _lib.FP4_EINVAL
+    assert lib.fp4_quantize(P, 0, 64, 64, 32, ctypes.byref(c), P, P, P, None, None, None, None) == _lib.FP4_EINVAL
+    assert lib.fp4_quantize(None, 0, 64, 64, 64, ctypes.byref(c), P, P, P, None, None, None, None) == _lib.FP4_EINVAL
+    assert lib.fp4_quantize(ctypes.c_void_p(4098), 0, 64, 64, 64, ctypes.byref(c), P, P, P, None, None, None,
+                            None) == _lib.FP4_EALIGN
+    assert lib.fp4_quantize(P, 0, 64, 64, 68, ctypes.byref(c), P, P, P, None, None, None, None) == _lib.FP4_EALIGN
+    assert lib.fp4_quantize(P, 0, 64, 64, 64, ctypes.byref(c), None, P, P, None, None, None, None) == _lib.FP4_EINVAL
+    assert lib.fp4_quantize(P, 3, 64, 64, 64, ctypes.byref(c), P, P, P, None, None, None, None) == _lib.FP4_EINVAL
+    c2 = cfg(view=1)
+    assert lib.fp4_quantize(P, 0, 40, 64, 64, ctypes.byref(c2), P, P, P, None, None, None, None) == _lib.FP4_EINVAL
+    c3 = cfg(view=2)
+    assert lib.fp4_quantize(P, 0, 64, 64, 64, ctypes.byref(c3), P, P, P, None, None, None, None) == _lib.FP4_EINVAL
+    assert "q_t" in lib.fp4_last_error().decode()
+
+
+def op(rows=64, k=128, fmt=0, block=16, layout=0, q=4096, s=4096):
+    return _lib.Operand(q, s, None, fmt, block, layout, 0, rows, k)
+
+
+def test_gemm_rejects_bad_operands(lib):
+    y = ctypes.c_void_p(4096)
+    a, b = op(), op(k=192)
+    assert lib.fp4_gemm_fprop(ctypes.byref(a), ctypes.byref(b), y, 0, None) == _lib.FP4_EINVAL      # K mismatch
+    a, b = op(k=96), op(k=96)
+    assert lib.fp4_gemm_fprop(ctypes.byref(a), ctypes.byref(b), y, 0, None) == _lib.FP4_EINVAL      # K % 64
+    a, b = op(), op(fmt=1)
+    assert lib.fp4_gemm_fprop(ctypes.byref(a), ctypes.byref(b), y, 0, None) == _lib.FP4_EUNSUPPORTED
+    a, b = op(), op(layout=2)
+    assert lib.fp4_gemm_fprop(ctypes.byref(a), ctypes.byref(b), y, 0, None) == _lib.FP4_EUNSUPPORTED
+    assert lib.fp4_gemm_dgrad(ctypes.byref(op()), ctypes.byref(op(layout=1)), y, 0, None) == _lib.FP4_EUNSUPPORTED
+    assert lib.fp4_gemm_wgrad(ctypes.byref(op()), ctypes.byref(op()), y, 8, 0, None) == _lib.FP4_EINVAL
+    assert lib.fp4_gemm_fprop(ctypes.byref(op(q=4097)), ctypes.byref(op()), y, 0, None) == _lib.FP4_EALIGN
+    assert lib.fp4_gemm_fprop(ctypes.byref(op()), ctypes.byref(op()), None, 0, None) == _lib.FP4_EINVAL
+    assert lib.fp4_gemm_fprop(ctypes.byref(op(fmt=2, block=32, layout=1, rows=64)), ctypes.byref(op(fmt=2, block=32)),
+                              y, 0, None) == _lib.FP4_EUNSUPPORTED
+    assert lib.fp4_gemm_fprop(None, ctypes.byref(op()), y, 0, None) == _lib.FP4_EINVAL
+
+
+def test_gemm_empty_is_noop(lib):
+    assert lib.fp4_gemm_fprop(ctypes.byref(op(rows=0)), ctypes.byref(op()), None, 0, None) == _lib.FP4_OK
+
+
+def test_cache_and_debug_validation(lib):
+    c = _lib.AmaxCacheC(None, None, 50)
+    assert lib.amax_cache_update(ctypes.byref(c), 0, ctypes.c_void_p(16), None) == _lib.FP4_EINVAL
+    c = _lib.AmaxCacheC(16, 16, 0)
+    assert lib.amax_cache_update(ctypes.byref(c), 0, ctypes.c_void_p(16), None) == _lib.FP4_EINVAL
+    assert lib.fp4_debug_encode(None, None, 10, 0, None, None) == _lib.FP4_EINVAL
+    assert lib.fp4_tensor_amax(ctypes.c_void_p(16), 0, 64, 64, 64, 8, ctypes.c_void_p(16), None) == _lib.FP4_EINVAL
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import numpy as np
+    import torch
+    import fp4_block_scaled_tensor_amd as fp4
+    with pytest.raises(ValueError, match="device tensors"):
+        fp4.quantize(torch.zeros((16, 64), dtype=torch.bfloat16), fp4.UE5M3, 16, fp4.ROW,
+                     amax=torch.ones(1))

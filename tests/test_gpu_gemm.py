@@ -1,0 +1,193 @@
+"""GEMM parity: HIP kernels vs the oracle's group model, bit for bit; float64 tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle import formats as OF
+from tests._helpers import (assert_f32_bits_equal, dev_input, dev_scalar, qtensor_from_oracle, random_operand)
+
+pytestmark = pytest.mark.gpu
+
+fp4 = pytest.importorskip("fp4_block_scaled_tensor_amd")
+
+
+def _oracle_y(qa, qb, va="1d", vb="1d", canon=False, hadamard_n=0, rows=None):
+    a, sa = oracle.operand_from_quant(qa, va)
+    b, sb = oracle.operand_from_quant(qb, vb)
+    if rows is not None:
+        a, sa = a[rows], sa[rows]
+    alpha = oracle.output_scale(qa.g, qb.g, hadamard_n)
+    return oracle.gemm_model(a, sa, b, sb, qa.block, alpha=alpha, canon=canon)
+
+
+STRESS = [
+    # fmt, block, spread, M, N, K, canon
+    (OF.UE5M3, 16, 1, 64, 64, 64, False),
+    (OF.UE5M3, 16, 6, 200, 136, 320, False),
+    (OF.UE5M3, 16, 3, 129, 257, 1024, True),
+    (OF.UE5M3, 32, 5, 96, 160, 576, False),
+    (OF.E4M3, 16, 4, 130, 70, 448, False),
+    (OF.E4M3, 32, 2, 64, 128, 256, True),
+    (OF.E8M0, 32, 2, 200, 136, 320, False),
+    (OF.E8M0, 32, 6, 128, 128, 512, False),
+    (OF.E8M0, 32, 24, 160, 96, 1024, True),
+]
+
+
+@pytest.mark.parametrize("fmt,block,spread,M,N,K,canon", STRESS)
+def test_group_model_stress(fmt, block, spread, M, N, K, canon):
+    """Operands built in the quantized domain with wide scale spreads inside each group,
+    ragged M/N and a partial last K stage: every rounding rule of the model is exercised."""
+    rng = np.random.default_rng(M * 7 + N * 3 + K + spread)
+    qa = random_operand(rng, M, K, fmt, block, spread, zero_frac=0.1)
+    qb = random_operand(rng, N, K, fmt, block, spread)
+    qa.g, qb.g = np.float32(0.75), np.float32(1.25)
+    want = _oracle_y(qa, qb, canon=canon)
+    got = fp4.gemm_fprop(qtensor_from_oracle(qa), qtensor_from_oracle(qb), canon=canon)
+    torch.cuda.synchronize()
+    assert_f32_bits_equal(got, want, f"fmt={fmt} B={block} spread={spread} {M}x{N}x{K}")
+
+
+def test_same_sign_rtz_drift():
+    """All-positive products: every cross-group add truncates in the same direction."""
+    rng = np.random.default_rng(5)
+    for fmt, block, spread in ((OF.UE5M3, 16, 6), (OF.E8M0, 32, 12)):
+        qa = random_operand(rng, 64, 4096, fmt, block, spread)
+        qb = random_operand(rng, 64, 4096, fmt, block, spread)
+        qa.codes &= 7
+        qb.codes &= 7
+        want = _oracle_y(qa, qb)
+        got = fp4.gemm_fprop(qtensor_from_oracle(qa), qtensor_from_oracle(qb))
+        torch.cuda.synchronize()
+        assert_f32_bits_equal(got, want, f"drift fmt={fmt}")
+        exact, _ = oracle.gemm_fp64(*oracle.operand_from_quant(qa), *oracle.operand_from_quant(qb), block)
+        assert np.any(want.astype(np.float64) < exact)    # truncation really happened
+
+
+def test_tiny_end_to_end():
+    """256x256 fp32 X, W ~ N(0,1); UE5M3 block 16, T = 448, nearest-even; Y = X W^T; W both
+    with 1D and with 2D 16x16 scales."""
+    cfg = synth.make_config(1)
+    X, W = cfg["X"], cfg["W"]
+    Ax, Aw = oracle.tensor_amax(X.values), oracle.tensor_amax(W.values)
+    qx = fp4.quantize(dev_input(X), fp4.UE5M3, 16, fp4.ROW, amax=dev_scalar(Ax), T=448)
+    qw = fp4.quantize(dev_input(W), fp4.UE5M3, 16, fp4.ROW, amax=dev_scalar(Aw), T=448)
+    w2, w2t = fp4.quantize(dev_input(W), fp4.UE5M3, 16, fp4.TILE2D, amax=dev_scalar(Aw), T=448)
+    y1 = fp4.gemm_fprop(qx, qw)
+    y2 = fp4.gemm_fprop(qx, w2)
+    y3 = fp4.gemm_fprop(qx, w2, canon=True)
+    torch.cuda.synchronize()
+    rx = oracle.quantize_1d(X.values, OF.UE5M3, 16, amax=Ax, T=448)
+    rw = oracle.quantize_1d(W.values, OF.UE5M3, 16, amax=Aw, T=448)
+    rw2 = oracle.quantize_2d(W.values, OF.UE5M3, amax=Aw, T=448)
+    assert_f32_bits_equal(y1, _oracle_y(rx, rw), "1D weight")
+    assert_f32_bits_equal(y2, _oracle_y(rx, rw2, vb="2d"), "2D weight")
+    assert_f32_bits_equal(y3, _oracle_y(rx, rw2, vb="2d", canon=True), "2D weight, canonicalised")
+    a, sa = oracle.operand_from_quant(rx)
+    b, sb = oracle.operand_from_quant(rw)
+    y64, sabs = oracle.gemm_fp64(a, sa, b, sb, 16, rx.g, rw.g)
+    assert np.all(np.abs(y1.cpu().numpy() - y64) <= 1e-6 * sabs)
+
+
+@pytest.mark.parametrize("fmt,block", [(OF.UE5M3, 16), (OF.E4M3, 16), (OF.E8M0, 32)])
+def test_format_sweep_2048(fmt, block):
+    """2048^3 bf16 N(0,1) with 0.1% outlier columns, each format, quantize + GEMM on the GPU;
+    128 output rows against the oracle, all rows against float64 within tolerance."""
+    cfg = synth.make_config(2)
+    X, W = cfg["X"], cfg["W"]
+    Ax, Aw = oracle.tensor_amax(X.values), oracle.tensor_amax(W.values)
+    qx = fp4.quantize(dev_input(X), fmt, block, fp4.ROW, amax=dev_scalar(Ax), T=448)
+    qw = fp4.quantize(dev_input(W), fmt, block, fp4.ROW, amax=dev_scalar(Aw), T=448)
+    y = fp4.gemm_fprop(qx, qw)
+    y_again = fp4.gemm_fprop(qx, qw)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    assert np.array_equal(y.view(np.uint32), y_again.cpu().numpy().view(np.uint32))   # run-to-run
+    rx = oracle.quantize_1d(X.values, fmt, block, amax=Ax, T=448)
+    rw = oracle.quantize_1d(W.values, fmt, block, amax=Aw, T=448)
+    rows = np.r_[0:64, 1000:1032, 2016:2048]
+    assert_f32_bits_equal(y[rows], _oracle_y(rx, rw, rows=rows), f"fmt {fmt}")
+    a, sa = oracle.operand_from_quant(rx)
+    b, sb = oracle.operand_from_quant(rw)
+    y64, sabs = oracle.gemm_fp64(a[rows], sa[rows], b, sb, block, rx.g, rw.g)
+    assert np.all(np.abs(y[rows] - y64) <= 1e-6 * sabs)
+
+
+def test_backward_dgrad_wgrad():
+    """dX = dY W (2D weight, transposed copy) and dW = dY^T X (stochastic dY, T = 2048 for the
+    wgrad dY view), with and without H16, at a reduced token count."""
+    T_, Fo, Fi = 512, 256, 384
+    dY = synth.Tensor("dY", synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(synth.normal((T_, Fo), 1e-3, 401))), "bf16")
+    W = synth.Tensor("W", synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(synth.normal((Fo, Fi), 0.02, 402))), "bf16")
+    X = synth.Tensor("X", synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(synth.student_t((T_, Fi), 3.0, 403))), "bf16")
+    Ady, Aw = oracle.tensor_amax(dY.values), oracle.tensor_amax(W.values)
+    # dgrad
+    qdy = fp4.quantize(dev_input(dY), fp4.UE5M3, 16, fp4.ROW, amax=dev_scalar(Ady), T=448, stochastic=True, seed=42,
+                       offset=0)
+    _, wt = fp4.quantize(dev_input(W), fp4.UE5M3, 16, fp4.TILE2D, amax=dev_scalar(Aw), T=448)
+    dx = fp4.gemm_dgrad(qdy, wt)
+    torch.cuda.synchronize()
+    rdy = oracle.quantize_1d(dY.values, OF.UE5M3, 16, amax=Ady, T=448, rounding="sr", seed=42, offset=0)
+    rw = oracle.quantize_2d(W.values, OF.UE5M3, amax=Aw, T=448)
+    assert_f32_bits_equal(dx, _oracle_y(rdy, rw, vb="2dT"), "dgrad")
+    # wgrad
+    for hn in (0, 16, 32):
+        Ay, Ax = oracle.tensor_amax(dY.values, hn), oracle.tensor_amax(X.values, hn)
+        qdyt = fp4.quantize(dev_input(dY), fp4.UE5M3, 16, fp4.COL, amax=dev_scalar(Ay), T=2048, stochastic=True,
+                            seed=42, offset=1, hadamard_n=hn)
+        qxt = fp4.quantize(dev_input(X), fp4.UE5M3, 16, fp4.COL, amax=dev_scalar(Ax), T=448, hadamard_n=hn)
+        dw = fp4.gemm_wgrad(qdyt, qxt, hadamard_n=hn)
+        torch.cuda.synchronize()
+        rdyt = oracle.quantize_col(dY.values, OF.UE5M3, 16, amax=Ay, T=2048, rounding="sr", seed=42, offset=1,
+                                   hadamard_n=hn)
+        rxt = oracle.quantize_col(X.values, OF.UE5M3, 16, amax=Ax, T=448, hadamard_n=hn)
+        assert_f32_bits_equal(dw, _oracle_y(rdyt, rxt, hadamard_n=hn), f"wgrad H{hn}")
+
+
+def test_mxfp4_backward():
+    T_, Fo, Fi = 256, 128, 192
+    dY = synth.normal((T_, Fo), 1e-3, 11)
+    X = synth.student_t((T_, Fi), 3.0, 12)
+    W = synth.normal((Fo, Fi), 0.02, 13)
+    qdy = fp4.quantize(torch.from_numpy(dY).cuda(), fp4.E8M0, 32, fp4.ROW, stochastic=True, seed=42, offset=0)
+    qwt = fp4.quantize(torch.from_numpy(np.ascontiguousarray(W.T)).cuda(), fp4.E8M0, 32, fp4.ROW)
+    qdyt = fp4.quantize(torch.from_numpy(dY).cuda(), fp4.E8M0, 32, fp4.COL, stochastic=True, seed=42, offset=1,
+                        hadamard_n=16)
+    qxt = fp4.quantize(torch.from_numpy(X).cuda(), fp4.E8M0, 32, fp4.COL, hadamard_n=16)
+    dx = fp4.gemm_dgrad(qdy, qwt)
+    dw = fp4.gemm_wgrad(qdyt, qxt, hadamard_n=16)
+    torch.cuda.synchronize()
+    rdy = oracle.quantize_1d(dY, OF.E8M0, 32, rounding="sr", seed=42, offset=0)
+    rwt = oracle.quantize_1d(np.ascontiguousarray(W.T), OF.E8M0, 32)
+    rdyt = oracle.quantize_col(dY, OF.E8M0, 32, rounding="sr", seed=42, offset=1, hadamard_n=16)
+    rxt = oracle.quantize_col(X, OF.E8M0, 32, hadamard_n=16)
+    assert_f32_bits_equal(dx, _oracle_y(rdy, rwt), "mx dgrad")
+    assert_f32_bits_equal(dw, _oracle_y(rdyt, rxt, hadamard_n=16), "mx wgrad H16")
+
+
+@pytest.mark.parametrize("fmt,block", [(OF.UE5M3, 16), (OF.E8M0, 32)])
+def test_up_projection_full_size_sampled(fmt, block):
+    """The 8192 x 4096 -> 14336 up-projection in full on the GPU (UE5M3: 2D weight scales;
+    MXFP4: 1D block 32); 16 sampled output rows against the oracle."""
+    cfg = synth.make_config(3)
+    X, W = cfg["X"], cfg["W"]
+    Ax, Aw = oracle.tensor_amax(X.values), oracle.tensor_amax(W.values)
+    qx = fp4.quantize(dev_input(X), fmt, block, fp4.ROW, amax=dev_scalar(Ax), T=448)
+    if fmt == OF.UE5M3:
+        qw, _ = fp4.quantize(dev_input(W), fmt, 16, fp4.TILE2D, amax=dev_scalar(Aw), T=448)
+    else:
+        qw = fp4.quantize(dev_input(W), fmt, block, fp4.ROW)
+    y = fp4.gemm_fprop(qx, qw)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 2047, 4096, 5000, 6143, 7000, 8000, 8100, 8150, 8189, 8190, 8191, 3333])
+    y_rows = y[torch.from_numpy(rows).cuda()].cpu().numpy()
+    rx = oracle.quantize_1d(X.values[rows], fmt, block, amax=Ax, T=448)
+    if fmt == OF.UE5M3:
+        rw = oracle.quantize_2d(W.values, fmt, amax=Aw, T=448)
+        want = _oracle_y(rx, rw, vb="2d")
+    else:
+        rw = oracle.quantize_1d(W.values, fmt, block)
+        want = _oracle_y(rx, rw)
+    assert_f32_bits_equal(y_rows, want, f"up-projection fmt {fmt}")
