@@ -165,20 +165,19 @@ __device__ __forceinline__ TensorScales tensor_scales(const float* d_amax, float
 }
 
 // ---- FP32 round-mode control (MODE register bits [1:0]; [3:2] = f64/f16 stay nearest) ----
-// Inline asm with a memory clobber orders these against the volatile adds that depend on them.
+// The switch is inline asm; sched_barrier(0) on both sides keeps the scheduler from moving
+// any instruction (in particular the ordinary float additions whose rounding it selects)
+// across it. The additions themselves stay ordinary C++ so that the compiler inserts the
+// wait states an MFMA result needs before a VALU instruction reads it.
 __device__ __forceinline__ void mode_f32_rtz() {
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 3\n\ts_nop 3" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 __device__ __forceinline__ void mode_f32_rne() {
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 0\n\ts_nop 3" ::: "memory");
-}
-
-// a + b with whatever FP32 round mode is current; volatile so it cannot move across a
-// mode switch.
-__device__ __forceinline__ float add_in_mode(float a, float b) {
-  float r;
-  asm volatile("v_add_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 }  // namespace fp4k

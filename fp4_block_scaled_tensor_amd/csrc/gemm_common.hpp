@@ -6,9 +6,15 @@
 //
 // Tiling: a 256-thread workgroup owns a 128x128 output tile as 2x2 waves of 64x64; each
 // wave computes 2x2 MFMA tiles of 32x32. K advances by stages of 256 elements (4 groups,
-// 128 payload bytes per row), double-buffered through LDS with register prefetch. LDS
-// rows are 128 bytes; 16-byte chunk j of row r is stored at chunk j ^ (r & 7) so that
-// eight consecutive rows reading the same chunk hit distinct banks.
+// 128 payload bytes per row). Payload stages go straight from global memory into LDS with
+// global_load_lds_dwordx4 (no staging registers), double-buffered; the scale bytes of a
+// stage go through registers into a small LDS array. LDS payload rows are 128 bytes;
+// 16-byte chunk j of row r sits at chunk position j ^ (r & 7), so eight consecutive rows
+// reading the same logical chunk hit distinct banks.
+//
+// Workgroup order: 8 consecutive workgroup ids land on the 8 XCDs round-robin, so ids are
+// remapped to give each XCD a contiguous run of tiles, ordered in groups of 8 M-tiles:
+// consecutive workgroups on one XCD share the B tile and keep 8 A tiles hot in its L2.
 #pragma once
 #include "fp4_device.hpp"
 #include "launch.hpp"
@@ -19,51 +25,71 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int GT = 128;        // output tile edge per workgroup
 constexpr int KS = 256;        // K elements per stage
+constexpr int SGR = KS / 64;   // groups per stage
 constexpr int ROWB = KS / 2;   // payload bytes per row per stage
 constexpr int GNT = 256;       // threads per workgroup
+constexpr int TILE_BYTES = GT * ROWB;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * ROWB + ((chunk ^ (row & 7)) << 4); }
 
-// Prefetch one stage of a 128-row payload tile into registers (4 x 16 bytes per thread).
-__device__ __forceinline__ void stage_load(const uint8_t* __restrict__ q, int64_t rows, int64_t K, int64_t row0,
-                                           int64_t k0, uint4* reg) {
+// Issue the direct global->LDS loads of one stage of a 128-row payload tile. Each wave
+// fills 4 x 1024 contiguous LDS bytes; lane i of a 1024-byte piece writes LDS bytes
+// [16i, 16i+16), i.e. row 8p + i/8 at chunk position i%8, so it loads logical chunk
+// (i%8) ^ (row & 7). Rows past the matrix and chunks past K read clamped, valid addresses
+// (their values only reach outputs that are not stored, or groups that are not computed).
+__device__ __forceinline__ void stage_issue(const uint8_t* __restrict__ q, int64_t rows, int64_t K, int64_t row0,
+                                            int64_t k0, uint8_t* lds) {
   const int64_t ldq = K / 2, kb0 = k0 / 2;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int c = threadIdx.x + GNT * j;
-    const int row = c >> 3, ch = c & 7;
-    const int64_t gb = kb0 + ch * 16;
-    if (row0 + row < rows && gb < ldq) reg[j] = *reinterpret_cast<const uint4*>(q + (row0 + row) * ldq + gb);
-    else reg[j] = make_uint4(0, 0, 0, 0);
+    const int piece = w * 4 + j;                 // 0..15, 1024 bytes each
+    const int row = piece * 8 + (l >> 3);
+    const int pos = l & 7;
+    const int chunk = pos ^ (row & 7);
+    int64_t grow = row0 + row;
+    grow = grow < rows ? grow : rows - 1;
+    int64_t gb = kb0 + chunk * 16;
+    gb = gb < ldq ? gb : ldq - 16;
+    __builtin_amdgcn_global_load_lds(q + grow * ldq + gb, (lds_void*)(lds + piece * 1024), 16, 0, 0);
   }
 }
 
-__device__ __forceinline__ void stage_store(uint8_t* lds, const uint4* reg) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = threadIdx.x + GNT * j;
-    *reinterpret_cast<uint4*>(lds + swz(c >> 3, c & 7)) = reg[j];
-  }
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Workgroup id -> (m tile, n tile), XCD-aware grouped order.
+__device__ __forceinline__ void tile_coords(int64_t M, int64_t N, int64_t& m0, int64_t& n0) {
+  const int64_t ntm = (M + GT - 1) / GT, ntn = (N + GT - 1) / GT;
+  const int64_t T = ntm * ntn;
+  int64_t id = blockIdx.x;
+  if ((T & 7) == 0) id = (id & 7) * (T >> 3) + (id >> 3);
+  const int64_t GM = 8;
+  const int64_t gsize = GM * ntn;
+  const int64_t gid = id / gsize;
+  const int64_t first = gid * GM;
+  const int64_t gm = (ntm - first) < GM ? (ntm - first) : GM;
+  const int64_t r = id % gsize;
+  m0 = (first + r % gm) * GT;
+  n0 = (r / gm) * GT;
 }
 
-// Scale code of (row, K-block blk) for a given layout. blocks_per_row = K / block.
-__device__ __forceinline__ uint32_t scale_at(const uint8_t* __restrict__ s, int layout, int64_t row, int64_t blk,
-                                             int64_t rows, int64_t blocks_per_row) {
-  if (layout == 0) return s[row * blocks_per_row + blk];
-  if (layout == 1) return s[(row >> 4) * blocks_per_row + blk];
-  return s[blk * (rows >> 4) + (row >> 4)];
-}
-
-// Output element (row, col) of register r of a 32x32 MFMA tile in lane l.
+// Output row of register r of a 32x32 MFMA tile in lane l (column = l & 31).
 __device__ __forceinline__ int tile_row(int r, int l) { return (r >> 2) * 8 + (l >> 5) * 4 + (r & 3); }
 
 // Epilogue: nearest-even mode, optional canonicalisation, scale by alpha, store float32.
 __device__ __forceinline__ void store_tiles(float* __restrict__ c, int64_t M, int64_t N, int64_t m0, int64_t n0,
                                             v16f (&acc)[2][2], const float* ga, const float* gb, int canon,
                                             int hadamard_n) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(acc[i][j][r]));   // accumulation done before the switch
   mode_f32_rne();
   float a = ga ? *ga : 1.0f;
   float b = gb ? *gb : 1.0f;

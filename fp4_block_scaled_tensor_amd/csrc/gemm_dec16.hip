@@ -21,36 +21,68 @@ namespace fp4k {
 
 // 8 E2M1 codes (one dword, element 0 in the low nibble) times scale value S -> 8 bf16.
 __device__ __forceinline__ v8bf decode8(uint32_t codes, float S) {
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  v2f qq[4];
+  qq[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+  qq[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+  qq[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+  qq[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
   uint32_t o[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    float2 q;
-    typedef float v2f __attribute__((ext_vector_type(2)));
-    v2f qq;
-    if (j == 0) qq = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
-    else if (j == 1) qq = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
-    else if (j == 2) qq = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
-    else qq = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
-    q.x = qq.x * S;   // exact
-    q.y = qq.y * S;
-    o[j] = __builtin_amdgcn_perm(__float_as_uint(q.y), __float_as_uint(q.x), 0x07060302u);
+    const float x = qq[j].x * S;   // exact
+    const float y = qq[j].y * S;
+    o[j] = __builtin_amdgcn_perm(__float_as_uint(y), __float_as_uint(x), 0x07060302u);
   }
   return __builtin_bit_cast(v8bf, v4u{o[0], o[1], o[2], o[3]});
 }
 
+// The 16 scale codes (one per 16-wide K slice; block 32 repeats each code twice) of one
+// operand row for stage st, in the operand's scale layout. Rows past the matrix and slices
+// past K get the code of 1.0.
 template <int FMT, int B>
-__global__ __launch_bounds__(GNT) void k_gemm_dec16(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
-                                                    int la, const uint8_t* __restrict__ qb,
-                                                    const uint8_t* __restrict__ sb, int lb,
-                                                    const float* __restrict__ ga, const float* __restrict__ gb,
-                                                    float* __restrict__ c, int64_t M, int64_t N, int64_t K, int canon,
-                                                    int hadamard_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t lA[2][GT * ROWB];
-  __shared__ __attribute__((aligned(16))) uint8_t lB[2][GT * ROWB];
+__device__ __forceinline__ uint4 scale_row16(const uint8_t* __restrict__ s, int layout, int64_t row, int64_t rows,
+                                             int64_t K, int64_t st) {
+  const uint32_t one = ScaleFmt<FMT>::ONE;
+  if (row >= rows) {
+    const uint32_t w = one * 0x01010101u;
+    return make_uint4(w, w, w, w);
+  }
+  const int64_t k16 = K / 16;        // 16-wide slices per row
+  uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t slice = st * 16 + i;
+    uint32_t b = one;
+    if (slice < k16) {
+      if (layout == 0) b = s[row * (K / B) + slice * 16 / B];
+      else if (layout == 1) b = s[(row >> 4) * k16 + slice];
+      else b = s[slice * (rows >> 4) + (row >> 4)];
+    }
+    w[i >> 2] |= b << (8 * (i & 3));
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ uint32_t byte_of(const uint4& v, int i) {
+  const uint32_t w = i < 4 ? v.x : (i < 8 ? v.y : (i < 12 ? v.z : v.w));
+  return (w >> (8 * (i & 3))) & 0xFFu;
+}
+
+template <int FMT, int B>
+__global__ __launch_bounds__(GNT, 2) void k_gemm_dec16(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
+                                                       int la, const uint8_t* __restrict__ qb,
+                                                       const uint8_t* __restrict__ sb, int lb,
+                                                       const float* __restrict__ ga, const float* __restrict__ gb,
+                                                       float* __restrict__ c, int64_t M, int64_t N, int64_t K,
+                                                       int canon, int hadamard_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lA[2][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lB[2][TILE_BYTES];
+  __shared__ uint4 lS[2][2 * GT];   // 16 slice-scale codes per row: A rows then B rows
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * GT, n0 = (int64_t)blockIdx.x * GT;
-  const int64_t bpr = K / B;        // blocks per row (1D layouts)
+  int64_t m0, n0;
+  tile_coords(M, N, m0, n0);
   const int64_t ngroups = K / 64;
   const int64_t nstages = (K + KS - 1) / KS;
   const int half = l >> 5;
@@ -63,86 +95,79 @@ __global__ __launch_bounds__(GNT) void k_gemm_dec16(const uint8_t* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  uint4 pa[4], pb[4];
-  stage_load(qa, M, K, m0, 0, pa);
-  stage_load(qb, N, K, n0, 0, pb);
-  stage_store(lA[0], pa);
-  stage_store(lB[0], pb);
+  const bool srow_is_a = threadIdx.x < GT;
+  const int srow = threadIdx.x & (GT - 1);
+  uint4 sreg = srow_is_a ? scale_row16<FMT, B>(sa, la, m0 + srow, M, K, 0)
+                         : scale_row16<FMT, B>(sb, lb, n0 + srow, N, K, 0);
+  if (nstages > 0) {
+    stage_issue(qa, M, K, m0, 0, lA[0]);
+    stage_issue(qb, N, K, n0, 0, lB[0]);
+  }
+  lS[0][threadIdx.x] = sreg;
+  wait_vm();
   __syncthreads();
-
-  const int64_t arow[2] = {m0 + wm * 64 + (l & 31), m0 + wm * 64 + 32 + (l & 31)};
-  const int64_t bcol[2] = {n0 + wn * 64 + (l & 31), n0 + wn * 64 + 32 + (l & 31)};
-  // 2D layouts index scales by 16-element K-block and 16-row group
-  const int64_t bpr_a = la == 0 ? bpr : K / 16;
-  const int64_t bpr_b = lb == 0 ? bpr : K / 16;
 
   for (int64_t st = 0; st < nstages; ++st) {
     const int buf = (int)(st & 1);
     if (st + 1 < nstages) {
-      stage_load(qa, M, K, m0, (st + 1) * KS, pa);
-      stage_load(qb, N, K, n0, (st + 1) * KS, pb);
+      stage_issue(qa, M, K, m0, (st + 1) * KS, lA[buf ^ 1]);
+      stage_issue(qb, N, K, n0, (st + 1) * KS, lB[buf ^ 1]);
+      sreg = srow_is_a ? scale_row16<FMT, B>(sa, la, m0 + srow, M, K, st + 1)
+                       : scale_row16<FMT, B>(sb, lb, n0 + srow, N, K, st + 1);
     }
-    const int64_t g_end = (ngroups - st * 4) < 4 ? (ngroups - st * 4) : 4;
+    uint4 scA[2], scB[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      scA[t] = lS[buf][wm * 64 + t * 32 + (l & 31)];
+      scB[t] = lS[buf][GT + wn * 64 + t * 32 + (l & 31)];
+    }
+    const int g_end = (int)((ngroups - st * SGR) < SGR ? (ngroups - st * SGR) : SGR);
     for (int g = 0; g < g_end; ++g) {
-      const int64_t gg = st * 4 + g;
-      // G: group partial per tile; H: second 32-block partial (block 32 only)
-      v16f G[2][2], H[2][2];
+      // decoded bf16 fragments of the group's four 16-wide slices
+      v8bf fa[4][2], fb[4][2];
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) {
-        const int64_t kelem = gg * 64 + sub * 16;       // first K index of this 16-wide slice
-        const int64_t blk = kelem / B;
-        const int64_t blk16 = kelem / 16;
-        v8bf fa[2], fb[2];
+        const int off = g * 32 + sub * 8 + half * 4;   // payload byte inside the stage row
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int rowa = wm * 64 + t * 32 + (l & 31);
           const int rowb = wn * 64 + t * 32 + (l & 31);
-          const int off = g * 32 + sub * 8 + half * 4;  // payload byte inside the stage row
           const uint32_t ca = *reinterpret_cast<const uint32_t*>(lA[buf] + swz(rowa, off >> 4) + (off & 15));
           const uint32_t cb = *reinterpret_cast<const uint32_t*>(lB[buf] + swz(rowb, off >> 4) + (off & 15));
-          const uint32_t sca = arow[t] < M ? scale_at(sa, la, arow[t], la == 0 ? blk : blk16, M, bpr_a)
-                                           : ScaleFmt<FMT>::ONE;
-          const uint32_t scb = bcol[t] < N ? scale_at(sb, lb, bcol[t], lb == 0 ? blk : blk16, N, bpr_b)
-                                           : ScaleFmt<FMT>::ONE;
-          fa[t] = decode8(ca, dec_scale3<FMT>(sca));
-          fb[t] = decode8(cb, dec_scale3<FMT>(scb));
+          fa[sub][t] = decode8(ca, dec_scale3<FMT>(byte_of(scA[t], g * 4 + sub)));
+          fb[sub][t] = decode8(cb, dec_scale3<FMT>(byte_of(scB[t], g * 4 + sub)));
         }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const v16f T = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], v16f{}, 0, 0, 0);
-            if constexpr (B == 16) {
-              // ((T0 + T1) + T2) + T3, nearest-even
-              if (sub == 0) G[i][j] = T;
-              else
-#pragma unroll
-                for (int r = 0; r < 16; ++r) G[i][j][r] = add_in_mode(G[i][j][r], T[r]);
-            } else {
-              // (T0 + T1) + (T2 + T3): inner adds exact, outer nearest-even
-              if (sub == 0) G[i][j] = T;
-              else if (sub == 1)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) G[i][j][r] = add_in_mode(G[i][j][r], T[r]);
-              else if (sub == 2) H[i][j] = T;
-              else
-#pragma unroll
-                for (int r = 0; r < 16; ++r) G[i][j][r] = add_in_mode(G[i][j][r], add_in_mode(H[i][j][r], T[r]));
-            }
-          }
       }
-      mode_f32_rtz();
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j) {
+          // group partial of this tile, nearest-even
+          v16f G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][i], fb[0][j], v16f{}, 0, 0, 0);
+          if constexpr (B == 16) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = add_in_mode(acc[i][j][r], G[i][j][r]);
-      mode_f32_rne();
+            for (int sub = 1; sub < 4; ++sub) {
+              const v16f T = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sub][i], fb[sub][j], v16f{}, 0, 0, 0);
+#pragma unroll
+              for (int r = 0; r < 16; ++r) G[r] = G[r] + T[r];
+            }
+          } else {
+            const v16f T1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][j], v16f{}, 0, 0, 0);
+            const v16f T2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[2][i], fb[2][j], v16f{}, 0, 0, 0);
+            const v16f T3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[3][i], fb[3][j], v16f{}, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) G[r] = (G[r] + T1[r]) + (T2[r] + T3[r]);   // inner adds exact
+          }
+          // cross-group accumulation, toward zero
+          mode_f32_rtz();
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = acc[i][j][r] + G[r];
+          mode_f32_rne();
+        }
     }
     if (st + 1 < nstages) {
-      stage_store(lA[buf ^ 1], pa);
-      stage_store(lB[buf ^ 1], pb);
+      lS[buf ^ 1][threadIdx.x] = sreg;
+      wait_vm();
       __syncthreads();
     }
   }
@@ -151,9 +176,9 @@ __global__ __launch_bounds__(GNT) void k_gemm_dec16(const uint8_t* __restrict__ 
 
 template <int FMT, int B>
 static hipError_t launch_dec16(const GemmArgs& g) {
-  dim3 grid((unsigned)((g.N + GT - 1) / GT), (unsigned)((g.M + GT - 1) / GT));
-  hipLaunchKernelGGL((k_gemm_dec16<FMT, B>), grid, dim3(GNT), 0, g.stream, g.a.q, g.a.s, g.a.layout, g.b.q, g.b.s,
-                     g.b.layout, g.a.g, g.b.g, g.c, g.M, g.N, g.K, g.canon, g.hadamard_n);
+  const int64_t tiles = ((g.M + GT - 1) / GT) * ((g.N + GT - 1) / GT);
+  hipLaunchKernelGGL((k_gemm_dec16<FMT, B>), dim3((unsigned)tiles), dim3(GNT), 0, g.stream, g.a.q, g.a.s, g.a.layout,
+                     g.b.q, g.b.s, g.b.layout, g.a.g, g.b.g, g.c, g.M, g.N, g.K, g.canon, g.hadamard_n);
   return hipGetLastError();
 }
 

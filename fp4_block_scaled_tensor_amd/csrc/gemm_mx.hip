@@ -10,13 +10,19 @@
 // exact two-block sum T0 + T1 whenever the combined block exponents of the two blocks,
 // (ea0+eb0) - (ea1+eb1), differ by at most 10: the sum then has at most 24 significant
 // bits, so it equals the model's nearest-even group partial. When a wave's rows or
-// columns could exceed that gap in a group, the group is instead computed as two MFMAs
-// with the other K-block's payload zeroed (each an exact 32-block partial) and the two
-// are added in float32 round-to-nearest-even. Group partials are then accumulated with
+// columns could exceed that gap in a group, the group is instead computed per tile as two
+// MFMAs with the other K-block's payload zeroed (each an exact 32-block partial) and the
+// two are added in float32 round-to-nearest-even. Group partials are accumulated with
 // v_add_f32 under round-toward-zero (MODE register), in K order.
+//
+// The fast path's adds are plain float additions: the whole K loop runs in
+// round-toward-zero mode and contains no other rounding-sensitive operation. The rare
+// slow path switches to nearest-even around its own inline-asm additions.
 #include "gemm_common.hpp"
 
 namespace fp4k {
+
+constexpr int SCB = SGR * 2;    // E8M0 scale bytes per row per stage (8)
 
 __device__ __forceinline__ int iabs(int x) { return x < 0 ? -x : x; }
 
@@ -26,26 +32,39 @@ __device__ __forceinline__ int wave_max_i(int d) {
   return d;
 }
 
-// Both E8M0 exponents (K-blocks 2g and 2g+1) of a row: low byte = block 2g.
-__device__ __forceinline__ uint32_t scale_pair(const uint8_t* __restrict__ s, int64_t row, int64_t rows,
-                                               int64_t nblk, int64_t g) {
-  if (row >= rows) return 0x7F7Fu;
-  return *reinterpret_cast<const uint16_t*>(s + row * nblk + 2 * g);
+// Load the 8 scale bytes (4 groups x 2 blocks) of one row for stage st into two dwords.
+// Rows past the matrix get 127 (2^0); groups past K get 127 too.
+__device__ __forceinline__ uint2 scale_row(const uint8_t* __restrict__ s, int64_t row, int64_t rows, int64_t nblk,
+                                           int64_t st) {
+  if (row >= rows) return make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+  const uint8_t* p = s + row * nblk + st * SCB;
+  if ((nblk & 7) == 0 && (reinterpret_cast<uintptr_t>(s) & 7) == 0 && (st + 1) * SCB <= nblk)
+    return *reinterpret_cast<const uint2*>(p);
+  uint32_t w[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < SCB; ++i) {
+    const uint32_t b = (st * SCB + i < nblk) ? p[i] : 0x7Fu;
+    w[i >> 2] |= b << (8 * (i & 3));
+  }
+  return make_uint2(w[0], w[1]);
 }
 
-__global__ __launch_bounds__(GNT) void k_gemm_mx(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
-                                                 const uint8_t* __restrict__ qb, const uint8_t* __restrict__ sb,
-                                                 const float* __restrict__ ga, const float* __restrict__ gb,
-                                                 float* __restrict__ c, int64_t M, int64_t N, int64_t K, int canon,
-                                                 int hadamard_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t lA[2][GT * ROWB];
-  __shared__ __attribute__((aligned(16))) uint8_t lB[2][GT * ROWB];
+__global__ __launch_bounds__(GNT, 2) void k_gemm_mx(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
+                                                    const uint8_t* __restrict__ qb, const uint8_t* __restrict__ sb,
+                                                    const float* __restrict__ ga, const float* __restrict__ gb,
+                                                    float* __restrict__ c, int64_t M, int64_t N, int64_t K, int canon,
+                                                    int hadamard_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lA[2][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lB[2][TILE_BYTES];
+  __shared__ uint2 lS[2][2 * GT];   // [buf][A rows 0..127, B rows 0..127]: 8 scale bytes per row
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * GT, n0 = (int64_t)blockIdx.x * GT;
+  int64_t m0, n0;
+  tile_coords(M, N, m0, n0);
   const int64_t nblk = K / 32;   // E8M0 scales per row
   const int64_t ngroups = K / 64;
   const int64_t nstages = (K + KS - 1) / KS;
+  const int half = l >> 5;
 
   v16f acc[2][2];
 #pragma unroll
@@ -55,94 +74,93 @@ __global__ __launch_bounds__(GNT) void k_gemm_mx(const uint8_t* __restrict__ qa,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  uint4 pa[4], pb[4];
-  stage_load(qa, M, K, m0, 0, pa);
-  stage_load(qb, N, K, n0, 0, pb);
-  stage_store(lA[0], pa);
-  stage_store(lB[0], pb);
+  // scale row handled by this thread: threads 0..127 -> A rows, 128..255 -> B rows
+  const bool srow_is_a = threadIdx.x < GT;
+  const int srow = threadIdx.x & (GT - 1);
+  uint2 sreg = srow_is_a ? scale_row(sa, m0 + srow, M, nblk, 0) : scale_row(sb, n0 + srow, N, nblk, 0);
+  if (nstages > 0) {
+    stage_issue(qa, M, K, m0, 0, lA[0]);
+    stage_issue(qb, N, K, n0, 0, lB[0]);
+  }
+  lS[0][threadIdx.x] = sreg;
+  wait_vm();
   __syncthreads();
-
-  // rows / cols of this lane in the wave's 2x2 tiles
-  const int64_t arow[2] = {m0 + wm * 64 + (l & 31), m0 + wm * 64 + 32 + (l & 31)};
-  const int64_t bcol[2] = {n0 + wn * 64 + (l & 31), n0 + wn * 64 + 32 + (l & 31)};
-  const int half = l >> 5;
 
   mode_f32_rtz();
   for (int64_t st = 0; st < nstages; ++st) {
     const int buf = (int)(st & 1);
     if (st + 1 < nstages) {
-      stage_load(qa, M, K, m0, (st + 1) * KS, pa);
-      stage_load(qb, N, K, n0, (st + 1) * KS, pb);
+      stage_issue(qa, M, K, m0, (st + 1) * KS, lA[buf ^ 1]);
+      stage_issue(qb, N, K, n0, (st + 1) * KS, lB[buf ^ 1]);
+      sreg = srow_is_a ? scale_row(sa, m0 + srow, M, nblk, st + 1) : scale_row(sb, n0 + srow, N, nblk, st + 1);
     }
-    const int64_t g_end = (ngroups - st * 4) < 4 ? (ngroups - st * 4) : 4;
+    // this lane's rows / columns and their 8 stage scale bytes
+    uint2 scA[2], scB[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      scA[t] = lS[buf][wm * 64 + t * 32 + (l & 31)];
+      scB[t] = lS[buf][GT + wn * 64 + t * 32 + (l & 31)];
+    }
+    const int g_end = (int)((ngroups - st * SGR) < SGR ? (ngroups - st * SGR) : SGR);
     for (int g = 0; g < g_end; ++g) {
-      const int64_t gg = st * 4 + g;
       v8i fa[2], fb[2];
-      uint32_t ea[2], eb[2];
+      int ea[2], eb[2];
       int da = 0, db = 0;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int rowa = wm * 64 + t * 32 + (l & 31);
-        const int rowb = wn * 64 + t * 32 + (l & 31);
-        const uint4 va = *reinterpret_cast<const uint4*>(lA[buf] + swz(rowa, g * 2 + half));
-        const uint4 vb = *reinterpret_cast<const uint4*>(lB[buf] + swz(rowb, g * 2 + half));
+        const uint4 va = *reinterpret_cast<const uint4*>(lA[buf] + swz(wm * 64 + t * 32 + (l & 31), g * 2 + half));
+        const uint4 vb = *reinterpret_cast<const uint4*>(lB[buf] + swz(wn * 64 + t * 32 + (l & 31), g * 2 + half));
         fa[t] = v8i{(int)va.x, (int)va.y, (int)va.z, (int)va.w, 0, 0, 0, 0};
         fb[t] = v8i{(int)vb.x, (int)vb.y, (int)vb.z, (int)vb.w, 0, 0, 0, 0};
-        const uint32_t pa2 = scale_pair(sa, arow[t], M, nblk, gg);
-        const uint32_t pb2 = scale_pair(sb, bcol[t], N, nblk, gg);
-        ea[t] = half ? (pa2 >> 8) : (pa2 & 0xFFu);
-        eb[t] = half ? (pb2 >> 8) : (pb2 & 0xFFu);
-        da = max(da, iabs((int)(pa2 & 0xFFu) - (int)(pa2 >> 8)));
-        db = max(db, iabs((int)(pb2 & 0xFFu) - (int)(pb2 >> 8)));
+        const uint32_t wa = (g < 2 ? scA[t].x : scA[t].y) >> (16 * (g & 1));
+        const uint32_t wb = (g < 2 ? scB[t].x : scB[t].y) >> (16 * (g & 1));
+        const int a0 = (int)(wa & 0xFFu), a1 = (int)((wa >> 8) & 0xFFu);
+        const int b0 = (int)(wb & 0xFFu), b1 = (int)((wb >> 8) & 0xFFu);
+        ea[t] = half ? a1 : a0;
+        eb[t] = half ? b1 : b0;
+        da = max(da, iabs(a0 - a1));
+        db = max(db, iabs(b0 - b1));
       }
       // Sufficient for every output of the wave: max|da| + max|db| <= 10. Cheap test first.
       bool fast = !__any(da > 5 || db > 5);
       if (!fast) fast = wave_max_i(da) + wave_max_i(db) <= 10;
-      v16f G[2][2];
       if (fast) {
+        v16f G[2][2];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
-            G[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], v16f{}, 4, 4, 0, (int)ea[i], 0,
-                                                                       (int)eb[j]);
+            G[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], v16f{}, 4, 4, 0, ea[i], 0, eb[j]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = acc[i][j][r] + G[i][j][r];   // round toward zero
       } else {
-        v8i fa0[2], fa1[2];
+        const v8i z = v8i{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const v8i z = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-          fa0[i] = half == 0 ? fa[i] : z;
-          fa1[i] = half == 1 ? fa[i] : z;
-        }
-        v16f T0[2][2], T1[2][2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
+          const v8i fa0 = half == 0 ? fa[i] : z;
+          const v8i fa1 = half == 1 ? fa[i] : z;
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            T0[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa0[i], fb[j], v16f{}, 4, 4, 0, (int)ea[i], 0,
-                                                                        (int)eb[j]);
-            T1[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa1[i], fb[j], v16f{}, 4, 4, 0, (int)ea[i], 0,
-                                                                        (int)eb[j]);
+            const v16f T0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa0, fb[j], v16f{}, 4, 4, 0, ea[i], 0, eb[j]);
+            const v16f T1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa1, fb[j], v16f{}, 4, 4, 0, ea[i], 0, eb[j]);
+            float Gs[16];
+            mode_f32_rne();
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Gs[r] = T0[r] + T1[r];
+            mode_f32_rtz();
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = acc[i][j][r] + Gs[r];
           }
-        mode_f32_rne();
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) G[i][j][r] = add_in_mode(T0[i][j][r], T1[i][j][r]);
-        mode_f32_rtz();
+        }
       }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = add_in_mode(acc[i][j][r], G[i][j][r]);
     }
     if (st + 1 < nstages) {
-      stage_store(lA[buf ^ 1], pa);
-      stage_store(lB[buf ^ 1], pb);
+      lS[buf ^ 1][threadIdx.x] = sreg;
+      wait_vm();
       __syncthreads();
     }
   }
@@ -151,9 +169,9 @@ __global__ __launch_bounds__(GNT) void k_gemm_mx(const uint8_t* __restrict__ qa,
 
 hipError_t run_gemm_mx(const GemmArgs& g) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
-  dim3 grid((unsigned)((g.N + GT - 1) / GT), (unsigned)((g.M + GT - 1) / GT));
-  hipLaunchKernelGGL(k_gemm_mx, grid, dim3(GNT), 0, g.stream, g.a.q, g.a.s, g.b.q, g.b.s, g.a.g, g.b.g, g.c, g.M, g.N,
-                     g.K, g.canon, g.hadamard_n);
+  const int64_t tiles = ((g.M + GT - 1) / GT) * ((g.N + GT - 1) / GT);
+  hipLaunchKernelGGL(k_gemm_mx, dim3((unsigned)tiles), dim3(GNT), 0, g.stream, g.a.q, g.a.s, g.b.q, g.b.s, g.a.g,
+                     g.b.g, g.c, g.M, g.N, g.K, g.canon, g.hadamard_n);
   return hipGetLastError();
 }
 
