@@ -9,8 +9,9 @@
 // 128 payload bytes per row). Payload stages go straight from global memory into LDS with
 // global_load_lds_dwordx4 (no staging registers), double-buffered; the scale bytes of a
 // stage go through registers into a small LDS array. LDS payload rows are 128 bytes;
-// 16-byte chunk j of row r sits at chunk position j ^ (r & 7), so eight consecutive rows
-// reading the same logical chunk hit distinct banks.
+// 16-byte chunk j of row r sits at chunk position j ^ ((r >> 1) & 7): sixteen consecutive
+// rows reading the same logical chunk then cover all 64 LDS banks (two rows per 256-byte
+// bank line, eight distinct positions within each row parity).
 //
 // Workgroup order: 8 consecutive workgroup ids land on the 8 XCDs round-robin, so ids are
 // remapped to give each XCD a contiguous run of tiles, ordered in groups of 8 M-tiles:
@@ -34,30 +35,49 @@ constexpr int ROWB = KS / 2;   // payload bytes per row per stage
 constexpr int GNT = 256;       // threads per workgroup
 constexpr int TILE_BYTES = GT * ROWB;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * ROWB + ((chunk ^ (row & 7)) << 4); }
+#ifndef FP4_SWZ_SHIFT
+#define FP4_SWZ_SHIFT 1
+#endif
+// chunk position of logical 16-byte chunk `chunk` in LDS row `row`
+__device__ __forceinline__ int swz_pos(int row, int chunk) { return chunk ^ ((row >> FP4_SWZ_SHIFT) & 7); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * ROWB + (swz_pos(row, chunk) << 4); }
 
-// Issue the direct global->LDS loads of one stage of a 128-row payload tile. Each wave
-// fills 4 x 1024 contiguous LDS bytes; lane i of a 1024-byte piece writes LDS bytes
-// [16i, 16i+16), i.e. row 8p + i/8 at chunk position i%8, so it loads logical chunk
-// (i%8) ^ (row & 7). Rows past the matrix and chunks past K read clamped, valid addresses
-// (their values only reach outputs that are not stored, or groups that are not computed).
-__device__ __forceinline__ void stage_issue(const uint8_t* __restrict__ q, int64_t rows, int64_t K, int64_t row0,
-                                            int64_t k0, uint8_t* lds) {
-  const int64_t ldq = K / 2, kb0 = k0 / 2;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+// Direct global->LDS loads of one stage of a 128-row payload tile. Each wave fills 4 x 1024
+// contiguous LDS bytes; lane i of a 1024-byte piece writes LDS bytes [16i, 16i+16), i.e.
+// row 8p + i/8 at chunk position i%8, so it loads the logical chunk stored there. Rows past
+// the matrix read a clamped (valid) row; their values only reach outputs that are not
+// stored. The per-lane byte offsets (row * K/2 + chunk * 16, below 2^31) are computed once.
+struct StageLoader {
+  const uint8_t* base;     // q + row0 * K/2, wave-uniform
+  uint32_t roff[4];        // per-lane row offsets (row * K/2) of the 4 pieces this wave loads
+  uint32_t coff[4];        // per-lane chunk offsets (logical chunk * 16) inside a stage row
+  int64_t ldq;
+
+  __device__ __forceinline__ void init(const uint8_t* q, int64_t rows, int64_t K, int64_t row0) {
+    ldq = K / 2;
+    base = q + row0 * ldq;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int piece = w * 4 + j;                 // 0..15, 1024 bytes each
-    const int row = piece * 8 + (l >> 3);
-    const int pos = l & 7;
-    const int chunk = pos ^ (row & 7);
-    int64_t grow = row0 + row;
-    grow = grow < rows ? grow : rows - 1;
-    int64_t gb = kb0 + chunk * 16;
-    gb = gb < ldq ? gb : ldq - 16;
-    __builtin_amdgcn_global_load_lds(q + grow * ldq + gb, (lds_void*)(lds + piece * 1024), 16, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+      const int row = (w * 4 + j) * 8 + (l >> 3);
+      const int64_t r = (row0 + row) < rows ? row : (rows - 1 - row0);
+      roff[j] = (uint32_t)(r * ldq);
+      coff[j] = (uint32_t)(swz_pos(row, l & 7) * 16);   // swz_pos is an involution in `chunk`
+    }
   }
-}
+  // stage st into lds; only the last stage of a K that is not a multiple of 256 clamps chunks
+  __device__ __forceinline__ void issue(int64_t st, uint8_t* lds) const {
+    const int w = threadIdx.x >> 6;
+    const uint32_t kb0 = (uint32_t)(st * ROWB);
+    const bool full = (int64_t)kb0 + ROWB <= ldq;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t c = kb0 + coff[j];
+      if (!full && c + 16 > (uint32_t)ldq) c = (uint32_t)ldq - 16;
+      __builtin_amdgcn_global_load_lds(base + roff[j] + c, (lds_void*)(lds + (w * 4 + j) * 1024), 16, 0, 0);
+    }
+  }
+};
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

@@ -99,9 +99,12 @@ __global__ __launch_bounds__(GNT, 2) void k_gemm_dec16(const uint8_t* __restrict
   const int srow = threadIdx.x & (GT - 1);
   uint4 sreg = srow_is_a ? scale_row16<FMT, B>(sa, la, m0 + srow, M, K, 0)
                          : scale_row16<FMT, B>(sb, lb, n0 + srow, N, K, 0);
+  StageLoader LA, LB;
+  LA.init(qa, M, K, m0);
+  LB.init(qb, N, K, n0);
   if (nstages > 0) {
-    stage_issue(qa, M, K, m0, 0, lA[0]);
-    stage_issue(qb, N, K, n0, 0, lB[0]);
+    LA.issue(0, lA[0]);
+    LB.issue(0, lB[0]);
   }
   lS[0][threadIdx.x] = sreg;
   wait_vm();
@@ -110,8 +113,8 @@ __global__ __launch_bounds__(GNT, 2) void k_gemm_dec16(const uint8_t* __restrict
   for (int64_t st = 0; st < nstages; ++st) {
     const int buf = (int)(st & 1);
     if (st + 1 < nstages) {
-      stage_issue(qa, M, K, m0, (st + 1) * KS, lA[buf ^ 1]);
-      stage_issue(qb, N, K, n0, (st + 1) * KS, lB[buf ^ 1]);
+      LA.issue(st + 1, lA[buf ^ 1]);
+      LB.issue(st + 1, lB[buf ^ 1]);
       sreg = srow_is_a ? scale_row16<FMT, B>(sa, la, m0 + srow, M, K, st + 1)
                        : scale_row16<FMT, B>(sb, lb, n0 + srow, N, K, st + 1);
     }
