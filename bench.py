@@ -8,15 +8,22 @@ wgrad dW = dY^T X. Inputs are seeded synthetic tensors already resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--fmt mxfp4|ue5m3|e4m3] [--hadamard 0|16|32]
 
-Prints one JSON line. ``value`` = FP4 GEMM FLOPs of the step / step wall time (TFLOP/s);
-``roofline`` is the fprop GEMM kernel's achieved FLOP rate (HIP events around each
-launch on the launch stream) against the FP4 MFMA peak; ``quantizer`` is the row-view
-activation quantizer's algorithmic GB/s against HBM peak; ``cpu_baseline`` times the CPU
-oracle on a bounded slice of the same workload.
+Prints one JSON line. ``value`` = FP4 GEMM FLOPs of the step / step wall time (TFLOP/s).
+``roofline`` is the GEMM kernel's achieved FLOP rate against the FP4 MFMA peak: the three
+GEMMs of the step (fprop 8192x14336 K=4096, dgrad 8192x4096 K=14336, wgrad 14336x4096
+K=8192) each do 2*8192*4096*14336 FLOP, and their launches are timed with HIP events on
+the launch stream. ``traffic`` is the HBM bytes per GEMM launch from the FETCH_SIZE and
+WRITE_SIZE counters, scaled by the counters' reading for a plain device copy of known
+size; it is read from the profile summary under ``profiles/`` and is null when the GEMM
+kernel sources changed since those counters were taken. ``quantizer`` is the row-view
+activation quantizer's algorithmic GB/s against HBM peak. ``cpu_baseline`` times the CPU
+oracle on a bounded slice of the same workload. ``--calib-copy-mib N`` runs one plain
+N-MiB device copy before warm-up, the known-size reference for the byte counters.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -29,6 +36,12 @@ FP4_PEAK_TFLOPS = 10100.0      # MI355X dense FP4/FP6 MFMA
 BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBS = 8000.0
 METRIC = "FP4 GEMM TFLOPS + quantize GB/s at 8192x4096x14336, % of MI355X peak"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "fp4_block_scaled_tensor_amd", "csrc")
+GEMM_SOURCES = {"mxfp4": ["gemm_mx.hip", "gemm_common.hpp", "fp4_device.hpp"],
+                "ue5m3": ["gemm_dec16.hip", "gemm_common.hpp", "fp4_device.hpp"],
+                "e4m3": ["gemm_dec16.hip", "gemm_common.hpp", "fp4_device.hpp"]}
+GEMM_KERNEL = {"mxfp4": "k_gemm_mx", "ue5m3": "k_gemm_dec16", "e4m3": "k_gemm_dec16"}
 
 
 def parse():
@@ -39,8 +52,36 @@ def parse():
     p.add_argument("--fmt", default="mxfp4", choices=["mxfp4", "ue5m3", "e4m3"])
     p.add_argument("--hadamard", type=int, default=0, choices=[0, 16, 32])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=32, help="output rows of the oracle GEMM sample")
+    p.add_argument("--cpu-rows", type=int, default=384, help="output rows of the oracle GEMM sample")
+    p.add_argument("--calib-copy-mib", type=int, default=0, help="one plain device copy of this size first")
     return p.parse_args()
+
+
+def gemm_source_hash(fmt_name):
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES[fmt_name]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(fmt_name):
+    """HBM bytes per GEMM launch recorded in profiles/, if taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{GEMM_KERNEL[fmt_name]}_{fmt_name}_8192x4096x14336_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("source_sha256_16") != gemm_source_hash(fmt_name):
+        return None
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 class LinearStep:
@@ -61,8 +102,18 @@ class LinearStep:
         self.Y = torch.empty((M_TOK, N_OUT), dtype=torch.float32, device=dev)
         self.dX = torch.empty((M_TOK, K_IN), dtype=torch.float32, device=dev)
         self.dW = torch.empty((N_OUT, K_IN), dtype=torch.float32, device=dev)
-        self.ev = []          # (start, end) events around each fprop GEMM
+        self.ev = []          # (start, end) events around each GEMM launch
         self.evq = []         # around each activation row-view quantization
+
+    def _timed(self, timed, fn, *a, **kw):
+        if not timed:
+            return fn(*a, **kw)
+        e0, e1 = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        r = fn(*a, **kw)
+        e1.record()
+        self.ev.append((e0, e1))
+        return r
 
     def _sample(self, cache, x, step, hn=0):
         if self.fmt == self.fp4.E8M0:
@@ -90,25 +141,19 @@ class LinearStep:
             qwt = fp4.quantize(self.W, self.fmt, B, fp4.COL)          # W^T, blocks along out-features
         else:
             qw, qwt = fp4.quantize(self.W, self.fmt, 16, fp4.TILE2D, amax=self.c_w.amax, T=448)
-        if timed:
-            g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            g0.record()
-        fp4.gemm_fprop(qx, qw, out=self.Y)
-        if timed:
-            g1.record()
-            self.ev.append((g0, g1))
+        self._timed(timed, fp4.gemm_fprop, qx, qw, out=self.Y)
         # backward: dgrad
         self._sample(self.c_dy, self.dY, step)
         qdy = fp4.quantize(self.dY, self.fmt, B, fp4.ROW, amax=self.c_dy.amax, T=448, stochastic=True, seed=42,
                            offset=step * 8 + 0)
-        fp4.gemm_dgrad(qdy, qwt, out=self.dX)
+        self._timed(timed, fp4.gemm_dgrad, qdy, qwt, out=self.dX)
         # backward: wgrad (dY^T with T = 2048, X^T with T = 448, optional Hadamard)
         self._sample(self.c_dyh, self.dY, step, self.hn)
         self._sample(self.c_xh, self.X, step, self.hn)
         qdyt = fp4.quantize(self.dY, self.fmt, B, fp4.COL, amax=self.c_dyh.amax, T=2048, stochastic=True, seed=42,
                             offset=step * 8 + 1, hadamard_n=self.hn)
         qxt = fp4.quantize(self.X, self.fmt, B, fp4.COL, amax=self.c_xh.amax, T=448, hadamard_n=self.hn)
-        fp4.gemm_wgrad(qdyt, qxt, hadamard_n=self.hn, out=self.dW)
+        self._timed(timed, fp4.gemm_wgrad, qdyt, qxt, hadamard_n=self.hn, out=self.dW)
 
 
 def bf16_device(torch, synth, x):
@@ -117,8 +162,9 @@ def bf16_device(torch, synth, x):
 
 
 def cpu_baseline(args, fmt_name, synth):
-    """The oracle as it stands, on the host: quantize a row slice of X and W and run the
-    group-model GEMM for args.cpu_rows output rows across all 14336 columns."""
+    """The oracle as it stands, on the host, on a bounded slice of the same workload:
+    the group-model GEMM for args.cpu_rows output rows across all 14336 columns (W quantized
+    in full, untimed), and the row-view quantizer on 1024 rows of the activation."""
     import oracle
     from oracle import formats as OF
     try:
@@ -129,35 +175,38 @@ def cpu_baseline(args, fmt_name, synth):
     fmt = {"mxfp4": OF.E8M0, "ue5m3": OF.UE5M3, "e4m3": OF.E4M3}[fmt_name]
     block = 32 if fmt == OF.E8M0 else 16
     rows = args.cpu_rows
-    Xs = synth.student_t((rows, K_IN), 3.0, 301)
+    qrows = 1024
+    Xs = synth.student_t((qrows, K_IN), 3.0, 301)
+    Xs, _ = synth.scale_channels(Xs, 4, 100.0, 302)
     W = synth.normal((N_OUT, K_IN), 0.02, 303)
+    amax_x = float(np.max(np.abs(Xs)))
     t0 = time.perf_counter()
-    qx = oracle.quantize_1d(Xs, fmt, block, amax=float(np.max(np.abs(Xs))), T=448)
+    oracle.quantize_1d(Xs, fmt, block, amax=amax_x, T=448)
     tq = time.perf_counter() - t0
+    qx = oracle.quantize_1d(Xs[:rows], fmt, block, amax=amax_x, T=448)
     if fmt == OF.E8M0:
         qw = oracle.quantize_1d(W, fmt, block)
-        a, sa = oracle.operand_from_quant(qx)
         b, sb = oracle.operand_from_quant(qw)
     else:
         qw = oracle.quantize_2d(W, fmt, amax=float(np.max(np.abs(W))), T=448)
-        a, sa = oracle.operand_from_quant(qx)
         b, sb = oracle.operand_from_quant(qw, "2d")
+    a, sa = oracle.operand_from_quant(qx)
     t1 = time.perf_counter()
     oracle.gemm_model(a, sa, b, sb, block, alpha=oracle.output_scale(qx.g, qw.g))
     tg = time.perf_counter() - t1
     flops = 2.0 * rows * N_OUT * K_IN
-    qbytes = rows * K_IN * (2 + 0.5 + 1.0 / block)
-    return {"value": flops / tg / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"group-model GEMM of {rows} output rows x {N_OUT} x K={K_IN} ({fmt_name}), "
-                      f"{tg:.1f} s; quantizer on {rows}x{K_IN}: {qbytes / tq / 1e9:.4f} GB/s",
-            "quantizer_GBps": qbytes / tq / 1e9, "seconds": tg + tq}
+    qbytes = qrows * K_IN * (2 + 0.5 + 1.0 / block)
+    return {"value": round(flops / tg / 1e12, 8), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"group-model GEMM of {rows} output rows x {N_OUT} cols, K={K_IN} ({fmt_name}): {tg:.1f} s; "
+                      f"row-view quantizer on {qrows}x{K_IN} bf16-valued activations: {tq:.2f} s",
+            "quantizer_GBps": round(qbytes / tq / 1e9, 6)}
 
 
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build targets the single-GPU FP4 hot path; "
-              "multi-GPU runs are not supported.", file=sys.stderr)
+        print("bench.py measures one GPU: the FP4 hot path here runs on a single GPU; "
+              "--gpus above 1 is not supported.", file=sys.stderr)
         sys.exit(2)
     import torch
     import synth
@@ -173,6 +222,14 @@ def main():
     dYd = bf16_device(torch, synth, synth.normal((M_TOK, N_OUT), 1e-3, 304))
     del X
     step_obj = LinearStep(fp4, torch, Xd, Wd, dYd, args.fmt, args.hadamard)
+    if args.calib_copy_mib > 0:
+        # known-size reference for the HBM byte counters: one plain copy of N MiB
+        src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for s in range(args.warmup):
         step_obj.run(s)
     torch.cuda.synchronize()
@@ -210,10 +267,11 @@ def main():
         "config": {"workload": f"FP4 linear training step 8192 tok x 4096 -> 14336 ({args.fmt}, H{args.hadamard})",
                    "tokens": M_TOK, "in_features": K_IN, "out_features": N_OUT, "gemms_per_step": 3,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "fprop GEMM " + ("k_gemm_mx" if args.fmt == "mxfp4" else "k_gemm_dec16"),
-                     "achieved": round(achieved, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP4_PEAK_TFLOPS, 4),
-                     "traffic": None, "avg_ms": round(gemm_ms, 4),
+                     "traffic": traffic_from_profile(args.fmt),
+                     "kernel": GEMM_KERNEL[args.fmt] + " (fprop, dgrad and wgrad launches, 2*8192*4096*14336 FLOP each)",
+                     "avg_ms": round(gemm_ms, 4), "source_sha256_16": gemm_source_hash(args.fmt),
                      "frac_of_bf16_peak": None if args.fmt == "mxfp4" else round(achieved / BF16_PEAK_TFLOPS, 4)},
         "quantizer": {"kernel": "k_quant_row (activation 8192x4096 bf16)", "achieved": round(q_gbs, 1),
                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(q_gbs / HBM_PEAK_GBS, 4),
