@@ -4,8 +4,8 @@
 // software GEMM model): 64-product groups; each group a float32 partial rounded to nearest
 // even; groups added in K order with round-toward-zero; optional 1/1024 canonicalisation.
 //
-// Tiling: a 256-thread workgroup owns a 128x128 output tile as 2x2 waves of 64x64; each
-// wave computes 2x2 MFMA tiles of 32x32. K advances by stages of 256 elements (4 groups,
+// Tiling: a workgroup of WM x WN waves owns a (WM*TM*32) x (WN*TN*32) output tile; each wave
+// computes TM x TN MFMA tiles of 32x32. K advances by stages of 256 elements (4 groups,
 // 128 payload bytes per row). Payload stages go straight from global memory into LDS with
 // global_load_lds_dwordx4 (no staging registers), double-buffered; the scale bytes of a
 // stage go through registers into a small LDS array. LDS payload rows are 128 bytes;
@@ -28,12 +28,22 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int GT = 128;        // output tile edge per workgroup
 constexpr int KS = 256;        // K elements per stage
 constexpr int SGR = KS / 64;   // groups per stage
 constexpr int ROWB = KS / 2;   // payload bytes per row per stage
-constexpr int GNT = 256;       // threads per workgroup
-constexpr int TILE_BYTES = GT * ROWB;
+
+// Workgroup geometry: WM x WN waves, each TM x TN MFMA tiles of 32x32.
+template <int WM_, int WN_, int TM_, int TN_>
+struct Tiling {
+  static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_;
+  static constexpr int NW = WM * WN;          // waves
+  static constexpr int NT = NW * 64;          // threads
+  static constexpr int BM = WM * TM * 32;     // output rows (A rows) per workgroup
+  static constexpr int BN = WN * TN * 32;     // output cols (B rows) per workgroup
+};
+
+// wave index inside the workgroup, as a wave-uniform (scalar) value
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 #ifndef FP4_SWZ_SHIFT
 #define FP4_SWZ_SHIFT 1
@@ -42,39 +52,76 @@ constexpr int TILE_BYTES = GT * ROWB;
 __device__ __forceinline__ int swz_pos(int row, int chunk) { return chunk ^ ((row >> FP4_SWZ_SHIFT) & 7); }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * ROWB + (swz_pos(row, chunk) << 4); }
 
-// Direct global->LDS loads of one stage of a 128-row payload tile. Each wave fills 4 x 1024
-// contiguous LDS bytes; lane i of a 1024-byte piece writes LDS bytes [16i, 16i+16), i.e.
-// row 8p + i/8 at chunk position i%8, so it loads the logical chunk stored there. Rows past
-// the matrix read a clamped (valid) row; their values only reach outputs that are not
-// stored. The per-lane byte offsets (row * K/2 + chunk * 16, below 2^31) are computed once.
+// LDS byte address of a pointer into a __shared__ array (a generic pointer to LDS keeps the
+// LDS offset in its low 32 bits).
+__device__ __forceinline__ uint32_t lds_offset(const void* p) { return (uint32_t)reinterpret_cast<uintptr_t>(p); }
+
+// One global_load_lds_dwordx4 for the wave: lane i copies the 16 bytes at sbase + voff(i)
+// to LDS bytes [dst + 16 i, dst + 16 i + 16) (dst is wave-uniform and goes in M0, with the
+// one-instruction gap the M0 write needs before the load). Written as inline assembly so
+// that the compiler's wait-count insertion does not treat the copy as an LDS write that may
+// alias later LDS reads of the other buffer: the kernels wait for these copies themselves
+// (vmcnt(0) and a barrier before the buffer is read).
+__device__ __forceinline__ void lds_dma16(const uint8_t* sbase, uint32_t voff, uint32_t dst) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 1\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(dst)
+      : "memory", "m0");
+}
+
+// Direct global->LDS loads of one stage of a ROWS-row payload tile by NW waves. Each wave
+// fills P = ROWS / (8 NW) contiguous 1024-byte LDS pieces; lane i of piece p writes LDS
+// bytes [16i, 16i+16), i.e. row 8p + i/8 at chunk position i%8, so it loads the logical
+// chunk stored there: chunk position ^ ((row >> 1) & 7) = (i%8) ^ ((p & 1) << 2 | i/16).
+// Only two per-lane offsets exist (even and odd pieces); the piece's row base is
+// wave-uniform. In a tile that reaches past the matrix, rows past it read a clamped
+// (valid) row; their values only reach outputs that are not stored.
+template <int ROWS, int NW>
 struct StageLoader {
+  static constexpr int P = ROWS / (8 * NW);
+  static_assert(P >= 1 && P * 8 * NW == ROWS, "tile rows must be a multiple of 8 per wave");
+  static_assert(FP4_SWZ_SHIFT == 1, "piece-parity offsets assume the row-pair swizzle");
   const uint8_t* base;     // q + row0 * K/2, wave-uniform
-  uint32_t roff[4];        // per-lane row offsets (row * K/2) of the 4 pieces this wave loads
-  uint32_t coff[4];        // per-lane chunk offsets (logical chunk * 16) inside a stage row
+  uint32_t off_e, off_o;   // per-lane byte offsets inside an even / odd piece (row * K/2 + chunk * 16)
   int64_t ldq;
+  int64_t last;            // last valid tile row (rows - 1 - row0), for clamping
+  bool edge;               // tile reaches past the matrix
 
   __device__ __forceinline__ void init(const uint8_t* q, int64_t rows, int64_t K, int64_t row0) {
     ldq = K / 2;
     base = q + row0 * ldq;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = (w * 4 + j) * 8 + (l >> 3);
-      const int64_t r = (row0 + row) < rows ? row : (rows - 1 - row0);
-      roff[j] = (uint32_t)(r * ldq);
-      coff[j] = (uint32_t)(swz_pos(row, l & 7) * 16);   // swz_pos is an involution in `chunk`
-    }
+    last = rows - 1 - row0;
+    edge = row0 + ROWS > rows;
+    const int l = threadIdx.x & 63;
+    const uint32_t pos_e = (uint32_t)((l & 7) ^ (l >> 4));
+    off_e = (uint32_t)((l >> 3) * ldq) + pos_e * 16;
+    off_o = (uint32_t)((l >> 3) * ldq) + (pos_e ^ 4) * 16;
   }
   // stage st into lds; only the last stage of a K that is not a multiple of 256 clamps chunks
   __device__ __forceinline__ void issue(int64_t st, uint8_t* lds) const {
-    const int w = threadIdx.x >> 6;
+    const int w = wave_id();
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));   // keep the edge-tile offsets inside their branch (not hoisted, not live)
     const uint32_t kb0 = (uint32_t)(st * ROWB);
     const bool full = (int64_t)kb0 + ROWB <= ldq;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t c = kb0 + coff[j];
-      if (!full && c + 16 > (uint32_t)ldq) c = (uint32_t)ldq - 16;
-      __builtin_amdgcn_global_load_lds(base + roff[j] + c, (lds_void*)(lds + (w * 4 + j) * 1024), 16, 0, 0);
+    for (int j = 0; j < P; ++j) {
+      const int piece = w * P + j;
+      const bool odd = (P % 2 == 0) ? (j & 1) : (piece & 1);
+      const uint32_t dst = lds_offset(lds + piece * 1024);
+      if (!(edge || !full)) {
+        // scalar piece base + per-lane offset
+        lds_dma16(base + ((int64_t)piece * 8 * ldq + kb0), odd ? off_o : off_e, dst);
+      } else {
+        const int64_t row = piece * 8 + (l >> 3);
+        const int64_t r = row <= last ? row : last;
+        uint32_t c = kb0 + (uint32_t)((((l & 7) ^ ((odd ? 4 : 0) | (l >> 4)))) * 16);
+        if (!full && c + 16 > (uint32_t)ldq) c = (uint32_t)ldq - 16;
+        lds_dma16(base, (uint32_t)(r * ldq) + c, dst);
+      }
     }
   }
 };
@@ -82,8 +129,8 @@ struct StageLoader {
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Workgroup id -> (m tile, n tile), XCD-aware grouped order.
-__device__ __forceinline__ void tile_coords(int64_t M, int64_t N, int64_t& m0, int64_t& n0) {
-  const int64_t ntm = (M + GT - 1) / GT, ntn = (N + GT - 1) / GT;
+__device__ __forceinline__ void tile_coords(int64_t M, int64_t N, int BM, int BN, int64_t& m0, int64_t& n0) {
+  const int64_t ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
   const int64_t T = ntm * ntn;
   int64_t id = blockIdx.x;
   if ((T & 7) == 0) id = (id & 7) * (T >> 3) + (id >> 3);
@@ -93,23 +140,54 @@ __device__ __forceinline__ void tile_coords(int64_t M, int64_t N, int64_t& m0, i
   const int64_t first = gid * GM;
   const int64_t gm = (ntm - first) < GM ? (ntm - first) : GM;
   const int64_t r = id % gsize;
-  m0 = (first + r % gm) * GT;
-  n0 = (r / gm) * GT;
+  m0 = (first + r % gm) * BM;
+  n0 = (r / gm) * BN;
+}
+
+// Float additions are ordinary register operations: nothing orders them against the
+// s_setreg that switches the rounding mode. An empty volatile asm that takes a value in and
+// out of a register is ordered against the mode-switch asm (volatile asm statements keep
+// their order), so routing operands and results through one pins the additions between
+// the switches. It emits no instruction.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(v16f& x) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float v = x[r];
+    pin(v);
+    x[r] = v;
+  }
+}
+
+// T0 + T1 rounded to nearest even, elementwise, called from round-toward-zero code: the
+// mode is switched for the additions and restored afterwards.
+__device__ __forceinline__ v16f add_rne_from_rtz(v16f T0, v16f T1) {
+  mode_f32_rne();
+  pin(T0);
+  pin(T1);
+  v16f G;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) G[r] = T0[r] + T1[r];
+  pin(G);
+  mode_f32_rtz();
+  pin(G);
+  return G;
 }
 
 // Output row of register r of a 32x32 MFMA tile in lane l (column = l & 31).
 __device__ __forceinline__ int tile_row(int r, int l) { return (r >> 2) * 8 + (l >> 5) * 4 + (r & 3); }
 
 // Epilogue: nearest-even mode, optional canonicalisation, scale by alpha, store float32.
+// (m0, n0) is the wave's first output row and column; tile (i, j) covers rows m0 + 32i and
+// columns n0 + 32j.
+template <int TM, int TN>
 __device__ __forceinline__ void store_tiles(float* __restrict__ c, int64_t M, int64_t N, int64_t m0, int64_t n0,
-                                            v16f (&acc)[2][2], const float* ga, const float* gb, int canon,
+                                            v16f (&acc)[TM][TN], const float* ga, const float* gb, int canon,
                                             int hadamard_n) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(acc[i][j][r]));   // accumulation done before the switch
+    for (int j = 0; j < TN; ++j) pin(acc[i][j]);   // accumulation done before the switch
   mode_f32_rne();
   float a = ga ? *ga : 1.0f;
   float b = gb ? *gb : 1.0f;
@@ -118,9 +196,9 @@ __device__ __forceinline__ void store_tiles(float* __restrict__ c, int64_t M, in
   if (hadamard_n) alpha = alpha * (1.0f / (float)hadamard_n);
   const int l = threadIdx.x & 63;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < TM; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < TN; ++ct) {
       const int64_t col = n0 + ct * 32 + (l & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {

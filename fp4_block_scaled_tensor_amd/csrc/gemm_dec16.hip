@@ -69,20 +69,24 @@ __device__ __forceinline__ uint32_t byte_of(const uint4& v, int i) {
   return (w >> (8 * (i & 3))) & 0xFFu;
 }
 
+using DecTiling = Tiling<2, 2, 2, 2>;   // 128x128 workgroup tile, 4 waves of 64x64
+
 template <int FMT, int B>
-__global__ __launch_bounds__(GNT, 2) void k_gemm_dec16(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
+__global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
                                                        int la, const uint8_t* __restrict__ qb,
                                                        const uint8_t* __restrict__ sb, int lb,
                                                        const float* __restrict__ ga, const float* __restrict__ gb,
                                                        float* __restrict__ c, int64_t M, int64_t N, int64_t K,
                                                        int canon, int hadamard_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lA[2][TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t lB[2][TILE_BYTES];
-  __shared__ uint4 lS[2][2 * GT];   // 16 slice-scale codes per row: A rows then B rows
+  using TL = DecTiling;
+  constexpr int GT = TL::BM;        // == TL::BN
+  __shared__ __attribute__((aligned(1024))) uint8_t lA[2][TL::BM * ROWB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lB[2][TL::BN * ROWB];
+  __shared__ uint4 lS[2][TL::BM + TL::BN];   // 16 slice-scale codes per row: A rows then B rows
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
   int64_t m0, n0;
-  tile_coords(M, N, m0, n0);
+  tile_coords(M, N, TL::BM, TL::BN, m0, n0);
   const int64_t ngroups = K / 64;
   const int64_t nstages = (K + KS - 1) / KS;
   const int half = l >> 5;
@@ -99,7 +103,8 @@ __global__ __launch_bounds__(GNT, 2) void k_gemm_dec16(const uint8_t* __restrict
   const int srow = threadIdx.x & (GT - 1);
   uint4 sreg = srow_is_a ? scale_row16<FMT, B>(sa, la, m0 + srow, M, K, 0)
                          : scale_row16<FMT, B>(sb, lb, n0 + srow, N, K, 0);
-  StageLoader LA, LB;
+  StageLoader<TL::BM, TL::NW> LA;
+  StageLoader<TL::BN, TL::NW> LB;
   LA.init(qa, M, K, m0);
   LB.init(qb, N, K, n0);
   if (nstages > 0) {
@@ -145,27 +150,32 @@ __global__ __launch_bounds__(GNT, 2) void k_gemm_dec16(const uint8_t* __restrict
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          // group partial of this tile, nearest-even
-          v16f G = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][i], fb[0][j], v16f{}, 0, 0, 0);
+          // group partial of this tile, nearest-even (the loop's mode); the MFMA results
+          // are pinned after the previous switch back to nearest-even
+          v16f T[4];
+#pragma unroll
+          for (int sub = 0; sub < 4; ++sub)
+            T[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sub][i], fb[sub][j], v16f{}, 0, 0, 0);
+#pragma unroll
+          for (int sub = 0; sub < 4; ++sub) pin(T[sub]);
+          v16f G;
           if constexpr (B == 16) {
 #pragma unroll
-            for (int sub = 1; sub < 4; ++sub) {
-              const v16f T = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sub][i], fb[sub][j], v16f{}, 0, 0, 0);
-#pragma unroll
-              for (int r = 0; r < 16; ++r) G[r] = G[r] + T[r];
-            }
+            for (int r = 0; r < 16; ++r) G[r] = ((T[0][r] + T[1][r]) + T[2][r]) + T[3][r];
           } else {
-            const v16f T1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][j], v16f{}, 0, 0, 0);
-            const v16f T2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[2][i], fb[2][j], v16f{}, 0, 0, 0);
-            const v16f T3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[3][i], fb[3][j], v16f{}, 0, 0, 0);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) G[r] = (G[r] + T1[r]) + (T2[r] + T3[r]);   // inner adds exact
+            for (int r = 0; r < 16; ++r) G[r] = (T[0][r] + T[1][r]) + (T[2][r] + T[3][r]);   // inner adds exact
           }
-          // cross-group accumulation, toward zero
+          // cross-group accumulation, toward zero (pinned between the mode switches)
+          pin(G);
           mode_f32_rtz();
+          pin(G);
+          pin(acc[i][j]);
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[i][j][r] = acc[i][j][r] + G[r];
+          pin(acc[i][j]);
           mode_f32_rne();
+          pin(acc[i][j]);
         }
     }
     if (st + 1 < nstages) {
@@ -174,13 +184,14 @@ __global__ __launch_bounds__(GNT, 2) void k_gemm_dec16(const uint8_t* __restrict
       __syncthreads();
     }
   }
-  store_tiles(c, M, N, m0 + wm * 64, n0 + wn * 64, acc, ga, gb, canon, hadamard_n);
+  store_tiles<2, 2>(c, M, N, m0 + wm * 64, n0 + wn * 64, acc, ga, gb, canon, hadamard_n);
 }
 
 template <int FMT, int B>
 static hipError_t launch_dec16(const GemmArgs& g) {
-  const int64_t tiles = ((g.M + GT - 1) / GT) * ((g.N + GT - 1) / GT);
-  hipLaunchKernelGGL((k_gemm_dec16<FMT, B>), dim3((unsigned)tiles), dim3(GNT), 0, g.stream, g.a.q, g.a.s, g.a.layout,
+  using TL = DecTiling;
+  const int64_t tiles = ((g.M + TL::BM - 1) / TL::BM) * ((g.N + TL::BN - 1) / TL::BN);
+  hipLaunchKernelGGL((k_gemm_dec16<FMT, B>), dim3((unsigned)tiles), dim3(TL::NT), 0, g.stream, g.a.q, g.a.s, g.a.layout,
                      g.b.q, g.b.s, g.b.layout, g.a.g, g.b.g, g.c, g.M, g.N, g.K, g.canon, g.hadamard_n);
   return hipGetLastError();
 }

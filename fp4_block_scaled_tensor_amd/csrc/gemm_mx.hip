@@ -15,11 +15,20 @@
 // two are added in float32 round-to-nearest-even. Group partials are accumulated with
 // v_add_f32 under round-toward-zero (MODE register), in K order.
 //
-// The gap test runs once per stage (4 groups): the thread that stages a row's 8 scale
-// bytes also stores the row's largest in-group exponent gap, and each wave checks its 64
-// rows and 64 columns. A stage that passes runs a branch-free body of 4 groups whose
-// additions are plain float adds (the K loop runs in round-toward-zero mode and contains
-// no other rounding-sensitive operation).
+// Scales: per stage (4 groups) the thread that owns an operand row loads the row's 8 E8M0
+// bytes and stages them as two words, one per K-half (byte g = group g, the byte the MFMA
+// picks with op_sel g); each staging wave also stores the largest in-group exponent gap
+// |e0 - e1| of its 64 rows. While the A rows' and B rows' largest gaps sum to at most 10,
+// every group of the stage passes and the tile runs branch-free stages whose additions are
+// plain float adds (the K loop runs in round-toward-zero mode and contains no other
+// rounding-sensitive operation). From the first stage that fails, the tile finishes in a
+// simple loop that tests each group.
+//
+// The per-group float32 add bounds this kernel: 16 v_add_f32 per lane per 32x32x64 MFMA,
+// which the vector ALU issues in about the time the matrix core takes for the MFMA, and
+// the two overlap only in part. The stage loop is therefore kept free of other vector
+// work: fragment addresses are one per-lane base XOR a group constant plus immediate
+// offsets, and the direct-to-LDS loads use a scalar base plus a per-lane offset.
 #include "gemm_common.hpp"
 
 namespace fp4k {
@@ -28,74 +37,93 @@ constexpr int SCB = SGR * 2;    // E8M0 scale bytes per row per stage (8)
 
 __device__ __forceinline__ int iabs(int x) { return x < 0 ? -x : x; }
 
+// Maximum over the wave, returned wave-uniform: xor swizzles within each 32-lane half
+// (ds_swizzle bit mode: and 0x1F, xor m), then the two halves' lane 0 values.
 __device__ __forceinline__ int wave_max_i(int d) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) d = max(d, __shfl_xor(d, o, 64));
-  return d;
+  d = max(d, __builtin_amdgcn_ds_swizzle(d, (1 << 10) | 0x1F));
+  d = max(d, __builtin_amdgcn_ds_swizzle(d, (2 << 10) | 0x1F));
+  d = max(d, __builtin_amdgcn_ds_swizzle(d, (4 << 10) | 0x1F));
+  d = max(d, __builtin_amdgcn_ds_swizzle(d, (8 << 10) | 0x1F));
+  d = max(d, __builtin_amdgcn_ds_swizzle(d, (16 << 10) | 0x1F));
+  return max(__builtin_amdgcn_readlane(d, 0), __builtin_amdgcn_readlane(d, 32));
 }
 
-// Scale bytes of one operand row, staged once per stage by one thread:
-// .x/.y = the stage's 8 E8M0 bytes (group g: bytes 2g, 2g+1), .z = largest |e0 - e1| over
-// the stage's groups. Rows past the matrix and groups past K read as 127 (2^0).
+// Scale bytes of one operand row, staged once per stage by one thread. load() fetches the
+// stage's 8 E8M0 bytes (group g: bytes 2g and 2g+1, its two K-blocks, in one 2-byte
+// load); split() turns them
+// into h0 (K-block 0 of groups 0..3, byte g) and h1 (K-block 1) and the largest |e0 - e1|
+// over the stage's groups. The two are separate so that nothing waits for the load before
+// the stage's compute has been issued (a wait on it would also wait for the payload loads
+// issued before it). Rows past the matrix and groups past K read as 127 (2^0).
 struct ScaleStager {
-  const uint8_t* p;
+  const uint8_t* p;   // the row, clamped to the last row of the matrix
   int64_t nblk;
-  bool fast_load;
 
   __device__ __forceinline__ void init(const uint8_t* s, int64_t row, int64_t rows, int64_t nb) {
     nblk = nb;
-    p = row < rows ? s + row * nb : nullptr;
-    fast_load = (nb & 7) == 0 && (reinterpret_cast<uintptr_t>(s) & 7) == 0;
+    p = s + (row < rows ? row : rows - 1) * nb;
   }
+  // Unconditional: four 2-byte loads (the scale pointer is 2-byte aligned and K/32 is even)
+  // at positions clamped into the row. Rows past the matrix and groups past K read real
+  // scale bytes of another row or group: their values reach only outputs that are not
+  // stored or groups that are not computed, and in the gap test they are real gaps (the
+  // test stays conservative). Any condition on the load would let the compiler predicate
+  // it and wait for it at once, and a wait on it also waits for the payload loads issued
+  // before it.
+  // (the four loads stay separate values until split(): combining them here would wait)
   __device__ __forceinline__ uint4 load(int64_t st) const {
-    uint32_t w0 = 0x7F7F7F7Fu, w1 = 0x7F7F7F7Fu;
-    if (p) {
-      if (fast_load && (st + 1) * SCB <= nblk) {
-        const uint2 v = *reinterpret_cast<const uint2*>(p + st * SCB);
-        w0 = v.x;
-        w1 = v.y;
-      } else {
-        uint32_t w[2] = {0, 0};
-#pragma unroll
-        for (int i = 0; i < SCB; ++i) {
-          const uint32_t b = (st * SCB + i < nblk) ? p[st * SCB + i] : 0x7Fu;
-          w[i >> 2] |= b << (8 * (i & 3));
-        }
-        w0 = w[0];
-        w1 = w[1];
-      }
-    }
-    int gap = 0;
+    uint32_t h[SGR];
 #pragma unroll
     for (int g = 0; g < SGR; ++g) {
-      const uint32_t h = (g < 2 ? w0 : w1) >> (16 * (g & 1));
-      gap = max(gap, iabs((int)(h & 0xFFu) - (int)((h >> 8) & 0xFFu)));
+      const int64_t i = st * SCB + 2 * g;
+      h[g] = *reinterpret_cast<const uint16_t*>(p + (i < nblk ? i : nblk - 2));
     }
-    return make_uint4(w0, w1, (uint32_t)gap, 0u);
+    return make_uint4(h[0], h[1], h[2], h[3]);
+  }
+  __device__ __forceinline__ static void split(uint4 q, uint32_t& h0, uint32_t& h1, int& gap) {
+    const uint32_t x = q.x | (q.y << 16), y = q.z | (q.w << 16);
+    h0 = __builtin_amdgcn_perm(y, x, 0x06040200u);
+    h1 = __builtin_amdgcn_perm(y, x, 0x07050301u);
+    gap = 0;
+#pragma unroll
+    for (int g = 0; g < SGR; ++g)
+      gap = max(gap, iabs((int)((h0 >> (8 * g)) & 0xFFu) - (int)((h1 >> (8 * g)) & 0xFFu)));
   }
 };
-
-// The four scale bytes (groups 0..3) of this lane's K-half: bytes 0,2,4,6 of the staged
-// pair (x, y) for lanes 0-31, bytes 1,3,5,7 for lanes 32-63; the MFMA picks group g's byte
-// with op_sel g.
-__device__ __forceinline__ uint32_t half_bytes(uint4 v, int half) {
-  return __builtin_amdgcn_perm(v.y, v.x, half ? 0x07050301u : 0x06040200u);
-}
 
 template <int G>
 __device__ __forceinline__ v16f mfma_g(const v8i& a, const v8i& b, uint32_t sa, uint32_t sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, v16f{}, 4, 4, G, (int)sa, G, (int)sb);
 }
 
-__device__ __forceinline__ void load_frags(const uint8_t* la, const uint8_t* lb, int ra0, int rb0, int half, int g,
-                                           v8i (&fa)[2], v8i (&fb)[2]) {
+__device__ __forceinline__ v16f mfma_sel(int g, const v8i& a, const v8i& b, uint32_t sa, uint32_t sb) {
+  if (g == 0) return mfma_g<0>(a, b, sa, sb);
+  if (g == 1) return mfma_g<1>(a, b, sa, sb);
+  if (g == 2) return mfma_g<2>(a, b, sa, sb);
+  return mfma_g<3>(a, b, sa, sb);
+}
+
+// LDS fragment addressing. Lane l reads row r = r0 + (l & 31) (r0 a multiple of 32) at
+// logical chunk c = 2g + half of group g. With key = (r >> 1) & 7 = 2 k2 + k1 the stored
+// chunk position is c ^ key = 2 (g ^ k2) + (half ^ k1), so the byte offset is
+// r * 128 + 32 (g ^ k2) + 16 (half ^ k1) = L ^ (g << 5) with the per-lane base
+// L = r * 128 + 32 k2 + 16 (half ^ k1). Tile t of the wave (rows + 32 t, same key) adds 4096 t.
+__device__ __forceinline__ uint32_t frag_lane_base(int r0, int l) {
+  const int r = r0 + (l & 31), key = (r >> 1) & 7, half = l >> 5;
+  return (uint32_t)(r * ROWB + ((key >> 1) << 5) + ((half ^ (key & 1)) << 4));
+}
+__device__ __forceinline__ v8i frag(const uint8_t* lds, uint32_t L, int t, int g) {
+  const uint4 v = *reinterpret_cast<const uint4*>(lds + (L ^ (uint32_t)(g << 5)) + t * 32 * ROWB);
+  return v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void load_frags(const uint8_t* la, const uint8_t* lb, uint32_t La, uint32_t Lb, int g,
+                                           v8i (&fa)[TM], v8i (&fb)[TN]) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const uint4 va = *reinterpret_cast<const uint4*>(la + swz(ra0 + t * 32, g * 2 + half));
-    const uint4 vb = *reinterpret_cast<const uint4*>(lb + swz(rb0 + t * 32, g * 2 + half));
-    fa[t] = v8i{(int)va.x, (int)va.y, (int)va.z, (int)va.w, 0, 0, 0, 0};
-    fb[t] = v8i{(int)vb.x, (int)vb.y, (int)vb.z, (int)vb.w, 0, 0, 0, 0};
-  }
+  for (int t = 0; t < TM; ++t) fa[t] = frag(la, La, t, g);
+#pragma unroll
+  for (int t = 0; t < TN; ++t) fb[t] = frag(lb, Lb, t, g);
 }
 
 __device__ __forceinline__ void add_tile(v16f& acc, const v16f& G) {
@@ -103,165 +131,252 @@ __device__ __forceinline__ void add_tile(v16f& acc, const v16f& G) {
   for (int r = 0; r < 16; ++r) acc[r] = acc[r] + G[r];   // round toward zero (K-loop mode)
 }
 
-// A full stage of 4 groups x 4 tiles, software-pipelined: the MFMA of unit u+1 is issued
-// before the 16 additions of unit u (two partial buffers), and the fragments of group g+1
-// are read from LDS while group g is computed.
-__device__ __forceinline__ void fast_stage(const uint8_t* la, const uint8_t* lb, int ra0, int rb0, int half,
-                                           const uint32_t (&sa)[2], const uint32_t (&sb)[2], v16f (&acc)[2][2]) {
-  v8i fa[2][2], fb[2][2];
-  load_frags(la, lb, ra0, rb0, half, 0, fa[0], fb[0]);
-  v16f Gb[2];
-  int pi = -1, pj = -1;
+// Largest |e0 - e1| of group g over the wave's rows (TM row tiles from the A rows, TN from
+// the B rows at offset bm), as a wave-uniform value. sw points at the stage's [K-half][row]
+// scale words (K-half stride nr).
+template <int TM, int TN>
+__device__ __forceinline__ int group_gap_sum(const uint32_t* sw, int nr, int ra0, int rb0, int bm, int g) {
+  int dga = 0, dgb = 0;
 #pragma unroll
-  for (int g = 0; g < SGR; ++g) {
-    if (g + 1 < SGR) load_frags(la, lb, ra0, rb0, half, g + 1, fa[(g + 1) & 1], fb[(g + 1) & 1]);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int i = t >> 1, j = t & 1;
-      const int u = g * 4 + t;
-      v16f& cur = Gb[u & 1];
-      if (g == 0) cur = mfma_g<0>(fa[0][i], fb[0][j], sa[i], sb[j]);
-      else if (g == 1) cur = mfma_g<1>(fa[1][i], fb[1][j], sa[i], sb[j]);
-      else if (g == 2) cur = mfma_g<2>(fa[0][i], fb[0][j], sa[i], sb[j]);
-      else cur = mfma_g<3>(fa[1][i], fb[1][j], sa[i], sb[j]);
-      if (u > 0) add_tile(acc[pi][pj], Gb[(u - 1) & 1]);
-      pi = i;
-      pj = j;
-    }
+  for (int t = 0; t < TM; ++t) {
+    const int r = ra0 + t * 32;
+    dga = max(dga, iabs((int)((sw[r] >> (8 * g)) & 0xFFu) - (int)((sw[nr + r] >> (8 * g)) & 0xFFu)));
   }
-  add_tile(acc[pi][pj], Gb[1]);
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    const int r = bm + rb0 + t * 32;
+    dgb = max(dgb, iabs((int)((sw[r] >> (8 * g)) & 0xFFu) - (int)((sw[nr + r] >> (8 * g)) & 0xFFu)));
+  }
+  return wave_max_i(dga) + wave_max_i(dgb);
 }
 
-__global__ __launch_bounds__(GNT, 2) void k_gemm_mx(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
-                                                    const uint8_t* __restrict__ qb, const uint8_t* __restrict__ sb,
-                                                    const float* __restrict__ ga, const float* __restrict__ gb,
-                                                    float* __restrict__ c, int64_t M, int64_t N, int64_t K, int canon,
-                                                    int hadamard_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lA[2][TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t lB[2][TILE_BYTES];
-  __shared__ uint4 lS[2][2 * GT];   // [buf][A rows 0..127, B rows 0..127]
-  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  int64_t m0, n0;
-  tile_coords(M, N, m0, n0);
-  const int64_t nblk = K / 32;   // E8M0 scales per row
-  const int64_t ngroups = K / 64;
-  const int64_t nstages = (K + KS - 1) / KS;
-  const int half = l >> 5;
-  const int ra0 = wm * 64 + (l & 31), rb0 = wn * 64 + (l & 31);
-
-  v16f acc[2][2];
+// A full stage (4 groups) for a tile whose every group passed the gap test: one MFMA per
+// group partial, software-pipelined (the MFMA of unit u+1 is issued before the 16
+// additions of unit u; two partial buffers). All tile indices are compile-time constants.
+#ifndef FP4_MX_PIPE
+#define FP4_MX_PIPE 0
+#endif
+template <int TM, int TN>
+__device__ __forceinline__ void fast_stage(const uint8_t* la, const uint8_t* lb, uint32_t La, uint32_t Lb,
+                                           const uint32_t (&sa)[TM], const uint32_t (&sb)[TN],
+                                           v16f (&acc)[TM][TN]) {
+  if (FP4_MX_PIPE) {
+    v16f Gb[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int g = 0; g < SGR; ++g) {
+      v8i fa[TM], fb[TN];
+      load_frags<TM, TN>(la, lb, La, Lb, g, fa, fb);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  StageLoader LA, LB;
-  LA.init(qa, M, K, m0);
-  LB.init(qb, N, K, n0);
-  ScaleStager SS;
-  if (threadIdx.x < GT) SS.init(sa, m0 + threadIdx.x, M, nblk);
-  else SS.init(sb, n0 + threadIdx.x - GT, N, nblk);
-  uint4 sreg = SS.load(0);
-  if (nstages > 0) {
-    LA.issue(0, lA[0]);
-    LB.issue(0, lB[0]);
-  }
-  lS[0][threadIdx.x] = sreg;
-  wait_vm();
-  __syncthreads();
-
-  mode_f32_rtz();
-  for (int64_t st = 0; st < nstages; ++st) {
-    const int buf = (int)(st & 1);
-    if (st + 1 < nstages) {
-      LA.issue(st + 1, lA[buf ^ 1]);
-      LB.issue(st + 1, lB[buf ^ 1]);
-      sreg = SS.load(st + 1);
-    }
-    const uint4 sA0 = lS[buf][ra0], sA1 = lS[buf][ra0 + 32];
-    const uint4 sB0 = lS[buf][GT + rb0], sB1 = lS[buf][GT + rb0 + 32];
-    const uint32_t sa4[2] = {half_bytes(sA0, half), half_bytes(sA1, half)};
-    const uint32_t sb4[2] = {half_bytes(sB0, half), half_bytes(sB1, half)};
-    const int da = (int)max(sA0.z, sA1.z), db = (int)max(sB0.z, sB1.z);
-    // sufficient for every output of the wave and every group of the stage: max|da| + max|db| <= 10
-    bool fast = !__any(da > 5 || db > 5);
-    if (!fast) fast = wave_max_i(da) + wave_max_i(db) <= 10;
-    const int g_end = (int)((ngroups - st * SGR) < SGR ? (ngroups - st * SGR) : SGR);
-    if (fast && g_end == SGR) {
-      fast_stage(lA[buf], lB[buf], ra0, rb0, half, sa4, sb4, acc);
-    } else {
-      for (int g = 0; g < g_end; ++g) {
-        v8i fa[2], fb[2];
-        int ea[2], eb[2];
-        int dga = 0, dgb = 0;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const uint4 va = *reinterpret_cast<const uint4*>(lA[buf] + swz(ra0 + t * 32, g * 2 + half));
-          const uint4 vb = *reinterpret_cast<const uint4*>(lB[buf] + swz(rb0 + t * 32, g * 2 + half));
-          fa[t] = v8i{(int)va.x, (int)va.y, (int)va.z, (int)va.w, 0, 0, 0, 0};
-          fb[t] = v8i{(int)vb.x, (int)vb.y, (int)vb.z, (int)vb.w, 0, 0, 0, 0};
-          const uint4 pa = t ? sA1 : sA0, pb = t ? sB1 : sB0;
-          const uint32_t wa = (g < 2 ? pa.x : pa.y) >> (16 * (g & 1));
-          const uint32_t wb = (g < 2 ? pb.x : pb.y) >> (16 * (g & 1));
-          const int a0 = (int)(wa & 0xFFu), a1 = (int)((wa >> 8) & 0xFFu);
-          const int b0 = (int)(wb & 0xFFu), b1 = (int)((wb >> 8) & 0xFFu);
-          ea[t] = half ? a1 : a0;
-          eb[t] = half ? b1 : b0;
-          dga = max(dga, iabs(a0 - a1));
-          dgb = max(dgb, iabs(b0 - b1));
-        }
-        const bool gfast = wave_max_i(dga) + wave_max_i(dgb) <= 10;
-        if (gfast) {
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              const v16f Gt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], v16f{}, 4, 4, 0, ea[i], 0,
-                                                                              eb[j]);
-#pragma unroll
-              for (int r = 0; r < 16; ++r) acc[i][j][r] = acc[i][j][r] + Gt[r];
-            }
-        } else {
-          const v8i z = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const v8i fa0 = half == 0 ? fa[i] : z;
-            const v8i fa1 = half == 1 ? fa[i] : z;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              const v16f T0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa0, fb[j], v16f{}, 4, 4, 0, ea[i], 0,
-                                                                              eb[j]);
-              const v16f T1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa1, fb[j], v16f{}, 4, 4, 0, ea[i], 0,
-                                                                              eb[j]);
-              float Gs[16];
-              mode_f32_rne();
-#pragma unroll
-              for (int r = 0; r < 16; ++r) Gs[r] = T0[r] + T1[r];            // nearest-even group partial
-              mode_f32_rtz();
-#pragma unroll
-              for (int r = 0; r < 16; ++r) acc[i][j][r] = acc[i][j][r] + Gs[r];
-            }
-          }
+      for (int t = 0; t < TM * TN; ++t) {
+        const int u = g * TM * TN + t;
+        Gb[u & 1] = mfma_sel(g, fa[t / TN], fb[t % TN], sa[t / TN], sb[t % TN]);
+        if (u > 0) {
+          const int p = (u - 1) % (TM * TN);
+          add_tile(acc[p / TN][p % TN], Gb[(u - 1) & 1]);
         }
       }
     }
-    if (st + 1 < nstages) {
-      lS[buf ^ 1][threadIdx.x] = sreg;
+    constexpr int last = SGR * TM * TN - 1;
+    add_tile(acc[(last % (TM * TN)) / TN][(last % (TM * TN)) % TN], Gb[last & 1]);
+  } else {
+#pragma unroll
+    for (int g = 0; g < SGR; ++g) {
+      v8i fa[TM], fb[TN];
+      load_frags<TM, TN>(la, lb, La, Lb, g, fa, fb);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) add_tile(acc[i][j], mfma_sel(g, fa[i], fb[j], sa[i], sb[j]));
+    }
+  }
+}
+
+// Groups [0, g_end) of a stage, one group at a time. With check set, each group is tested
+// for the exponent gap and a failing group's partials are two MFMAs with the other
+// K-block's payload zeroed, added in float32 nearest-even.
+template <int TM, int TN>
+__device__ __forceinline__ void plain_stage(const uint8_t* la, const uint8_t* lb, uint32_t La, uint32_t Lb,
+                                            const uint32_t (&sa)[TM], const uint32_t (&sb)[TN], bool check,
+                                            int g_end, const uint32_t* sw, int nr, int ra0, int rb0, int bm,
+                                            int half, v16f (&acc)[TM][TN]) {
+  for (int g = 0; g < g_end; ++g) {
+    const bool gf = !check || group_gap_sum<TM, TN>(sw, nr, ra0, rb0, bm, g) <= 10;
+    if (gf) {
+      v8i fa[TM], fb[TN];
+      load_frags<TM, TN>(la, lb, La, Lb, g, fa, fb);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) add_tile(acc[i][j], mfma_sel(g, fa[i], fb[j], sa[i], sb[j]));
+    } else {
+      // one tile at a time, fragments read just in time: this path keeps few registers live
+      const v8i z = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const v8i fa = frag(la, La, i, g);
+          const v8i fb = frag(lb, Lb, j, g);
+          const v16f T0 = mfma_sel(g, half == 0 ? fa : z, fb, sa[i], sb[j]);
+          const v16f T1 = mfma_sel(g, half == 1 ? fa : z, fb, sa[i], sb[j]);
+          add_tile(acc[i][j], add_rne_from_rtz(T0, T1));   // nearest-even group partial, then toward zero
+        }
+      }
+    }
+  }
+}
+
+#ifndef FP4_MX_MINB
+#define FP4_MX_MINB 4
+#endif
+
+// LDS of one workgroup: double-buffered payload tiles, scale words and gap maxima.
+template <class TL>
+struct MxSmem {
+  static constexpr int NR = TL::BM + TL::BN;
+  uint8_t a[2][TL::BM * ROWB];
+  uint8_t b[2][TL::BN * ROWB];
+  uint32_t sw[2][2][NR];      // [buf][K-half][A rows, then B rows]
+  int gmax[2][NR / 64];       // [buf][staging wave] largest in-group exponent gap of its rows
+};
+
+template <class TL>
+__global__ __launch_bounds__(TL::NT, FP4_MX_MINB) void k_gemm_mx(
+    const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const uint8_t* __restrict__ qb,
+    const uint8_t* __restrict__ sb, const float* __restrict__ ga, const float* __restrict__ gb, float* __restrict__ c,
+    int64_t M, int64_t N, int64_t K, int canon, int hadamard_n) {
+  constexpr int TM = TL::TM, TN = TL::TN, BM = TL::BM, BN = TL::BN, NR = BM + BN;
+  static_assert(TL::NT >= NR && BM % 64 == 0 && BN % 64 == 0, "one thread per staged scale row, whole waves");
+  __shared__ __attribute__((aligned(1024))) MxSmem<TL> sm;
+  const int l = threadIdx.x & 63, w = wave_id(), t = threadIdx.x;
+  const int wm = w / TL::WN, wn = w % TL::WN;
+  int64_t m0, n0;
+  tile_coords(M, N, BM, BN, m0, n0);
+  const int64_t nblk = K / 32;   // E8M0 scales per row
+  const int64_t ngroups = K / 64;
+  const int64_t nstages = (K + KS - 1) / KS;
+  const int64_t nfull = ngroups / SGR;   // stages with 4 groups
+  const int half = l >> 5;
+  const int ra0 = wm * (TM * 32) + (l & 31), rb0 = wn * (TN * 32) + (l & 31);
+  const uint32_t La = frag_lane_base(wm * (TM * 32), l), Lb = frag_lane_base(wn * (TN * 32), l);
+
+  StageLoader<BM, TL::NW> LA;
+  StageLoader<BN, TL::NW> LB;
+  LA.init(qa, M, K, m0);
+  LB.init(qb, N, K, n0);
+  // scale rows: whole waves (threads below NR), one row each; A rows first
+  const bool stager = w < NR / 64;
+  ScaleStager SS;
+  if (t < BM) SS.init(sa, m0 + t, M, nblk);
+  else SS.init(sb, n0 + t - BM, N, nblk);
+  uint4 sraw = make_uint4(0, 0, 0, 0);   // the next stage's scale bytes, in flight during a stage
+  auto load_scales = [&](int64_t st) {
+    if (stager) sraw = SS.load(st);
+  };
+  auto store_scales = [&](int buf) {
+    if (stager) {
+      uint32_t h0, h1;
+      int gap;
+      ScaleStager::split(sraw, h0, h1, gap);
+      sm.sw[buf][0][t] = h0;
+      sm.sw[buf][1][t] = h1;
+      const int gm = wave_max_i(gap);
+      if (l == 0) sm.gmax[buf][w] = gm;
+    }
+  };
+  // every group of the stage in buffer buf passes the gap test (wave-uniform)
+  auto stage_passes = [&](int buf) {
+    int gA = 0, gB = 0;
+#pragma unroll
+    for (int i = 0; i < BM / 64; ++i) gA = max(gA, sm.gmax[buf][i]);
+#pragma unroll
+    for (int i = BM / 64; i < NR / 64; ++i) gB = max(gB, sm.gmax[buf][i]);
+    return __builtin_amdgcn_readfirstlane(gA) + __builtin_amdgcn_readfirstlane(gB) <= 10;
+  };
+
+  if (nstages > 0) {
+    LA.issue(0, sm.a[0]);
+    LB.issue(0, sm.b[0]);
+  }
+  load_scales(0);
+  store_scales(0);
+  wait_vm();
+  __syncthreads();
+
+  v16f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  mode_f32_rtz();
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) pin(acc[i][j]);   // additions after the switch
+
+  int64_t st = 0;
+  // full stages whose every group passes: one MFMA per group partial
+  for (; st < nfull; ++st) {
+    const int buf = (int)(st & 1);
+    if (!stage_passes(buf)) break;
+    const bool more = st + 1 < nstages;
+    if (more) {
+      LA.issue(st + 1, sm.a[buf ^ 1]);
+      LB.issue(st + 1, sm.b[buf ^ 1]);
+      load_scales(st + 1);
+    }
+    uint32_t s4a[TM], s4b[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) s4a[i] = sm.sw[buf][half][ra0 + i * 32];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) s4b[j] = sm.sw[buf][half][BM + rb0 + j * 32];
+    fast_stage<TM, TN>(sm.a[buf], sm.b[buf], La, Lb, s4a, s4b, acc);
+    if (more) {
+      store_scales(buf ^ 1);
       wait_vm();
       __syncthreads();
     }
   }
-  store_tiles(c, M, N, m0 + wm * 64, n0 + wn * 64, acc, ga, gb, canon, hadamard_n);
+  // the rest (a stage that failed, then every later one, and a partial last stage): each
+  // group tested on its own
+  for (; st < nstages; ++st) {
+    const int buf = (int)(st & 1);
+    const bool more = st + 1 < nstages;
+    if (more) {
+      LA.issue(st + 1, sm.a[buf ^ 1]);
+      LB.issue(st + 1, sm.b[buf ^ 1]);
+      load_scales(st + 1);
+    }
+    uint32_t s4a[TM], s4b[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) s4a[i] = sm.sw[buf][half][ra0 + i * 32];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) s4b[j] = sm.sw[buf][half][BM + rb0 + j * 32];
+    const int g_end = (int)((ngroups - st * SGR) < SGR ? (ngroups - st * SGR) : SGR);
+    plain_stage<TM, TN>(sm.a[buf], sm.b[buf], La, Lb, s4a, s4b, true, g_end, &sm.sw[buf][0][0], NR, ra0, rb0, BM,
+                        half, acc);
+    if (more) {
+      store_scales(buf ^ 1);
+      wait_vm();
+      __syncthreads();
+    }
+  }
+  store_tiles<TM, TN>(c, M, N, m0 + wm * (TM * 32), n0 + wn * (TN * 32), acc, ga, gb, canon, hadamard_n);
 }
+
+#ifndef FP4_MX_TILING
+#define FP4_MX_TILING 2, 4, 2, 1
+#endif
+using MxTiling = Tiling<FP4_MX_TILING>;
 
 hipError_t run_gemm_mx(const GemmArgs& g) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
-  const int64_t tiles = ((g.M + GT - 1) / GT) * ((g.N + GT - 1) / GT);
-  hipLaunchKernelGGL(k_gemm_mx, dim3((unsigned)tiles), dim3(GNT), 0, g.stream, g.a.q, g.a.s, g.b.q, g.b.s, g.a.g,
-                     g.b.g, g.c, g.M, g.N, g.K, g.canon, g.hadamard_n);
+  using TL = MxTiling;
+  const int64_t tiles = ((g.M + TL::BM - 1) / TL::BM) * ((g.N + TL::BN - 1) / TL::BN);
+  hipLaunchKernelGGL(k_gemm_mx<TL>, dim3((unsigned)tiles), dim3(TL::NT), 0, g.stream, g.a.q, g.a.s, g.b.q, g.b.s,
+                     g.a.g, g.b.g, g.c, g.M, g.N, g.K, g.canon, g.hadamard_n);
   return hipGetLastError();
 }
 
