@@ -11,14 +11,20 @@
 // Hadamard rotation of the weight-gradient operands, fused here into the transposed pass.
 //
 // Kernels:
-//   k_quant_row   ROW view: one thread per B-element block along the row; 16-byte loads.
-//   k_quant_col   COL view: a 256-token x 64-feature tile staged in LDS; each thread owns a
-//                 16/32-token run of one feature (optionally rotated by the FWHT), writes its
-//                 payload to an LDS output tile, which is stored row-contiguously.
+//   k_quant_row   ROW view: one thread per B-element block along the row, two rows per
+//                 thread with both rows' loads issued first; a workgroup covers several rows
+//                 when a row has fewer than 256 blocks; 16-byte loads.
+//   k_quant_col   COL view: a 128-token x 64-feature tile staged in LDS (four workgroups fit a
+//                 CU); each thread owns a 16/32-token run of one feature (optionally rotated by
+//                 the FWHT), writes its payload to an LDS output tile, which is stored
+//                 row-contiguously.
 //   k_quant_2d    TILE2D: a 64x64 tile in LDS; tile amaxes by lane shuffles; both the forward
 //                 payload (row segments) and the transposed payload (column segments).
-//   k_amax_*      max|x| (plain, or along-token FWHT for Hadamard views) by atomicMax on the
-//                 float bits (non-negative floats order like unsigned integers).
+//   k_amax_*      max|x| (plain, or along-token FWHT for Hadamard views): a workgroup max, then
+//                 one atomicMax per workgroup on the float bits (non-negative floats order like
+//                 unsigned integers).
+// The quantize kernels also write the operand's g (workgroup 0, thread 0) and, if asked,
+// fold their block maxima into the observed amax (one atomic per workgroup).
 #include "fp4_device.hpp"
 #include "launch.hpp"
 
@@ -34,6 +40,26 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ void atomic_max_nonneg(float* p, float v) {
   atomicMax(reinterpret_cast<unsigned int*>(p), __float_as_uint(v));
+}
+
+// Workgroup max of a non-negative value folded into *out with one atomic (all NT threads call).
+__device__ __forceinline__ void wg_max_to(float* out, float v) {
+  __shared__ float part[NT / 64];
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = part[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) m = fmaxf(m, part[i]);
+    atomic_max_nonneg(out, m);
+  }
+}
+
+// g of the operand (1 for E8M0), written once per launch.
+template <int FMT>
+__device__ __forceinline__ void write_g(float* d_g, const TensorScales& ts) {
+  if (d_g && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *d_g = (FMT == FMT_E8M0) ? 1.0f : ts.g;
 }
 
 // Load 8 consecutive input elements (bf16 or fp32) as floats.
@@ -88,44 +114,67 @@ __device__ __forceinline__ void payload(const float* v, float mult, uint64_t i0,
 }
 
 // ---------------------------------------------------------------- ROW view
+// Thread layout: TPR threads per row (a power of two, at most NT), NT / TPR rows per pass;
+// block index b = blockIdx.x * TPR + (thread % TPR). Each thread does rows r and r + RPW/2
+// of a group of RPW = 2 NT / TPR rows, both rows' loads issued before either is used.
+template <int B, bool F32>
+__device__ __forceinline__ void load_block(const void* x, int64_t elem, float (&v)[B]) {
+#pragma unroll
+  for (int j = 0; j < B / 8; ++j) load8<F32>(x, elem + 8 * j, v + 8 * j);
+}
+
+template <int FMT, int B, bool SR>
+__device__ __forceinline__ float quant_block_row(const float (&v)[B], const TensorScales& ts, int64_t r, int64_t b,
+                                                 int64_t cols, uint64_t seed, uint64_t offset, uint8_t* __restrict__ q,
+                                                 uint8_t* __restrict__ s) {
+  float amax_b = 0.0f;
+#pragma unroll
+  for (int j = 0; j < B; ++j) amax_b = fmaxf(amax_b, fabsf(v[j]));
+  uint32_t code;
+  float mult;
+  block_scale<FMT>(amax_b, ts, code, mult);
+  uint32_t words[B / 8];
+  payload<B, SR>(v, mult, (uint64_t)(r * cols + b * B), seed, offset, words);
+  uint8_t* qp = q + r * (cols / 2) + b * (B / 2);
+  if constexpr (B == 16) *reinterpret_cast<uint2*>(qp) = make_uint2(words[0], words[1]);
+  else *reinterpret_cast<uint4*>(qp) = make_uint4(words[0], words[1], words[2], words[3]);
+  s[r * (cols / B) + b] = (uint8_t)code;
+  return amax_b;
+}
+
 template <int FMT, int B, bool SR, bool F32>
 __global__ __launch_bounds__(NT) void k_quant_row(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
-                                                  const float* __restrict__ d_amax, float T, uint64_t seed,
-                                                  uint64_t offset, uint8_t* __restrict__ q, uint8_t* __restrict__ s,
-                                                  float* __restrict__ d_amax_obs) {
+                                                  int tpr_log2, const float* __restrict__ d_amax, float T,
+                                                  uint64_t seed, uint64_t offset, uint8_t* __restrict__ q,
+                                                  uint8_t* __restrict__ s, float* __restrict__ d_amax_obs,
+                                                  float* __restrict__ d_g) {
+  const int tpr = 1 << tpr_log2;
+  const int half_rows = NT >> tpr_log2;                // rows per pass
   const int64_t nbr = cols / B;
-  const int64_t b = (int64_t)blockIdx.x * NT + threadIdx.x;
+  const int64_t b = (int64_t)blockIdx.x * tpr + (threadIdx.x & (tpr - 1));
   TensorScales ts{1.0f, 1.0f, 1.0f};
   if constexpr (FMT != FMT_E8M0) ts = tensor_scales(d_amax, T);
+  write_g<FMT>(d_g, ts);
   float obs = 0.0f;
   if (b < nbr) {
-    for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
-      float v[B];
-#pragma unroll
-      for (int j = 0; j < B / 8; ++j) load8<F32>(x, r * ld + b * B + 8 * j, v + 8 * j);
-      float amax_b = 0.0f;
-#pragma unroll
-      for (int j = 0; j < B; ++j) amax_b = fmaxf(amax_b, fabsf(v[j]));
-      obs = fmaxf(obs, amax_b);
-      uint32_t code;
-      float mult;
-      block_scale<FMT>(amax_b, ts, code, mult);
-      uint32_t words[B / 8];
-      payload<B, SR>(v, mult, (uint64_t)(r * cols + b * B), seed, offset, words);
-      uint8_t* qp = q + r * (cols / 2) + b * (B / 2);
-      if constexpr (B == 16) *reinterpret_cast<uint2*>(qp) = make_uint2(words[0], words[1]);
-      else *reinterpret_cast<uint4*>(qp) = make_uint4(words[0], words[1], words[2], words[3]);
-      s[r * nbr + b] = (uint8_t)code;
+    // row groups of 2 * half_rows rows, strided over the grid (one group per workgroup
+    // unless the matrix has more than 65535 groups)
+    for (int64_t rg = blockIdx.y; rg * 2 * half_rows < rows; rg += gridDim.y) {
+      const int64_t r0 = rg * (2 * half_rows) + (threadIdx.x >> tpr_log2);
+      const int64_t r1 = r0 + half_rows;
+      const bool has0 = r0 < rows, has1 = r1 < rows;
+      float v0[B], v1[B];
+      if (has0) load_block<B, F32>(x, r0 * ld + b * B, v0);
+      if (has1) load_block<B, F32>(x, r1 * ld + b * B, v1);
+      if (has0) obs = fmaxf(obs, quant_block_row<FMT, B, SR>(v0, ts, r0, b, cols, seed, offset, q, s));
+      if (has1) obs = fmaxf(obs, quant_block_row<FMT, B, SR>(v1, ts, r1, b, cols, seed, offset, q, s));
     }
   }
-  if (d_amax_obs) {
-    obs = wave_max(obs);
-    if ((threadIdx.x & 63) == 0) atomic_max_nonneg(d_amax_obs, obs);
-  }
+  if (d_amax_obs) wg_max_to(d_amax_obs, obs);
 }
 
 // ---------------------------------------------------------------- COL view (wgrad operands)
-constexpr int CT = 256;   // tokens per tile
+constexpr int CT = 128;   // tokens per tile
 constexpr int CF = 64;    // features per tile
 
 template <int HN>
@@ -166,7 +215,7 @@ template <int FMT, int B, bool SR, bool F32, int HN>
 __global__ __launch_bounds__(NT) void k_quant_col(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
                                                   const float* __restrict__ d_amax, float T, uint64_t seed,
                                                   uint64_t offset, uint8_t* __restrict__ q, uint8_t* __restrict__ s,
-                                                  float* __restrict__ d_amax_obs) {
+                                                  float* __restrict__ d_amax_obs, float* __restrict__ d_g) {
   constexpr int U = (HN > B) ? HN : B;          // tokens per thread unit
   constexpr int UNITS = CT / U;                 // units per feature in a tile
   __shared__ float tile[CT][CF + 1];
@@ -178,6 +227,7 @@ __global__ __launch_bounds__(NT) void k_quant_col(const void* __restrict__ x, in
   __syncthreads();
   TensorScales ts{1.0f, 1.0f, 1.0f};
   if constexpr (FMT != FMT_E8M0) ts = tensor_scales(d_amax, T);
+  write_g<FMT>(d_g, ts);
   const int f = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   float obs = 0.0f;
@@ -222,10 +272,7 @@ __global__ __launch_bounds__(NT) void k_quant_col(const void* __restrict__ x, in
     const int ff = c / (CT / B), j = c % (CT / B);
     if (f0 + ff < cols && t0 + (int64_t)j * B < rows) s[(f0 + ff) * srow + t0 / B + j] = sout[ff][j];
   }
-  if (d_amax_obs) {
-    obs = wave_max(obs);
-    if ((threadIdx.x & 63) == 0) atomic_max_nonneg(d_amax_obs, obs);
-  }
+  if (d_amax_obs) wg_max_to(d_amax_obs, obs);
 }
 
 // ---------------------------------------------------------------- TILE2D (weights)
@@ -235,7 +282,7 @@ template <int FMT, bool F32>
 __global__ __launch_bounds__(NT) void k_quant_2d(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
                                                  const float* __restrict__ d_amax, float T, uint8_t* __restrict__ q,
                                                  uint8_t* __restrict__ qt, uint8_t* __restrict__ s,
-                                                 float* __restrict__ d_amax_obs) {
+                                                 float* __restrict__ d_amax_obs, float* __restrict__ d_g) {
   __shared__ float tile[WT][WT + 1];
   __shared__ float mults[WT / 16][WT / 16];
   const int64_t r0 = (int64_t)blockIdx.y * WT, c0 = (int64_t)blockIdx.x * WT;
@@ -253,6 +300,7 @@ __global__ __launch_bounds__(NT) void k_quant_2d(const void* __restrict__ x, int
   }
   __syncthreads();
   TensorScales ts = tensor_scales(d_amax, T);
+  write_g<FMT>(d_g, ts);
   // forward view: thread = (row r, 16-col segment sg); lanes 4k+sg of a wave share a 16x16 tile
   const int r = threadIdx.x >> 2, sg = threadIdx.x & 3;
   float v[16];
@@ -284,10 +332,7 @@ __global__ __launch_bounds__(NT) void k_quant_2d(const void* __restrict__ x, int
   payload<16, false>(v, mults[rs][cc >> 4], 0, 0, 0, words);
   if ((c0 + cc) < cols && (r0 + rs * 16) < rows)
     *reinterpret_cast<uint2*>(qt + (c0 + cc) * (rows / 2) + (r0 + rs * 16) / 2) = make_uint2(words[0], words[1]);
-  if (d_amax_obs) {
-    float o = wave_max(m);
-    if ((threadIdx.x & 63) == 0) atomic_max_nonneg(d_amax_obs, o);
-  }
+  if (d_amax_obs) wg_max_to(d_amax_obs, m);
 }
 
 // ---------------------------------------------------------------- amax
@@ -304,8 +349,7 @@ __global__ __launch_bounds__(NT) void k_amax_plain(const void* __restrict__ x, i
       for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
     }
   }
-  m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) atomic_max_nonneg(out, m);
+  wg_max_to(out, m);
 }
 
 template <bool F32, int HN>
@@ -325,8 +369,7 @@ __global__ __launch_bounds__(NT) void k_amax_hadamard(const void* __restrict__ x
 #pragma unroll
     for (int i = 0; i < HN; ++i) m = fmaxf(m, fabsf(v[i]));   // padded rows/cols are zero
   }
-  m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) atomic_max_nonneg(out, m);
+  wg_max_to(out, m);
 }
 
 __global__ void k_fill_f32(float* p, float v) { *p = v; }
@@ -359,14 +402,18 @@ __global__ void k_debug_encode(const float* __restrict__ x, const uint16_t* __re
 }
 
 // ---------------------------------------------------------------- launchers
-static inline unsigned grid_rows(int64_t rows) { return (unsigned)(rows < 65535 ? (rows > 0 ? rows : 1) : 65535); }
 
 template <int FMT, int B, bool SR, bool F32>
 static hipError_t launch_row(const QuantArgs& a) {
   const int64_t nbr = a.cols / B;
-  dim3 grid((unsigned)((nbr + NT - 1) / NT), grid_rows(a.rows));
-  hipLaunchKernelGGL((k_quant_row<FMT, B, SR, F32>), grid, dim3(NT), 0, a.stream, a.x, a.rows, a.cols, a.ld, a.d_amax,
-                     a.T, a.seed, a.offset, a.q, a.s, a.d_amax_obs);
+  int tpr_log2 = 0;
+  while ((1 << tpr_log2) < nbr && (1 << tpr_log2) < NT) ++tpr_log2;     // threads per row
+  const int64_t rows_per_wg = 2 * (NT >> tpr_log2);
+  const int64_t groups = (a.rows + rows_per_wg - 1) / rows_per_wg;
+  const unsigned gy = (unsigned)(groups < 65535 ? groups : 65535);     // the kernel strides over the rest
+  dim3 grid((unsigned)((nbr + (1 << tpr_log2) - 1) >> tpr_log2), gy);
+  hipLaunchKernelGGL((k_quant_row<FMT, B, SR, F32>), grid, dim3(NT), 0, a.stream, a.x, a.rows, a.cols, a.ld, tpr_log2,
+                     a.d_amax, a.T, a.seed, a.offset, a.q, a.s, a.d_amax_obs, a.d_g);
   return hipGetLastError();
 }
 
@@ -374,7 +421,7 @@ template <int FMT, int B, bool SR, bool F32, int HN>
 static hipError_t launch_col(const QuantArgs& a) {
   dim3 grid((unsigned)((a.rows + CT - 1) / CT), (unsigned)((a.cols + CF - 1) / CF));
   hipLaunchKernelGGL((k_quant_col<FMT, B, SR, F32, HN>), grid, dim3(NT), 0, a.stream, a.x, a.rows, a.cols, a.ld,
-                     a.d_amax, a.T, a.seed, a.offset, a.q, a.s, a.d_amax_obs);
+                     a.d_amax, a.T, a.seed, a.offset, a.q, a.s, a.d_amax_obs, a.d_g);
   return hipGetLastError();
 }
 
@@ -382,7 +429,7 @@ template <int FMT, bool F32>
 static hipError_t launch_2d(const QuantArgs& a) {
   dim3 grid((unsigned)((a.cols + WT - 1) / WT), (unsigned)((a.rows + WT - 1) / WT));
   hipLaunchKernelGGL((k_quant_2d<FMT, F32>), grid, dim3(NT), 0, a.stream, a.x, a.rows, a.cols, a.ld, a.d_amax, a.T, a.q,
-                     a.qt, a.s, a.d_amax_obs);
+                     a.qt, a.s, a.d_amax_obs, a.d_g);
   return hipGetLastError();
 }
 
@@ -414,12 +461,15 @@ hipError_t run_quantize(const QuantArgs& a) {
     hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, a.stream, a.d_amax_obs, 0.0f);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (a.d_g) {
-    hipLaunchKernelGGL(k_write_g, dim3(1), dim3(1), 0, a.stream, a.d_amax, a.T, a.fmt, a.d_g);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.rows == 0 || a.cols == 0) {
+    // nothing to quantize: g is still defined by the tensor scale
+    if (a.d_g) {
+      hipLaunchKernelGGL(k_write_g, dim3(1), dim3(1), 0, a.stream, a.d_amax, a.T, a.fmt, a.d_g);
+      return hipGetLastError();
+    }
+    return hipSuccess;
   }
-  if (a.rows == 0 || a.cols == 0) return hipSuccess;
-  return a.f32 ? dispatch_fmt<true>(a) : dispatch_fmt<false>(a);
+  return a.f32 ? dispatch_fmt<true>(a) : dispatch_fmt<false>(a);   // the kernel writes g
 }
 
 hipError_t run_amax(const void* x, bool f32, int64_t rows, int64_t cols, int64_t ld, int hadamard_n, float* out,
@@ -428,9 +478,11 @@ hipError_t run_amax(const void* x, bool f32, int64_t rows, int64_t cols, int64_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || rows == 0 || cols == 0) return e;
   if (hadamard_n == 0) {
+    // a bounded grid (at most 16 x 256 workgroups), each striding over many rows: one atomic
+    // per workgroup
     const int64_t chunks = cols / 8;
     const unsigned gx = (unsigned)((chunks + NT - 1) / NT > 16 ? 16 : (chunks + NT - 1) / NT);
-    const unsigned gy = (unsigned)(rows < 4096 ? rows : 4096);
+    const unsigned gy = (unsigned)(rows < 256 ? rows : 256);
     if (f32) hipLaunchKernelGGL(k_amax_plain<true>, dim3(gx, gy), dim3(NT), 0, stream, x, rows, cols, ld, out);
     else hipLaunchKernelGGL(k_amax_plain<false>, dim3(gx, gy), dim3(NT), 0, stream, x, rows, cols, ld, out);
     return hipGetLastError();
