@@ -179,11 +179,12 @@ __device__ __forceinline__ int tile_row(int r, int l) { return (r >> 2) * 8 + (l
 
 // Epilogue: nearest-even mode, optional canonicalisation, scale by alpha, store float32.
 // (m0, n0) is the wave's first output row and column; tile (i, j) covers rows m0 + 32i and
-// columns n0 + 32j.
+// columns n0 + 32j. pre (a power of two) undoes a constant factor the K loop carried; it is
+// exact and applied before the canonicalisation.
 template <int TM, int TN>
 __device__ __forceinline__ void store_tiles(float* __restrict__ c, int64_t M, int64_t N, int64_t m0, int64_t n0,
                                             v16f (&acc)[TM][TN], const float* ga, const float* gb, int canon,
-                                            int hadamard_n) {
+                                            int hadamard_n, float pre = 1.0f) {
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -203,7 +204,7 @@ __device__ __forceinline__ void store_tiles(float* __restrict__ c, int64_t M, in
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + rt * 32 + tile_row(r, l);
-        float v = acc[rt][ct][r];
+        float v = acc[rt][ct][r] * pre;
         if (canon) v = __builtin_rintf(v * 1024.0f) * (1.0f / 1024.0f);
         v = v * alpha;
         if (row < M && col < N) c[row * N + col] = v;

@@ -5,11 +5,16 @@
 // section (한계): UE5M3 has no native hardware support, so it runs through an exact route.
 //
 // The gfx950 scaled MFMA carries only power-of-two scales per 32 elements, so it cannot
-// apply a UE5M3/E4M3 scale per 16 elements. Every decoded operand value q*S (E2M1 times a
-// 4-significant-bit scale) has at most 6 significant bits and lies within bf16 range, so
-// it is exact in bf16; one v_mfma_f32_32x32x16_bf16 with C = 0 then returns the exact
-// partial sum of a 16-wide K slice (all 16 products share one scale pair, so the sum has
-// at most 21 significant bits). The slices are combined on the VALU:
+// apply a UE5M3/E4M3 scale per 16 elements. The operands are decoded exactly to fp16
+// instead, shifted by 2^-3: with S = M 2^E (M in [1, 2), at most 4 significant bits),
+// v_cvt_scalef32_pk_f16_fp4 gives q 2^(E-3) and one v_pk_mul_f16 multiplies by M. Every
+// value q S 2^-3 has at most 6 significant bits and lies in [2^-21, 46080], inside fp16
+// (subnormals included), so both steps are exact. One v_mfma_f32_32x32x16_f16 with C = 0
+// then returns 2^-6 times the exact partial sum of a 16-wide K slice (all 16 products share
+// one scale pair, so the sum has at most 21 significant bits). All sums below carry the same
+// 2^-6 factor; a power-of-two factor commutes with every rounding of the model (no value
+// comes near the float32 subnormal or overflow range), and the epilogue removes it. The
+// slices are combined on the VALU:
 //   block 16: G = ((T0 + T1) + T2) + T3, each add float32 nearest-even;
 //   block 32: G = (T0 + T1) + (T2 + T3); the inner adds are exact (same scale pair), the
 //             outer one nearest-even.
@@ -19,22 +24,34 @@
 
 namespace fp4k {
 
-// 8 E2M1 codes (one dword, element 0 in the low nibble) times scale value S -> 8 bf16.
-__device__ __forceinline__ v8bf decode8(uint32_t codes, float S) {
-  typedef float v2f __attribute__((ext_vector_type(2)));
-  v2f qq[4];
-  qq[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
-  qq[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
-  qq[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
-  qq[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
-  uint32_t o[4];
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+// The decode factors of scale value S = M 2^E: 2^(E-3) as float (for the convert) and M as a
+// packed fp16 pair (for the multiply). S is a normal float32 for every UE5M3/E4M3 code.
+struct DecScale {
+  float p2;
+  v2h m2;
+};
+__device__ __forceinline__ DecScale dec_factors(float S) {
+  const uint32_t b = __float_as_uint(S);
+  DecScale d;
+  d.p2 = __uint_as_float((b & 0x7F800000u) - (3u << 23));
+  const _Float16 m = (_Float16)__uint_as_float((b & 0x007FFFFFu) | 0x3F800000u);   // exact
+  d.m2 = v2h{m, m};
+  return d;
+}
+
+// 8 E2M1 codes (one dword, element 0 in the low nibble) times S 2^-3 -> 8 fp16, exactly.
+__device__ __forceinline__ v8h decode8(uint32_t codes, const DecScale& d) {
+  v2h h[4];
+  h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, d.p2, 0);
+  h[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, d.p2, 1);
+  h[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, d.p2, 2);
+  h[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, d.p2, 3);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float x = qq[j].x * S;   // exact
-    const float y = qq[j].y * S;
-    o[j] = __builtin_amdgcn_perm(__float_as_uint(y), __float_as_uint(x), 0x07060302u);
-  }
-  return __builtin_bit_cast(v8bf, v4u{o[0], o[1], o[2], o[3]});
+  for (int j = 0; j < 4; ++j) h[j] = h[j] * d.m2;   // v_pk_mul_f16, exact
+  return v8h{h[0].x, h[0].y, h[1].x, h[1].y, h[2].x, h[2].y, h[3].x, h[3].y};
 }
 
 // The 16 scale codes (one per 16-wide K slice; block 32 repeats each code twice) of one
@@ -131,8 +148,8 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
     }
     const int g_end = (int)((ngroups - st * SGR) < SGR ? (ngroups - st * SGR) : SGR);
     for (int g = 0; g < g_end; ++g) {
-      // decoded bf16 fragments of the group's four 16-wide slices
-      v8bf fa[4][2], fb[4][2];
+      // decoded fp16 fragments (times 2^-3) of the group's four 16-wide slices
+      v8h fa[4][2], fb[4][2];
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) {
         const int off = g * 32 + sub * 8 + half * 4;   // payload byte inside the stage row
@@ -142,8 +159,8 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
           const int rowb = wn * 64 + t * 32 + (l & 31);
           const uint32_t ca = *reinterpret_cast<const uint32_t*>(lA[buf] + swz(rowa, off >> 4) + (off & 15));
           const uint32_t cb = *reinterpret_cast<const uint32_t*>(lB[buf] + swz(rowb, off >> 4) + (off & 15));
-          fa[sub][t] = decode8(ca, dec_scale3<FMT>(byte_of(scA[t], g * 4 + sub)));
-          fb[sub][t] = decode8(cb, dec_scale3<FMT>(byte_of(scB[t], g * 4 + sub)));
+          fa[sub][t] = decode8(ca, dec_factors(dec_scale3<FMT>(byte_of(scA[t], g * 4 + sub))));
+          fb[sub][t] = decode8(cb, dec_factors(dec_scale3<FMT>(byte_of(scB[t], g * 4 + sub))));
         }
       }
 #pragma unroll
@@ -155,7 +172,7 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
           v16f T[4];
 #pragma unroll
           for (int sub = 0; sub < 4; ++sub)
-            T[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sub][i], fb[sub][j], v16f{}, 0, 0, 0);
+            T[sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[sub][i], fb[sub][j], v16f{}, 0, 0, 0);
 #pragma unroll
           for (int sub = 0; sub < 4; ++sub) pin(T[sub]);
           v16f G;
@@ -184,7 +201,7 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
       __syncthreads();
     }
   }
-  store_tiles<2, 2>(c, M, N, m0 + wm * 64, n0 + wn * 64, acc, ga, gb, canon, hadamard_n);
+  store_tiles<2, 2>(c, M, N, m0 + wm * 64, n0 + wn * 64, acc, ga, gb, canon, hadamard_n, 64.0f);   // undo 2^-3 x 2^-3
 }
 
 template <int FMT, int B>
