@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--fmt", default="mxfp4", choices=["mxfp4", "ue5m3", "e4m3"])
     p.add_argument("--hadamard", type=int, default=0, choices=[0, 16, 32])
+    p.add_argument("--separate", action="store_true",
+                   help="quantize the ROW and COL views of X and dY with two calls instead of the fused one")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=384, help="output rows of the oracle GEMM sample")
     p.add_argument("--calib-copy-mib", type=int, default=0, help="one plain device copy of this size first")
@@ -87,8 +89,9 @@ def traffic_from_profile(fmt_name):
 class LinearStep:
     """Buffers and per-operand amax caches of one FP4 linear layer (fprop + dgrad + wgrad)."""
 
-    def __init__(self, fp4, torch, X, W, dY, fmt_name, hadamard):
+    def __init__(self, fp4, torch, X, W, dY, fmt_name, hadamard, fused=True):
         self.fp4, self.torch = fp4, torch
+        self.fused = fused
         self.X, self.W, self.dY = X, W, dY
         self.hn = hadamard
         self.fmt = {"mxfp4": fp4.E8M0, "ue5m3": fp4.UE5M3, "e4m3": fp4.E4M3}[fmt_name]
@@ -126,13 +129,19 @@ class LinearStep:
         fp4, torch = self.fp4, self.torch
         E8 = self.fmt == fp4.E8M0
         B = self.block
-        # forward
+        # forward: X is quantized once for fprop (ROW) and, in the same pass when fused, for
+        # wgrad (COL, saved for the backward)
         self._sample(self.c_x, self.X, step)
+        self._sample(self.c_xh, self.X, step, self.hn)
         self._sample(self.c_w, self.W, step)
         if timed:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-        qx = fp4.quantize(self.X, self.fmt, B, fp4.ROW, amax=self.c_x.amax, T=448)
+        if self.fused:
+            qx, qxt = fp4.quantize_rowcol(self.X, self.fmt, B, amax_row=self.c_x.amax, amax_col=self.c_xh.amax,
+                                          T_row=448, T_col=448, hadamard_n=self.hn)
+        else:
+            qx = fp4.quantize(self.X, self.fmt, B, fp4.ROW, amax=self.c_x.amax, T=448)
         if timed:
             e1.record()
             self.evq.append((e0, e1))
@@ -142,17 +151,23 @@ class LinearStep:
         else:
             qw, qwt = fp4.quantize(self.W, self.fmt, 16, fp4.TILE2D, amax=self.c_w.amax, T=448)
         self._timed(timed, fp4.gemm_fprop, qx, qw, out=self.Y)
-        # backward: dgrad
+        # backward: dY for dgrad (ROW, T = 448) and wgrad (COL, T = 2048, optional Hadamard),
+        # both with stochastic rounding
         self._sample(self.c_dy, self.dY, step)
-        qdy = fp4.quantize(self.dY, self.fmt, B, fp4.ROW, amax=self.c_dy.amax, T=448, stochastic=True, seed=42,
-                           offset=step * 8 + 0)
-        self._timed(timed, fp4.gemm_dgrad, qdy, qwt, out=self.dX)
-        # backward: wgrad (dY^T with T = 2048, X^T with T = 448, optional Hadamard)
         self._sample(self.c_dyh, self.dY, step, self.hn)
-        self._sample(self.c_xh, self.X, step, self.hn)
-        qdyt = fp4.quantize(self.dY, self.fmt, B, fp4.COL, amax=self.c_dyh.amax, T=2048, stochastic=True, seed=42,
-                            offset=step * 8 + 1, hadamard_n=self.hn)
-        qxt = fp4.quantize(self.X, self.fmt, B, fp4.COL, amax=self.c_xh.amax, T=448, hadamard_n=self.hn)
+        if self.fused:
+            qdy, qdyt = fp4.quantize_rowcol(self.dY, self.fmt, B, amax_row=self.c_dy.amax, amax_col=self.c_dyh.amax,
+                                            T_row=448, T_col=2048, stochastic_row=True, stochastic_col=True,
+                                            seed_row=42, offset_row=step * 8 + 0, seed_col=42,
+                                            offset_col=step * 8 + 1, hadamard_n=self.hn)
+        else:
+            qdy = fp4.quantize(self.dY, self.fmt, B, fp4.ROW, amax=self.c_dy.amax, T=448, stochastic=True, seed=42,
+                               offset=step * 8 + 0)
+            qdyt = fp4.quantize(self.dY, self.fmt, B, fp4.COL, amax=self.c_dyh.amax, T=2048, stochastic=True,
+                                seed=42, offset=step * 8 + 1, hadamard_n=self.hn)
+        self._timed(timed, fp4.gemm_dgrad, qdy, qwt, out=self.dX)
+        if not self.fused:
+            qxt = fp4.quantize(self.X, self.fmt, B, fp4.COL, amax=self.c_xh.amax, T=448, hadamard_n=self.hn)
         self._timed(timed, fp4.gemm_wgrad, qdyt, qxt, hadamard_n=self.hn, out=self.dW)
 
 
@@ -252,7 +267,7 @@ def main():
     Wd = bf16_device(torch, synth, synth.normal((N_OUT, K_IN), 0.02, 303))
     dYd = bf16_device(torch, synth, synth.normal((M_TOK, N_OUT), 1e-3, 304))
     del X
-    step_obj = LinearStep(fp4, torch, Xd, Wd, dYd, args.fmt, args.hadamard)
+    step_obj = LinearStep(fp4, torch, Xd, Wd, dYd, args.fmt, args.hadamard, fused=not args.separate)
     if args.calib_copy_mib > 0:
         # known-size reference for the HBM byte counters: one plain copy of N MiB
         src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
@@ -283,8 +298,17 @@ def main():
     torch.cuda.synchronize()
     same = lambda o: bool(torch.equal(o.q, ref_q.q) and torch.equal(o.s, ref_q.s))
     quant_ms, quant_ok = graph_time_ms(torch, qfn, same)
-    if not quant_ok:
+    if not quant_ok and args.separate:
         quant_ms = quant_ms_step
+    # the fused ROW + COL activation quantizer (X for fprop and X^T for wgrad from one read)
+    cargs = dict(amax_row=step_obj.c_x.amax, amax_col=step_obj.c_xh.amax) if step_obj.fmt != fp4.E8M0 else {}
+    rcfn = lambda: fp4.quantize_rowcol(Xd, step_obj.fmt, step_obj.block, hadamard_n=args.hadamard, **cargs)
+    ref_rc = rcfn()
+    torch.cuda.synchronize()
+    same_rc = lambda o: all(bool(torch.equal(a.q, b.q) and torch.equal(a.s, b.s)) for a, b in zip(o, ref_rc))
+    rc_ms, rc_ok = graph_time_ms(torch, rcfn, same_rc)
+    rc_bpe = 2 + 2 * (0.5 + 1.0 / step_obj.block)
+    rc_gbs = M_TOK * K_IN * rc_bpe / (rc_ms * 1e-3) / 1e9
     flop_gemm = 2.0 * M_TOK * N_OUT * K_IN
     step_flops = 3 * flop_gemm
     value = step_flops / (ms_step * 1e-3) / 1e12
@@ -316,8 +340,14 @@ def main():
         "quantizer": {"kernel": "k_quant_row (activation 8192x4096 bf16)", "achieved": round(q_gbs, 1),
                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(q_gbs / HBM_PEAK_GBS, 4),
                       "bytes_per_elem": bpe, "avg_ms": round(quant_ms, 4),
-                      "timing": "graph replay of 20 calls" if quant_ok else "events in the step",
-                      "in_step_avg_ms": round(quant_ms_step, 4)},
+                      "timing": "graph replay of 20 calls" if quant_ok else
+                                ("events in the step" if args.separate else "graph replay check failed"),
+                      "in_step_avg_ms": round(quant_ms_step, 4) if args.separate else None},
+        "quantizer_rowcol": {"kernel": f"k_quant_rowcol (activation 8192x4096 bf16, COL view H{args.hadamard})",
+                             "achieved": round(rc_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(rc_gbs / HBM_PEAK_GBS, 4), "bytes_per_elem": rc_bpe,
+                             "avg_ms": round(rc_ms, 4), "replay_matches_eager": rc_ok,
+                             "in_step_avg_ms": None if args.separate else round(quant_ms_step, 4)},
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:

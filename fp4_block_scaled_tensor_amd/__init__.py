@@ -19,7 +19,8 @@ from ._lib import (FP4_UE5M3, FP4_E4M3, FP4_E8M0, FP4_VIEW_ROW, FP4_VIEW_COL, FP
 UE5M3, E4M3, E8M0 = FP4_UE5M3, FP4_E4M3, FP4_E8M0
 ROW, COL, TILE2D = FP4_VIEW_ROW, FP4_VIEW_COL, FP4_VIEW_TILE2D
 
-__all__ = ["UE5M3", "E4M3", "E8M0", "ROW", "COL", "TILE2D", "QTensor", "AmaxCache", "quantize", "tensor_amax",
+__all__ = ["UE5M3", "E4M3", "E8M0", "ROW", "COL", "TILE2D", "QTensor", "AmaxCache", "quantize", "quantize_rowcol",
+           "tensor_amax",
            "gemm_fprop", "gemm_dgrad", "gemm_wgrad", "debug_encode", "FP4Error", "library"]
 
 
@@ -105,6 +106,47 @@ def quantize(x: torch.Tensor, fmt: int = UE5M3, block: int = 16, view: int = ROW
         return QTensor(q, s, g, fmt, block, FP4_SCALES_1D, cols, rows)
     return (QTensor(q, s, g, fmt, 16, FP4_SCALES_2D, rows, cols),
             QTensor(qt, s, g, fmt, 16, FP4_SCALES_2D_T, cols, rows))
+
+
+def _in_dtype(x: torch.Tensor) -> int:
+    if x.dtype == torch.bfloat16:
+        return _lib.FP4_IN_BF16
+    if x.dtype == torch.float32:
+        return _lib.FP4_IN_FP32
+    raise ValueError("x must be bfloat16 or float32")
+
+
+def quantize_rowcol(x: torch.Tensor, fmt: int = UE5M3, block: int = 16, amax_row: torch.Tensor | None = None,
+                    amax_col: torch.Tensor | None = None, T_row: float = 448.0, T_col: float = 448.0,
+                    stochastic_row: bool = False, stochastic_col: bool = False, seed_row: int = 0,
+                    offset_row: int = 0, seed_col: int = 0, offset_col: int = 0, hadamard_n: int = 0,
+                    amax_obs_row: torch.Tensor | None = None, amax_obs_col: torch.Tensor | None = None):
+    """fp4_quantize_rowcol: (ROW operand [rows x cols], COL operand x^T [cols x rows]) from one pass
+    over x; each equals the matching fp4_quantize call. hadamard_n rotates the COL view only."""
+    lib = _lib.load()
+    _dev_check(x, amax_row, amax_col, amax_obs_row, amax_obs_col)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    dt = _in_dtype(x)
+    rows, cols = x.shape
+    cr = _cfg(fmt, block, ROW, stochastic_row, 0, T_row, seed_row, offset_row)
+    cc = _cfg(fmt, block, COL, stochastic_col, hadamard_n, T_col, seed_col, offset_col)
+    for cfg in (cr, cc):
+        qb, sb, qtb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+        _lib.check(lib.fp4_quantize_sizes(rows, cols, ctypes.byref(cfg), ctypes.byref(qb), ctypes.byref(sb),
+                                          ctypes.byref(qtb)))
+    dev = x.device
+    q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    s = torch.empty((rows, cols // block), dtype=torch.uint8, device=dev)
+    qt = torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev)
+    st = torch.empty((cols, rows // block), dtype=torch.uint8, device=dev)
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    gt = torch.empty(1, dtype=torch.float32, device=dev)
+    _lib.check(lib.fp4_quantize_rowcol(_ptr(x), dt, rows, cols, x.stride(0), ctypes.byref(cr), ctypes.byref(cc),
+                                       _ptr(amax_row), _ptr(amax_col), _ptr(q), _ptr(s), _ptr(g), _ptr(amax_obs_row),
+                                       _ptr(qt), _ptr(st), _ptr(gt), _ptr(amax_obs_col), _stream()))
+    return (QTensor(q, s, g, fmt, block, FP4_SCALES_1D, rows, cols),
+            QTensor(qt, st, gt, fmt, block, FP4_SCALES_1D, cols, rows))
 
 
 def tensor_amax(x: torch.Tensor, hadamard_n: int = 0, out: torch.Tensor | None = None) -> torch.Tensor:

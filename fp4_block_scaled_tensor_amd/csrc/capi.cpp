@@ -200,6 +200,67 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t co
   return hip_status(fp4k::run_quantize(a), "fp4_quantize");
 }
 
+fp4_status fp4_quantize_rowcol(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld,
+                               const fp4_quant_cfg* cfg_row, const fp4_quant_cfg* cfg_col, const float* d_amax_row,
+                               const float* d_amax_col, uint8_t* q, uint8_t* s, float* d_g, float* d_amax_obs_row,
+                               uint8_t* q_t, uint8_t* s_t, float* d_g_t, float* d_amax_obs_col, void* stream) {
+  fp4_status st;
+  if ((st = check_cfg(cfg_row)) != FP4_OK) return st;
+  if ((st = check_cfg(cfg_col)) != FP4_OK) return st;
+  if (cfg_row->view != FP4_VIEW_ROW || cfg_col->view != FP4_VIEW_COL)
+    return fail(FP4_EINVAL, "rowcol: cfg_row must be a ROW view and cfg_col a COL view");
+  if (cfg_row->fmt != cfg_col->fmt || cfg_row->block != cfg_col->block)
+    return fail(FP4_EUNSUPPORTED, "rowcol: both views must use the same format and block");
+  if ((st = check_shape(rows, cols, cfg_row)) != FP4_OK) return st;
+  if ((st = check_shape(rows, cols, cfg_col)) != FP4_OK) return st;
+  if (x_dtype != FP4_IN_BF16 && x_dtype != FP4_IN_FP32) return fail(FP4_EINVAL, "unknown input dtype %d", x_dtype);
+  const int64_t esz = x_dtype == FP4_IN_FP32 ? 4 : 2;
+  if (ld < cols) return fail(FP4_EINVAL, "ld (%lld) < cols (%lld)", (long long)ld, (long long)cols);
+  if (rows > 0 && cols > 0) {
+    if (!x || !q || !s || !q_t || !s_t) return fail(FP4_EINVAL, "NULL x, q, s, q_t or s_t");
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(q_t, 16))
+      return fail(FP4_EALIGN, "x, q and q_t must be 16-byte aligned");
+    if ((ld * esz) % 16) return fail(FP4_EALIGN, "row stride must be a multiple of 16 bytes");
+  }
+  // 32-bit lane offsets inside a 128 x 64 tile
+  if (ld * esz > (int64_t(1) << 24) || rows > (int64_t(1) << 25) || cols > (int64_t(1) << 25))
+    return fail(FP4_EUNSUPPORTED, "rowcol: needs ld*elem_size <= 2^24 bytes and rows, cols <= 2^25");
+  if (cfg_row->fmt != FP4_E8M0 && (!d_amax_row || !d_amax_col))
+    return fail(FP4_EINVAL, "UE5M3/E4M3 need the cached amax of both views");
+  for (const float* p : {(const float*)d_amax_row, (const float*)d_amax_col, (const float*)d_g, (const float*)d_g_t,
+                         (const float*)d_amax_obs_row, (const float*)d_amax_obs_col})
+    if (p && !aligned(p, 4)) return fail(FP4_EALIGN, "amax / g pointers must be 4-byte aligned");
+  fp4k::RowColArgs a;
+  a.x = x;
+  a.f32 = x_dtype == FP4_IN_FP32;
+  a.rows = rows;
+  a.cols = cols;
+  a.ld = ld;
+  a.fmt = cfg_row->fmt;
+  a.block = cfg_row->block;
+  a.hadamard_n = cfg_col->hadamard_n;
+  a.sr_r = cfg_row->stochastic != 0;
+  a.sr_c = cfg_col->stochastic != 0;
+  a.amax_r = d_amax_row;
+  a.amax_c = d_amax_col;
+  a.T_r = cfg_row->T;
+  a.T_c = cfg_col->T;
+  a.seed_r = cfg_row->seed;
+  a.offset_r = cfg_row->offset;
+  a.seed_c = cfg_col->seed;
+  a.offset_c = cfg_col->offset;
+  a.q = q;
+  a.s = s;
+  a.qt = q_t;
+  a.st = s_t;
+  a.g_r = d_g;
+  a.g_c = d_g_t;
+  a.obs_r = d_amax_obs_row;
+  a.obs_c = d_amax_obs_col;
+  a.stream = (hipStream_t)stream;
+  return hip_status(fp4k::run_quantize_rowcol(a), "fp4_quantize_rowcol");
+}
+
 fp4_status fp4_tensor_amax(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld, int32_t hadamard_n,
                            float* d_amax_out, void* stream) {
   if (x_dtype != FP4_IN_BF16 && x_dtype != FP4_IN_FP32) return fail(FP4_EINVAL, "unknown input dtype %d", x_dtype);

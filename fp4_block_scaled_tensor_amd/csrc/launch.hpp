@@ -40,6 +40,26 @@ struct GemmArgs {
 };
 
 hipError_t run_quantize(const QuantArgs& a);
+
+// ROW and COL views of one tensor in one pass (same format and block; per-view amax, T,
+// stochastic flag and counter offset; Hadamard on the COL view only).
+struct RowColArgs {
+  const void* x;
+  bool f32;
+  int64_t rows, cols, ld;
+  int fmt, block;
+  int hadamard_n;
+  bool sr_r, sr_c;
+  const float* amax_r;
+  const float* amax_c;
+  float T_r, T_c;
+  uint64_t seed_r, offset_r, seed_c, offset_c;
+  uint8_t *q, *s, *qt, *st;
+  float *g_r, *g_c;
+  float *obs_r, *obs_c;   // observed amax outputs (max-accumulated; cleared by the caller side)
+  hipStream_t stream;
+};
+hipError_t run_quantize_rowcol(const RowColArgs& a);
 hipError_t run_amax(const void* x, bool f32, int64_t rows, int64_t cols, int64_t ld, int hadamard_n, float* out,
                     hipStream_t stream);
 hipError_t run_cache_update(float* amax, int32_t* valid, int32_t D, int64_t step, const float* obs, hipStream_t stream);

@@ -25,6 +25,9 @@
 //                 unsigned integers).
 // The quantize kernels also write the operand's g (workgroup 0, thread 0) and, if asked,
 // fold their block maxima into the observed amax (one atomic per workgroup).
+#include <atomic>
+#include <type_traits>
+
 #include "fp4_device.hpp"
 #include "launch.hpp"
 
@@ -211,23 +214,16 @@ __device__ __forceinline__ void stage_tile(const void* __restrict__ x, int64_t r
   }
 }
 
-template <int FMT, int B, bool SR, bool F32, int HN>
-__global__ __launch_bounds__(NT) void k_quant_col(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
-                                                  const float* __restrict__ d_amax, float T, uint64_t seed,
-                                                  uint64_t offset, uint8_t* __restrict__ q, uint8_t* __restrict__ s,
-                                                  float* __restrict__ d_amax_obs, float* __restrict__ d_g) {
+// COL-view quantization of one staged CT x CF tile (tokens x features): each thread owns a
+// U-token run of one feature, the payload goes through the LDS output tile and is stored
+// row-contiguously (feature rows of q). Returns the thread's largest block amax.
+template <int FMT, int B, bool SR, int HN>
+__device__ __forceinline__ float col_tile(float (*tile)[CF + 1], uint32_t (*qout)[CT / 8 + 1], uint8_t (*sout)[CT / B],
+                                          int64_t rows, int64_t cols, int64_t t0, int64_t f0, const TensorScales& ts,
+                                          uint64_t seed, uint64_t offset, uint8_t* __restrict__ q,
+                                          uint8_t* __restrict__ s) {
   constexpr int U = (HN > B) ? HN : B;          // tokens per thread unit
   constexpr int UNITS = CT / U;                 // units per feature in a tile
-  __shared__ float tile[CT][CF + 1];
-  __shared__ uint32_t qout[CF][CT / 8 + 1];     // 8 codes per dword
-  __shared__ uint8_t sout[CF][CT / B];
-  const int64_t t0 = (int64_t)blockIdx.x * CT;
-  const int64_t f0 = (int64_t)blockIdx.y * CF;
-  stage_tile<F32>(x, rows, cols, ld, t0, f0, tile);
-  __syncthreads();
-  TensorScales ts{1.0f, 1.0f, 1.0f};
-  if constexpr (FMT != FMT_E8M0) ts = tensor_scales(d_amax, T);
-  write_g<FMT>(d_g, ts);
   const int f = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   float obs = 0.0f;
@@ -272,7 +268,267 @@ __global__ __launch_bounds__(NT) void k_quant_col(const void* __restrict__ x, in
     const int ff = c / (CT / B), j = c % (CT / B);
     if (f0 + ff < cols && t0 + (int64_t)j * B < rows) s[(f0 + ff) * srow + t0 / B + j] = sout[ff][j];
   }
+  return obs;
+}
+
+template <int FMT, int B, bool SR, bool F32, int HN>
+__global__ __launch_bounds__(NT) void k_quant_col(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+                                                  const float* __restrict__ d_amax, float T, uint64_t seed,
+                                                  uint64_t offset, uint8_t* __restrict__ q, uint8_t* __restrict__ s,
+                                                  float* __restrict__ d_amax_obs, float* __restrict__ d_g) {
+  __shared__ float tile[CT][CF + 1];
+  __shared__ uint32_t qout[CF][CT / 8 + 1];     // 8 codes per dword
+  __shared__ uint8_t sout[CF][CT / B];
+  const int64_t t0 = (int64_t)blockIdx.x * CT;
+  const int64_t f0 = (int64_t)blockIdx.y * CF;
+  stage_tile<F32>(x, rows, cols, ld, t0, f0, tile);
+  __syncthreads();
+  TensorScales ts{1.0f, 1.0f, 1.0f};
+  if constexpr (FMT != FMT_E8M0) ts = tensor_scales(d_amax, T);
+  write_g<FMT>(d_g, ts);
+  const float obs = col_tile<FMT, B, SR, HN>(tile, qout, sout, rows, cols, t0, f0, ts, seed, offset, q, s);
   if (d_amax_obs) wg_max_to(d_amax_obs, obs);
+}
+
+// ---------------------------------------------------------------- ROW + COL views in one pass
+// "Format-Aware Fusion for Fast FP4 Pretraining", abstract: the producer emits its consumers'
+// layouts. One read of x gives the forward operand (ROW view) and the saved-for-backward
+// operand (COL view, optionally Hadamard-rotated), each with its own cached amax, T and
+// rounding.
+//
+// A workgroup owns a 128-token x 64-feature tile. Lane l of a pass loads the 8 elements
+// [8(l%8), 8(l%8)+8) of token row l/8 (eight lanes read one 128-byte line), so the ROW
+// blocks are finished in registers: a block spans B/8 neighbouring lanes, whose maxima
+// are combined with DPP quad permutes. The tile is then written to LDS in the input's own
+// type (bf16 or float; 16 or 32 KB) for the COL view, whose payload is transposed through
+// a small LDS tile as in the COL kernel. Workgroups are ordered so that each XCD walks
+// the feature tiles of a token stripe in turn: the partial 128-byte lines each tile writes
+// are completed in that XCD's L2 before they are written back.
+constexpr int RT = 128;   // tokens per fused tile
+constexpr int RF = 64;    // features per fused tile
+
+// max over groups of G neighbouring lanes (G = 1, 2 or 4; groups aligned to G)
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (G >= 2)
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));  // lane ^ 1
+  if constexpr (G >= 4)
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));  // lane ^ 2
+  static_assert(G == 1 || G == 2 || G == 4, "ROW blocks span 1, 2 or 4 lanes");
+  return v;
+}
+
+// Raw buffer access: a per-tile resource (base, 0x7FFFFFF0 bytes) and 32-bit lane offsets.
+// A lane whose element lies outside the matrix uses offset OOB instead: the hardware's range
+// check then returns zeros for its load and drops its store, so every memory instruction is
+// issued by every wave (no branches around them, exact wait counts).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+constexpr uint32_t OOB = 0x80000000u;
+constexpr int RSRC_RANGE = 0x7FFFFFF0;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, RSRC_RANGE, 0x00020000);
+}
+
+// 8 consecutive input elements as loaded (one or two 16-byte words) and as floats
+template <bool F32>
+struct Chunk8 {
+  uint4 w[F32 ? 2 : 1];
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) {
+#pragma unroll
+    for (int h = 0; h < (F32 ? 2 : 1); ++h) {
+      const v4u t = __builtin_amdgcn_raw_buffer_load_b128(r, off == OOB ? OOB : off + 16u * h, 0, 0);
+      w[h] = make_uint4(t[0], t[1], t[2], t[3]);
+    }
+  }
+  __device__ __forceinline__ void to_float(float* v) const {
+    if constexpr (F32) {
+      v[0] = __uint_as_float(w[0].x); v[1] = __uint_as_float(w[0].y);
+      v[2] = __uint_as_float(w[0].z); v[3] = __uint_as_float(w[0].w);
+      v[4] = __uint_as_float(w[1].x); v[5] = __uint_as_float(w[1].y);
+      v[6] = __uint_as_float(w[1].z); v[7] = __uint_as_float(w[1].w);
+    } else {
+      v[0] = bf16_lo(w[0].x); v[1] = bf16_hi(w[0].x); v[2] = bf16_lo(w[0].y); v[3] = bf16_hi(w[0].y);
+      v[4] = bf16_lo(w[0].z); v[5] = bf16_hi(w[0].z); v[6] = bf16_lo(w[0].w); v[7] = bf16_hi(w[0].w);
+    }
+  }
+};
+
+// Persistent: gridDim.x workgroups walk the tiles. When the tile count and the grid are
+// multiples of 8, workgroup w (on XCD w % 8) takes tiles k*P + w/8 + i*(gridDim.x/8) of
+// the contiguous run [k*P, (k+1)*P) of XCD k = w % 8 (P = tiles / 8). The next tile's
+// loads are issued before the current tile is processed. Lane offsets are 32-bit: the host
+// bounds ld, rows and cols so that no offset inside a tile reaches 2^31.
+template <int FMT, int B, bool SRR, bool SRC, bool F32, int HN>
+__global__ __launch_bounds__(NT) void k_quant_rowcol(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                     int64_t ld, const float* __restrict__ amax_r, float T_r,
+                                                     uint64_t seed_r, uint64_t offset_r,
+                                                     const float* __restrict__ amax_c, float T_c, uint64_t seed_c,
+                                                     uint64_t offset_c, uint8_t* __restrict__ q,
+                                                     uint8_t* __restrict__ s, float* __restrict__ g_r,
+                                                     float* __restrict__ obs_r, uint8_t* __restrict__ qt,
+                                                     uint8_t* __restrict__ st, float* __restrict__ g_c,
+                                                     float* __restrict__ obs_c) {
+  constexpr int U = (HN > B) ? HN : B;          // COL tokens per thread unit
+  constexpr int UNITS = RT / U;
+  constexpr int RPP = NT / 8;                   // token rows per load pass
+  constexpr int PASSES = RT / RPP;
+  constexpr int LB = B / 8;                     // lanes per ROW block
+  constexpr int ESZ = F32 ? 4 : 2;
+  using Elem = typename std::conditional<F32, float, uint16_t>::type;
+  __shared__ __align__(16) Elem tile[RT][RF];
+  __shared__ uint32_t qout[RF][RT / 8 + 1];
+  __shared__ uint8_t sout[RF][RT / B];
+  const uint32_t nft = (uint32_t)((cols + RF - 1) / RF);
+  const uint32_t total = (uint32_t)((rows + RT - 1) / RT) * nft;
+  const uint32_t G = gridDim.x;
+  uint32_t id, stride, end;
+  if ((total & 7) == 0 && (G & 7) == 0) {
+    const uint32_t per = total >> 3, k = blockIdx.x & 7;
+    id = k * per + (blockIdx.x >> 3);
+    stride = G >> 3;
+    end = (k + 1) * per;
+  } else {
+    id = blockIdx.x;
+    stride = G;
+    end = total;
+  }
+
+  TensorScales tr{1.0f, 1.0f, 1.0f}, tc{1.0f, 1.0f, 1.0f};
+  if constexpr (FMT != FMT_E8M0) {
+    tr = tensor_scales(amax_r, T_r);
+    tc = tensor_scales(amax_c, T_c);
+  }
+  write_g<FMT>(g_r, tr);
+  write_g<FMT>(g_c, tc);
+
+  const int lc = threadIdx.x & 7, lr = threadIdx.x >> 3;
+  const int f = threadIdx.x & 63;
+  const uint32_t ld_b = (uint32_t)(ld * ESZ);
+  const uint32_t qcols = (uint32_t)(cols / 2), scols = (uint32_t)(cols / B);
+  const uint32_t qrows = (uint32_t)(rows / 2), srows = (uint32_t)(rows / B);
+
+  // loads of tile `tid` (all lanes OOB when tid is past the end: no traffic)
+  auto load_tile = [&](uint32_t tid, Chunk8<F32> (&c)[PASSES]) {
+    const bool any = tid < end;
+    const uint32_t tt = any ? tid / nft : 0, ft = any ? tid - tt * nft : 0;
+    const int64_t t0 = (int64_t)tt * RT, f0 = (int64_t)ft * RF;
+    const rsrc_t rx = make_rsrc(reinterpret_cast<const char*>(x) + (t0 * ld + f0) * ESZ);
+    const int rl = (int)min(rows - t0, (int64_t)RT), cl = (int)min(cols - f0, (int64_t)RF);   // valid rows, cols
+    const bool cok = any && lc * 8 < cl;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int r = p * RPP + lr;
+      c[p].load(rx, (cok && r < rl) ? (uint32_t)r * ld_b + (uint32_t)(lc * 8 * ESZ) : OOB);
+    }
+  };
+  float orow = 0.0f, ocol = 0.0f;
+  Chunk8<F32> cur[PASSES];
+  load_tile(id, cur);
+  // wait for the first tile here: inside the loop the current tile always comes from the
+  // previous iteration's prefetch, whose wait counts are exact
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+    for (int h = 0; h < (F32 ? 2 : 1); ++h)
+      asm volatile("" ::"v"(cur[p].w[h].x), "v"(cur[p].w[h].y), "v"(cur[p].w[h].z), "v"(cur[p].w[h].w));
+  for (; id < end; id += stride) {
+    Chunk8<F32> nxt[PASSES];
+    load_tile(id + stride, nxt);
+    const uint32_t tt = id / nft, ft = id - tt * nft;
+    const int64_t t0 = (int64_t)tt * RT, f0 = (int64_t)ft * RF;
+    const int rl = (int)min(rows - t0, (int64_t)RT), cl = (int)min(cols - f0, (int64_t)RF);
+    const bool cok = lc * 8 < cl;
+
+    // ROW view
+    const rsrc_t rq = make_rsrc(q + t0 * qcols + f0 / 2);
+    const rsrc_t rs = make_rsrc(s + t0 * scols + f0 / B);
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int r = p * RPP + lr;
+      const bool ok = cok && r < rl;
+      float v[8];
+      cur[p].to_float(v);
+      float am = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(v[j]));
+      am = group_max<LB>(am);
+      uint32_t code;
+      float mult;
+      block_scale<FMT>(am, tr, code, mult);
+      uint32_t w;
+      payload<8, SRR>(v, mult, SRR ? (uint64_t)((t0 + r) * cols + f0 + lc * 8) : 0, seed_r, offset_r, &w);
+      __builtin_amdgcn_raw_buffer_store_b32(w, rq, ok ? (uint32_t)r * qcols + (uint32_t)(lc * 4) : OOB, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code, rs,
+                                           (ok && (lc & (LB - 1)) == 0) ? (uint32_t)r * scols + (uint32_t)(lc / LB) : OOB,
+                                           0, 0);
+      if (ok) orow = fmaxf(orow, am);
+    }
+
+    // stage the tile in the input's own type for the COL view
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      uint4* dst = reinterpret_cast<uint4*>(&tile[p * RPP + lr][lc * 8]);
+#pragma unroll
+      for (int h = 0; h < (F32 ? 2 : 1); ++h) dst[h] = cur[p].w[h];
+    }
+    __syncthreads();
+
+    // COL view: thread -> (feature f, unit u) of U consecutive tokens
+    for (int u = threadIdx.x >> 6; u < UNITS; u += NT / 64) {
+      if (u * U >= rl) break;                   // rows % U == 0: units are whole
+      float c[U];
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        if constexpr (F32) c[i] = tile[u * U + i][f];
+        else c[i] = __uint_as_float((uint32_t)tile[u * U + i][f] << 16);
+      }
+      if constexpr (HN > 0) {
+#pragma unroll
+        for (int h0 = 0; h0 < U; h0 += HN) fwht_inplace<HN>(c + h0);
+      }
+#pragma unroll
+      for (int bb = 0; bb < U / B; ++bb) {
+        float amax_b = 0.0f;
+#pragma unroll
+        for (int i = 0; i < B; ++i) amax_b = fmaxf(amax_b, fabsf(c[bb * B + i]));
+        if (f < cl) ocol = fmaxf(ocol, amax_b);
+        uint32_t code;
+        float mult;
+        block_scale<FMT>(amax_b, tc, code, mult);
+        uint32_t words[B / 8];
+        const int tok = u * U + bb * B;
+        payload<B, SRC>(c + bb * B, mult, SRC ? (uint64_t)((f0 + f) * rows + t0 + tok) : 0, seed_c, offset_c, words);
+#pragma unroll
+        for (int j = 0; j < B / 8; ++j) qout[f][tok / 8 + j] = words[j];
+        sout[f][tok / B] = (uint8_t)code;
+      }
+    }
+    __syncthreads();   // also: every COL read of `tile` is done before the next tile is staged
+    const rsrc_t rqt = make_rsrc(qt + f0 * qrows + t0 / 2);
+    const rsrc_t rst = make_rsrc(st + f0 * srows + t0 / B);
+#pragma unroll
+    for (int k = 0; k < RF * (RT / 16) / NT; ++k) {
+      const int cc = threadIdx.x + k * NT;
+      const int ff = cc / (RT / 16), piece = cc % (RT / 16);
+      const bool ok = ff < cl && piece * 16 < rl;
+      const v2u w2 = {qout[ff][2 * piece], qout[ff][2 * piece + 1]};
+      __builtin_amdgcn_raw_buffer_store_b64(w2, rqt, ok ? (uint32_t)ff * qrows + (uint32_t)(piece * 8) : OOB, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < RF * (RT / B) / NT; ++k) {
+      const int cc = threadIdx.x + k * NT;
+      const int ff = cc / (RT / B), j = cc % (RT / B);
+      const bool ok = ff < cl && j * B < rl;
+      __builtin_amdgcn_raw_buffer_store_b8(sout[ff][j], rst, ok ? (uint32_t)ff * srows + (uint32_t)j : OOB, 0, 0);
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) cur[p] = nxt[p];
+  }
+  if (obs_r) wg_max_to(obs_r, orow);
+  if (obs_r && obs_c) __syncthreads();   // wg_max_to's partials array is reused
+  if (obs_c) wg_max_to(obs_c, ocol);
 }
 
 // ---------------------------------------------------------------- TILE2D (weights)
@@ -423,6 +679,79 @@ static hipError_t launch_col(const QuantArgs& a) {
   hipLaunchKernelGGL((k_quant_col<FMT, B, SR, F32, HN>), grid, dim3(NT), 0, a.stream, a.x, a.rows, a.cols, a.ld,
                      a.d_amax, a.T, a.seed, a.offset, a.q, a.s, a.d_amax_obs, a.d_g);
   return hipGetLastError();
+}
+
+// compute units of the current device (cached per device; 256 on MI355X)
+static int device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+template <int FMT, int B, bool SRR, bool SRC, bool F32, int HN>
+static hipError_t launch_rowcol(const RowColArgs& a) {
+  const int64_t tiles = ((a.rows + RT - 1) / RT) * ((a.cols + RF - 1) / RF);
+  // one resident wave of workgroups (rounded down to a multiple of 8 XCDs), or fewer
+  static const int per_cu = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_quant_rowcol<FMT, B, SRR, SRC, F32, HN>, NT, 0) !=
+            hipSuccess || n < 1)
+      n = 1;
+    return n;
+  }();
+  int64_t grid = (int64_t)per_cu * device_cu_count();
+  if (grid > tiles) grid = tiles;
+  if (grid >= 8) grid &= ~(int64_t)7;
+  hipLaunchKernelGGL((k_quant_rowcol<FMT, B, SRR, SRC, F32, HN>), dim3((unsigned)grid), dim3(NT), 0, a.stream, a.x, a.rows, a.cols,
+                     a.ld, a.amax_r, a.T_r, a.seed_r, a.offset_r, a.amax_c, a.T_c, a.seed_c, a.offset_c, a.q, a.s,
+                     a.g_r, a.obs_r, a.qt, a.st, a.g_c, a.obs_c);
+  return hipGetLastError();
+}
+
+template <int FMT, int B, bool SRR, bool SRC, bool F32>
+static hipError_t rowcol_h(const RowColArgs& a) {
+  if (a.hadamard_n == 16) return launch_rowcol<FMT, B, SRR, SRC, F32, 16>(a);
+  if (a.hadamard_n == 32) return launch_rowcol<FMT, B, SRR, SRC, F32, 32>(a);
+  return launch_rowcol<FMT, B, SRR, SRC, F32, 0>(a);
+}
+
+template <int FMT, int B, bool F32>
+static hipError_t rowcol_sr(const RowColArgs& a) {
+  if (a.sr_r) return a.sr_c ? rowcol_h<FMT, B, true, true, F32>(a) : rowcol_h<FMT, B, true, false, F32>(a);
+  return a.sr_c ? rowcol_h<FMT, B, false, true, F32>(a) : rowcol_h<FMT, B, false, false, F32>(a);
+}
+
+template <bool F32>
+static hipError_t rowcol_fmt(const RowColArgs& a) {
+  if (a.fmt == FMT_E8M0) return rowcol_sr<FMT_E8M0, 32, F32>(a);
+  if (a.fmt == FMT_UE5M3) return a.block == 16 ? rowcol_sr<FMT_UE5M3, 16, F32>(a) : rowcol_sr<FMT_UE5M3, 32, F32>(a);
+  return a.block == 16 ? rowcol_sr<FMT_E4M3, 16, F32>(a) : rowcol_sr<FMT_E4M3, 32, F32>(a);
+}
+
+hipError_t run_quantize_rowcol(const RowColArgs& a) {
+  hipError_t e = hipSuccess;
+  for (float* o : {a.obs_r, a.obs_c}) {
+    if (!o) continue;
+    hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, a.stream, o, 0.0f);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (a.rows == 0 || a.cols == 0) {
+    if (a.g_r) {
+      hipLaunchKernelGGL(k_write_g, dim3(1), dim3(1), 0, a.stream, a.amax_r, a.T_r, a.fmt, a.g_r);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (a.g_c) {
+      hipLaunchKernelGGL(k_write_g, dim3(1), dim3(1), 0, a.stream, a.amax_c, a.T_c, a.fmt, a.g_c);
+      e = hipGetLastError();
+    }
+    return e;
+  }
+  return a.f32 ? rowcol_fmt<true>(a) : rowcol_fmt<false>(a);
 }
 
 template <int FMT, bool F32>

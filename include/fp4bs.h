@@ -139,6 +139,31 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t co
                         uint8_t* q, uint8_t* s, uint8_t* q_t, float* d_g, float* d_amax_obs,
                         void* stream);
 
+/*
+ * fp4_quantize_rowcol - the ROW view and the COL view of one tensor from a single read of x
+ * [FUSION abstract: the producer writes the layouts its consumers read; HOPPER methodology:
+ * fused transposed quantization]. The outputs are byte-identical to two fp4_quantize calls,
+ * one with cfg_row (forward operand: q, s, d_g, d_amax_obs_row) and one with cfg_col
+ * (saved-for-backward operand x^T: q_t [cols x rows/2], s_t [cols x rows/B], d_g_t,
+ * d_amax_obs_col).
+ *   cfg_row  view FP4_VIEW_ROW, hadamard_n 0
+ *   cfg_col  view FP4_VIEW_COL; same fmt and block as cfg_row; its own T, stochastic flag,
+ *            seed/offset and hadamard_n (0, 16, 32)
+ *   d_amax_row, d_amax_col  device floats: each view's cached amax (UE5M3/E4M3; may be NULL
+ *            for E8M0). With a Hadamard rotation the COL view's amax is that of the rotated
+ *            tensor, so the two usually differ.
+ *   d_g, d_g_t, d_amax_obs_row, d_amax_obs_col  optional device float outputs, as in
+ *            fp4_quantize
+ * Requires the shape conditions of both views: cols % B == 0, rows % B == 0 and
+ * rows % hadamard_n == 0; also ld * elem_size <= 2^24 bytes and rows, cols <= 2^25
+ * (FP4_EUNSUPPORTED otherwise). Empty tensors are a no-op (g values are still written).
+ */
+fp4_status fp4_quantize_rowcol(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld,
+                               const fp4_quant_cfg* cfg_row, const fp4_quant_cfg* cfg_col,
+                               const float* d_amax_row, const float* d_amax_col,
+                               uint8_t* q, uint8_t* s, float* d_g, float* d_amax_obs_row,
+                               uint8_t* q_t, uint8_t* s_t, float* d_g_t, float* d_amax_obs_col, void* stream);
+
 /* fp4_quantize_sizes - byte sizes of q, s and q_t for a call with these arguments (host only). */
 fp4_status fp4_quantize_sizes(int64_t rows, int64_t cols, const fp4_quant_cfg* cfg,
                               size_t* q_bytes, size_t* s_bytes, size_t* qt_bytes);

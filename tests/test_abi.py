@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_and_binding_agree():
     decl = declared_functions()
     assert set(decl) == set(_lib.EXPORTED), decl
-    assert len(decl) == 11
+    assert len(decl) == 12
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -140,3 +140,29 @@ def test_binding_fails_loudly_without_gpu_tensors():
     with pytest.raises(ValueError, match="device tensors"):
         fp4.quantize(torch.zeros((16, 64), dtype=torch.bfloat16), fp4.UE5M3, 16, fp4.ROW,
                      amax=torch.ones(1))
+
+
+def rowcol(lib, cr, cc, rows=64, cols=64, ld=64, x=4096, q=4096, qt=4096, a_r=16, a_c=16):
+    P = ctypes.c_void_p(4096)
+    return lib.fp4_quantize_rowcol(ctypes.c_void_p(x), 0, rows, cols, ld, ctypes.byref(cr), ctypes.byref(cc),
+                                   ctypes.c_void_p(a_r), ctypes.c_void_p(a_c), ctypes.c_void_p(q), P, None, None,
+                                   ctypes.c_void_p(qt), P, None, None, None)
+
+
+def test_rowcol_rejects_bad_arguments(lib):
+    r, c = cfg(view=0), cfg(view=1, hn=16)
+    assert rowcol(lib, c, c) == _lib.FP4_EINVAL                       # first cfg must be ROW
+    assert rowcol(lib, r, r) == _lib.FP4_EINVAL                       # second cfg must be COL
+    assert rowcol(lib, r, cfg(view=1, block=32)) == _lib.FP4_EUNSUPPORTED   # same block
+    assert rowcol(lib, r, cfg(view=1, fmt=1)) == _lib.FP4_EUNSUPPORTED      # same format
+    assert rowcol(lib, cfg(view=0, hn=16), c) == _lib.FP4_EUNSUPPORTED      # Hadamard is COL-only
+    assert rowcol(lib, r, c, rows=40) == _lib.FP4_EINVAL                    # rows % B (COL)
+    assert rowcol(lib, r, c, cols=40, ld=40) == _lib.FP4_EINVAL             # cols % B (ROW)
+    assert rowcol(lib, r, cfg(view=1, hn=32), rows=48) == _lib.FP4_EINVAL   # rows % hadamard_n
+    assert rowcol(lib, r, c, qt=0) == _lib.FP4_EINVAL                       # q_t required
+    assert rowcol(lib, r, c, q=4100) == _lib.FP4_EALIGN
+    assert rowcol(lib, r, c, ld=68) == _lib.FP4_EALIGN
+    assert rowcol(lib, r, c, a_c=0) == _lib.FP4_EINVAL                      # UE5M3 needs both amax values
+    mr, mc = cfg(fmt=2, block=32, view=0, T=0.0), cfg(fmt=2, block=32, view=1, T=0.0)
+    assert rowcol(lib, mr, mc, rows=48) == _lib.FP4_EINVAL                  # 48 % 32
+    assert lib.fp4_last_error().decode()
