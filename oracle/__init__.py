@@ -23,16 +23,21 @@ Pins (tests/test_oracle_*.py) and their strength:
 - GEMM model: an exact-rational element-wise restatement (oracle.exact), RTZ addition
   against x86 SSE arithmetic under FE_TOWARDZERO, the K=64 B=32 textbook case, integer
   cases, and the float64 reference within the stated tolerance.
+- fake quantization: decode against exact rationals, E8M0 fake-quant values against a
+  brute-force nearest search over the block's scaled codebook, bfloat16 rounding against
+  torch's cast, policy order-dependence and D=1 == per-request amax.
 """
-from . import formats, philox, hadamard, quantize, gemm, exact
+from . import formats, philox, hadamard, quantize, gemm, exact, fakequant
 from .formats import UE5M3, E4M3, E8M0
 from .quantize import (AmaxCache, QuantResult, quantize_1d, quantize_2d, quantize_col, tensor_amax,
                        tensor_scales, pack_codes, unpack_codes, transposed_view)
 from .gemm import gemm_model, gemm_fp64, rtz_add_f32, operand_from_quant, output_scale, expand_2d_scales
+from .fakequant import dequantize, fake_quant, f32_to_bf16_bits, FakeQuantPolicy
 
 __all__ = [
-    "formats", "philox", "hadamard", "quantize", "gemm", "exact",
+    "formats", "philox", "hadamard", "quantize", "gemm", "exact", "fakequant",
     "UE5M3", "E4M3", "E8M0", "AmaxCache", "QuantResult", "quantize_1d", "quantize_2d", "quantize_col",
     "tensor_amax", "tensor_scales", "pack_codes", "unpack_codes", "transposed_view",
     "gemm_model", "gemm_fp64", "rtz_add_f32", "operand_from_quant", "output_scale", "expand_2d_scales",
+    "dequantize", "fake_quant", "f32_to_bf16_bits", "FakeQuantPolicy",
 ]
