@@ -20,7 +20,7 @@ UE5M3, E4M3, E8M0 = FP4_UE5M3, FP4_E4M3, FP4_E8M0
 ROW, COL, TILE2D = FP4_VIEW_ROW, FP4_VIEW_COL, FP4_VIEW_TILE2D
 
 __all__ = ["UE5M3", "E4M3", "E8M0", "ROW", "COL", "TILE2D", "QTensor", "AmaxCache", "quantize", "quantize_rowcol",
-           "tensor_amax",
+           "fake_quant", "dequantize", "FakeQuantPolicy", "tensor_amax",
            "gemm_fprop", "gemm_dgrad", "gemm_wgrad", "debug_encode", "FP4Error", "library"]
 
 
@@ -147,6 +147,73 @@ def quantize_rowcol(x: torch.Tensor, fmt: int = UE5M3, block: int = 16, amax_row
                                        _ptr(qt), _ptr(st), _ptr(gt), _ptr(amax_obs_col), _stream()))
     return (QTensor(q, s, g, fmt, block, FP4_SCALES_1D, rows, cols),
             QTensor(qt, st, gt, fmt, block, FP4_SCALES_1D, cols, rows))
+
+
+def _out_dtype(dtype) -> int:
+    if dtype == torch.bfloat16:
+        return _lib.FP4_IN_BF16
+    if dtype == torch.float32:
+        return _lib.FP4_IN_FP32
+    raise ValueError("output dtype must be bfloat16 or float32")
+
+
+def fake_quant(x: torch.Tensor, fmt: int = UE5M3, block: int = 16, amax: torch.Tensor | None = None,
+               T: float = 448.0, out_dtype=torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp4_fake_quant: the decoded value of x's ROW-view FP4 quantization, [rows, cols]."""
+    lib = _lib.load()
+    _dev_check(x, amax, out)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=out_dtype, device=x.device)
+    if out.dim() != 2 or out.shape != x.shape or out.stride(1) != 1:
+        raise ValueError("out must be [rows, cols] with unit column stride")
+    cfg = _cfg(fmt, block, ROW, False, 0, T, 0, 0)
+    _lib.check(lib.fp4_fake_quant(_ptr(x), _in_dtype(x), rows, cols, x.stride(0), ctypes.byref(cfg), _ptr(amax),
+                                  _ptr(out), _out_dtype(out.dtype), out.stride(0), _stream()))
+    return out
+
+
+def dequantize(a: QTensor, out_dtype=torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp4_dequantize: the decoded values [rows, k] of a quantized operand."""
+    lib = _lib.load()
+    if out is None:
+        out = torch.empty((a.rows, a.k), dtype=out_dtype, device=a.q.device)
+    _dev_check(out)
+    if out.dim() != 2 or tuple(out.shape) != (a.rows, a.k) or out.stride(1) != 1:
+        raise ValueError("out must be [rows, k] with unit column stride")
+    op = a.operand()
+    _lib.check(lib.fp4_dequantize(ctypes.byref(op), _ptr(out), _out_dtype(out.dtype), out.stride(0), _stream()))
+    return out
+
+
+class FakeQuantPolicy:
+    """Activation-scale policy of fake-quantized inference requests, taken in order: 'delayed'
+    (sample-and-hold cache, period D, 50 by default), 'current' (D = 1) or 'frozen' (a fixed
+    calibration amax). The sampling decision and the amax stay on the device."""
+
+    def __init__(self, kind: str, fmt: int = UE5M3, block: int = 16, T: float = 448.0, D: int | None = None,
+                 amax: float | None = None, device="cuda"):
+        if kind not in ("delayed", "current", "frozen"):
+            raise ValueError(kind)
+        self.kind, self.fmt, self.block, self.T = kind, fmt, block, T
+        if kind == "frozen":
+            if amax is None:
+                raise ValueError("a frozen policy needs its calibration amax")
+            self.cache = None
+            self.amax = torch.full((1,), float(amax), dtype=torch.float32, device=device)
+        else:
+            self.cache = AmaxCache(1 if kind == "current" else (50 if D is None else D), device=device)
+            self.amax = self.cache.amax
+            self._obs = torch.empty(1, dtype=torch.float32, device=device)
+
+    def __call__(self, request: int, x: torch.Tensor, out_dtype=torch.float32, out: torch.Tensor | None = None):
+        if self.cache is not None and self.fmt != E8M0 and self.cache.needs_sample(request):
+            tensor_amax(x, out=self._obs)
+            self.cache.update(request, self._obs)
+        return fake_quant(x, self.fmt, self.block, amax=None if self.fmt == E8M0 else self.amax, T=self.T,
+                          out_dtype=out_dtype, out=out)
 
 
 def tensor_amax(x: torch.Tensor, hadamard_n: int = 0, out: torch.Tensor | None = None) -> torch.Tensor:

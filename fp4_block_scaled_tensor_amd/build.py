@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfp4bs.so")
-SOURCES = ["capi.cpp", "quant.hip", "gemm_mx.hip", "gemm_dec16.hip"]
+SOURCES = ["capi.cpp", "quant.hip", "fakequant.hip", "gemm_mx.hip", "gemm_dec16.hip"]
 ARCH = "gfx950"
 
 
@@ -50,7 +50,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every source (always) and link libfp4bs.so; returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]

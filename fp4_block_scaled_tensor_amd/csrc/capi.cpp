@@ -261,6 +261,73 @@ fp4_status fp4_quantize_rowcol(const void* x, int32_t x_dtype, int64_t rows, int
   return hip_status(fp4k::run_quantize_rowcol(a), "fp4_quantize_rowcol");
 }
 
+fp4_status fp4_fake_quant(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld,
+                          const fp4_quant_cfg* cfg, const float* d_amax, void* y, int32_t y_dtype, int64_t ldy,
+                          void* stream) {
+  fp4_status st;
+  if ((st = check_cfg(cfg)) != FP4_OK) return st;
+  if (cfg->view != FP4_VIEW_ROW) return fail(FP4_EUNSUPPORTED, "fake_quant: ROW view only (blocks along cols)");
+  if (cfg->stochastic) return fail(FP4_EUNSUPPORTED, "fake_quant: nearest-even only");
+  if ((st = check_shape(rows, cols, cfg)) != FP4_OK) return st;
+  if (x_dtype != FP4_IN_BF16 && x_dtype != FP4_IN_FP32) return fail(FP4_EINVAL, "unknown input dtype %d", x_dtype);
+  if (y_dtype != FP4_IN_BF16 && y_dtype != FP4_IN_FP32) return fail(FP4_EINVAL, "unknown output dtype %d", y_dtype);
+  const int64_t esz = x_dtype == FP4_IN_FP32 ? 4 : 2, osz = y_dtype == FP4_IN_FP32 ? 4 : 2;
+  if (ld < cols || ldy < cols) return fail(FP4_EINVAL, "ld and ldy must be >= cols");
+  if (rows > 0 && cols > 0) {
+    if (!x || !y) return fail(FP4_EINVAL, "NULL x or y");
+    if (!aligned(x, 16) || !aligned(y, 16)) return fail(FP4_EALIGN, "x and y must be 16-byte aligned");
+    if ((ld * esz) % 16 || (ldy * osz) % 16) return fail(FP4_EALIGN, "row strides must be multiples of 16 bytes");
+    if (ld * esz > (int64_t(1) << 24) || ldy * osz > (int64_t(1) << 24))
+      return fail(FP4_EUNSUPPORTED, "fake_quant: row strides above 2^24 bytes");
+  }
+  if (cfg->fmt != FP4_E8M0 && !d_amax) return fail(FP4_EINVAL, "UE5M3/E4M3 need the cached amax d_amax");
+  if (d_amax && !aligned(d_amax, 4)) return fail(FP4_EALIGN, "d_amax must be 4-byte aligned");
+  fp4k::FakeQuantArgs a;
+  a.x = x;
+  a.f32 = x_dtype == FP4_IN_FP32;
+  a.rows = rows;
+  a.cols = cols;
+  a.ld = ld;
+  a.fmt = cfg->fmt;
+  a.block = cfg->block;
+  a.d_amax = d_amax;
+  a.T = cfg->T;
+  a.y = y;
+  a.bf16_out = y_dtype == FP4_IN_BF16;
+  a.ldy = ldy;
+  a.stream = (hipStream_t)stream;
+  return hip_status(fp4k::run_fake_quant(a), "fp4_fake_quant");
+}
+
+fp4_status fp4_dequantize(const fp4_operand* a, void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+  fp4_status st;
+  if ((st = check_operand(a, "operand")) != FP4_OK) return st;
+  if (y_dtype != FP4_IN_BF16 && y_dtype != FP4_IN_FP32) return fail(FP4_EINVAL, "unknown output dtype %d", y_dtype);
+  const int64_t osz = y_dtype == FP4_IN_FP32 ? 4 : 2;
+  if (ldy < a->k) return fail(FP4_EINVAL, "ldy must be >= k");
+  if (a->rows > 0 && a->k > 0) {
+    if (!y) return fail(FP4_EINVAL, "NULL y");
+    if (!aligned(y, 16)) return fail(FP4_EALIGN, "y must be 16-byte aligned");
+    if ((ldy * osz) % 16) return fail(FP4_EALIGN, "ldy * element size must be a multiple of 16 bytes");
+    if (ldy * osz > (int64_t(1) << 24) || a->k > (int64_t(1) << 25))
+      return fail(FP4_EUNSUPPORTED, "dequantize: row stride above 2^24 bytes or k above 2^25");
+  }
+  fp4k::DequantArgs d;
+  d.q = a->q;
+  d.s = a->s;
+  d.g = a->g;
+  d.fmt = a->fmt;
+  d.block = a->block;
+  d.layout = a->scale_layout;
+  d.rows = a->rows;
+  d.K = a->k;
+  d.y = y;
+  d.bf16_out = y_dtype == FP4_IN_BF16;
+  d.ldy = ldy;
+  d.stream = (hipStream_t)stream;
+  return hip_status(fp4k::run_dequantize(d), "fp4_dequantize");
+}
+
 fp4_status fp4_tensor_amax(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld, int32_t hadamard_n,
                            float* d_amax_out, void* stream) {
   if (x_dtype != FP4_IN_BF16 && x_dtype != FP4_IN_FP32) return fail(FP4_EINVAL, "unknown input dtype %d", x_dtype);

@@ -1,0 +1,213 @@
+// Inference fake quantization and operand decode for gfx950 (HBM-bound).
+//
+// "UE5M3 FP4 Block Scaling for Stable Language Model Pretraining", approach (접근 방법),
+// training and inference setup: held-out likelihoods are measured with FP4 fake
+// quantization, the activation scale following a delayed (D = 50), current (D = 1) or
+// frozen policy; the policies only decide which cached amax a call receives.
+//
+// Decoded value of an operand element: x_hat = E2M1(q) * S * g (g = 1 for E8M0). E2M1(q) comes
+// from v_cvt_scalef32_pk_f32_fp4 with scale 1.0 (exact); E2M1(q) * S is exact in float32
+// (at most 6 significant bits; an E8M0 scale is a power of two, 2^-127 included as a
+// subnormal); the product with g is one float32 multiply, nearest-even. A bfloat16 output is
+// rounded from that float32, nearest-even.
+//
+// Kernels:
+//   k_fake_quant  x -> x_hat in one pass (ROW view, nearest-even): a 128-row x 64-column tile
+//                 per workgroup, 8 lanes per 64-element row segment (one 128-byte bf16 line),
+//                 a block of B elements spans B/8 lanes whose maxima combine by DPP, codes are
+//                 made and decoded in registers.
+//   k_dequant     a quantized operand (1D, 2D or transposed-2D scales) -> x_hat, the same
+//                 tiling over its [rows x K] values.
+// Raw buffer loads and stores with out-of-range offsets for lanes outside the matrix.
+#include "quant_common.hpp"
+
+namespace fp4k {
+
+constexpr int FT = 128;   // rows per tile
+constexpr int FF = 64;    // columns per tile
+constexpr int FPP = NT / 8;          // rows per pass
+constexpr int FPASSES = FT / FPP;
+
+// nearest-even float32 -> bfloat16 bits (finite inputs; overflow rounds to infinity)
+__device__ __forceinline__ uint32_t bf16_rne(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// decoded float32 values of 8 codes (element 0 in the low nibble of w) for scale value sv
+// and tensor decode scale g
+template <int FMT, int J>
+__device__ __forceinline__ void decode2(uint32_t w, float sv, float g, float* y) {
+  const auto p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, J);
+  float a = p[0] * sv, b = p[1] * sv;                // exact
+  if constexpr (FMT != FMT_E8M0) {
+    a = a * g;
+    b = b * g;
+  }
+  y[2 * J] = a;
+  y[2 * J + 1] = b;
+}
+
+template <int FMT>
+__device__ __forceinline__ void decode8(uint32_t w, float sv, float g, float* y) {
+  decode2<FMT, 0>(w, sv, g, y);
+  decode2<FMT, 1>(w, sv, g, y);
+  decode2<FMT, 2>(w, sv, g, y);
+  decode2<FMT, 3>(w, sv, g, y);
+}
+
+// scale value of a code: UE5M3 / E4M3 by their decoders, E8M0 as 2^(c-127)
+template <int FMT>
+__device__ __forceinline__ float scale_value(uint32_t c) {
+  if constexpr (FMT == FMT_E8M0) return e8m0_inv(254u - c);
+  else return dec_scale3<FMT>(c);
+}
+
+// store 8 decoded values (float32: 32 bytes, bfloat16: 16 bytes) at byte offset off
+template <bool BF16>
+__device__ __forceinline__ void store8(rsrc_t r, uint32_t off, const float* y) {
+  if constexpr (BF16) {
+    const v4u w = {bf16_rne(y[0]) | (bf16_rne(y[1]) << 16), bf16_rne(y[2]) | (bf16_rne(y[3]) << 16),
+                   bf16_rne(y[4]) | (bf16_rne(y[5]) << 16), bf16_rne(y[6]) | (bf16_rne(y[7]) << 16)};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
+  } else {
+    const v4u a = {__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])};
+    const v4u b = {__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]), __float_as_uint(y[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(a, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(b, r, off == OOB ? OOB : off + 16u, 0, 0);
+  }
+}
+
+template <int FMT, int B, bool F32, bool BF16>
+__global__ __launch_bounds__(NT) void k_fake_quant(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                   int64_t ld, const float* __restrict__ d_amax, float T,
+                                                   void* __restrict__ y, int64_t ldy) {
+  constexpr int LB = B / 8;                     // lanes per block
+  constexpr int ESZ = F32 ? 4 : 2, OSZ = BF16 ? 2 : 4;
+  const int64_t nft = (cols + FF - 1) / FF;
+  const int64_t t0 = (int64_t)(blockIdx.x / nft) * FT, f0 = (int64_t)(blockIdx.x % nft) * FF;
+  TensorScales ts{1.0f, 1.0f, 1.0f};
+  if constexpr (FMT != FMT_E8M0) ts = tensor_scales(d_amax, T);
+  const int lc = threadIdx.x & 7, lr = threadIdx.x >> 3;
+  const int rl = (int)min(rows - t0, (int64_t)FT), cl = (int)min(cols - f0, (int64_t)FF);
+  const bool cok = lc * 8 < cl;
+  const rsrc_t rx = make_rsrc(reinterpret_cast<const char*>(x) + (t0 * ld + f0) * ESZ);
+  const rsrc_t ry = make_rsrc(reinterpret_cast<char*>(y) + (t0 * ldy + f0) * OSZ);
+  const uint32_t ld_b = (uint32_t)(ld * ESZ), ldy_b = (uint32_t)(ldy * OSZ);
+  Chunk8<F32> c[FPASSES];
+#pragma unroll
+  for (int p = 0; p < FPASSES; ++p) {
+    const int r = p * FPP + lr;
+    c[p].load(rx, (cok && r < rl) ? (uint32_t)r * ld_b + (uint32_t)(lc * 8 * ESZ) : OOB);
+  }
+#pragma unroll
+  for (int p = 0; p < FPASSES; ++p) {
+    const int r = p * FPP + lr;
+    float v[8];
+    c[p].to_float(v);
+    float am = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(v[j]));
+    am = group_max<LB>(am);
+    uint32_t code;
+    float mult;
+    block_scale<FMT>(am, ts, code, mult);
+    uint32_t w;
+    payload<8, false>(v, mult, 0, 0, 0, &w);
+    float out[8];
+    decode8<FMT>(w, scale_value<FMT>(code), ts.g, out);
+    store8<BF16>(ry, (cok && r < rl) ? (uint32_t)r * ldy_b + (uint32_t)(lc * 8 * OSZ) : OOB, out);
+  }
+}
+
+// scale code of element (r, k) of an operand: 1D [rows x K/B], 2D [rows/16 x K/16], or the
+// transposed 2D grid [K/16 x rows/16] of the weight this operand is the transpose of
+template <int LAYOUT, int B>
+__device__ __forceinline__ int64_t scale_index(int64_t r, int64_t k, int64_t rows, int64_t K) {
+  if constexpr (LAYOUT == 0) return r * (K / B) + k / B;
+  else if constexpr (LAYOUT == 1) return (r / 16) * (K / 16) + k / 16;
+  else return (k / 16) * (rows / 16) + r / 16;
+}
+
+template <int FMT, int B, int LAYOUT, bool BF16>
+__global__ __launch_bounds__(NT) void k_dequant(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
+                                                const float* __restrict__ d_g, int64_t rows, int64_t K,
+                                                void* __restrict__ y, int64_t ldy) {
+  constexpr int OSZ = BF16 ? 2 : 4;
+  const int64_t nft = (K + FF - 1) / FF;
+  const int64_t t0 = (int64_t)(blockIdx.x / nft) * FT, f0 = (int64_t)(blockIdx.x % nft) * FF;
+  const float g = (FMT == FMT_E8M0 || d_g == nullptr) ? 1.0f : *d_g;
+  const int lc = threadIdx.x & 7, lr = threadIdx.x >> 3;
+  const int rl = (int)min(rows - t0, (int64_t)FT), cl = (int)min(K - f0, (int64_t)FF);
+  const bool cok = lc * 8 < cl;
+  const rsrc_t rq = make_rsrc(q + t0 * (K / 2) + f0 / 2);
+  const rsrc_t ry = make_rsrc(reinterpret_cast<char*>(y) + (t0 * ldy + f0) * OSZ);
+  const uint32_t qrow = (uint32_t)(K / 2), ldy_b = (uint32_t)(ldy * OSZ);
+  uint32_t w[FPASSES];
+  uint32_t sc[FPASSES];
+#pragma unroll
+  for (int p = 0; p < FPASSES; ++p) {
+    const int r = p * FPP + lr;
+    const bool ok = cok && r < rl;
+    w[p] = __builtin_amdgcn_raw_buffer_load_b32(rq, ok ? (uint32_t)r * qrow + (uint32_t)(lc * 4) : OOB, 0, 0);
+    sc[p] = ok ? s[scale_index<LAYOUT, B>(t0 + r, f0 + lc * 8, rows, K)] : 127u;
+  }
+#pragma unroll
+  for (int p = 0; p < FPASSES; ++p) {
+    const int r = p * FPP + lr;
+    float out[8];
+    decode8<FMT>(w[p], scale_value<FMT>(sc[p]), g, out);
+    store8<BF16>(ry, (cok && r < rl) ? (uint32_t)r * ldy_b + (uint32_t)(lc * 8 * OSZ) : OOB, out);
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+template <int FMT, int B, bool F32, bool BF16>
+static hipError_t launch_fq(const FakeQuantArgs& a) {
+  const int64_t tiles = ((a.rows + FT - 1) / FT) * ((a.cols + FF - 1) / FF);
+  hipLaunchKernelGGL((k_fake_quant<FMT, B, F32, BF16>), dim3((unsigned)tiles), dim3(NT), 0, a.stream, a.x, a.rows,
+                     a.cols, a.ld, a.d_amax, a.T, a.y, a.ldy);
+  return hipGetLastError();
+}
+
+template <int FMT, int B>
+static hipError_t fq_types(const FakeQuantArgs& a) {
+  if (a.f32) return a.bf16_out ? launch_fq<FMT, B, true, true>(a) : launch_fq<FMT, B, true, false>(a);
+  return a.bf16_out ? launch_fq<FMT, B, false, true>(a) : launch_fq<FMT, B, false, false>(a);
+}
+
+hipError_t run_fake_quant(const FakeQuantArgs& a) {
+  if (a.rows == 0 || a.cols == 0) return hipSuccess;
+  if (a.fmt == FMT_E8M0) return fq_types<FMT_E8M0, 32>(a);
+  if (a.fmt == FMT_UE5M3) return a.block == 16 ? fq_types<FMT_UE5M3, 16>(a) : fq_types<FMT_UE5M3, 32>(a);
+  return a.block == 16 ? fq_types<FMT_E4M3, 16>(a) : fq_types<FMT_E4M3, 32>(a);
+}
+
+template <int FMT, int B, int LAYOUT, bool BF16>
+static hipError_t launch_dq(const DequantArgs& a) {
+  const int64_t tiles = ((a.rows + FT - 1) / FT) * ((a.K + FF - 1) / FF);
+  hipLaunchKernelGGL((k_dequant<FMT, B, LAYOUT, BF16>), dim3((unsigned)tiles), dim3(NT), 0, a.stream, a.q, a.s, a.g,
+                     a.rows, a.K, a.y, a.ldy);
+  return hipGetLastError();
+}
+
+template <int FMT, int B, int LAYOUT>
+static hipError_t dq_out(const DequantArgs& a) {
+  return a.bf16_out ? launch_dq<FMT, B, LAYOUT, true>(a) : launch_dq<FMT, B, LAYOUT, false>(a);
+}
+
+template <int FMT>
+static hipError_t dq_layout(const DequantArgs& a) {
+  if (a.layout == 1) return dq_out<FMT, 16, 1>(a);
+  if (a.layout == 2) return dq_out<FMT, 16, 2>(a);
+  return a.block == 16 ? dq_out<FMT, 16, 0>(a) : dq_out<FMT, 32, 0>(a);
+}
+
+hipError_t run_dequantize(const DequantArgs& a) {
+  if (a.rows == 0 || a.K == 0) return hipSuccess;
+  if (a.fmt == FMT_E8M0) return dq_out<FMT_E8M0, 32, 0>(a);
+  if (a.fmt == FMT_UE5M3) return dq_layout<FMT_UE5M3>(a);
+  return dq_layout<FMT_E4M3>(a);
+}
+
+}  // namespace fp4k

@@ -60,6 +60,35 @@ struct RowColArgs {
   hipStream_t stream;
 };
 hipError_t run_quantize_rowcol(const RowColArgs& a);
+
+// Quantize then decode (ROW view, nearest-even) into float32 or bfloat16.
+struct FakeQuantArgs {
+  const void* x;
+  bool f32;
+  int64_t rows, cols, ld;
+  int fmt, block;
+  const float* d_amax;
+  float T;
+  void* y;
+  bool bf16_out;
+  int64_t ldy;
+  hipStream_t stream;
+};
+hipError_t run_fake_quant(const FakeQuantArgs& a);
+
+// Decode a quantized operand [rows x K] (layout 0: 1D scales, 1: 2D, 2: transposed 2D).
+struct DequantArgs {
+  const uint8_t* q;
+  const uint8_t* s;
+  const float* g;
+  int fmt, block, layout;
+  int64_t rows, K;
+  void* y;
+  bool bf16_out;
+  int64_t ldy;
+  hipStream_t stream;
+};
+hipError_t run_dequantize(const DequantArgs& a);
 hipError_t run_amax(const void* x, bool f32, int64_t rows, int64_t cols, int64_t ld, int hadamard_n, float* out,
                     hipStream_t stream);
 hipError_t run_cache_update(float* amax, int32_t* valid, int32_t D, int64_t step, const float* obs, hipStream_t stream);

@@ -25,96 +25,11 @@
 //                 unsigned integers).
 // The quantize kernels also write the operand's g (workgroup 0, thread 0) and, if asked,
 // fold their block maxima into the observed amax (one atomic per workgroup).
-#include <atomic>
 #include <type_traits>
 
-#include "fp4_device.hpp"
-#include "launch.hpp"
+#include "quant_common.hpp"
 
 namespace fp4k {
-
-constexpr int NT = 256;
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
-__device__ __forceinline__ void atomic_max_nonneg(float* p, float v) {
-  atomicMax(reinterpret_cast<unsigned int*>(p), __float_as_uint(v));
-}
-
-// Workgroup max of a non-negative value folded into *out with one atomic (all NT threads call).
-__device__ __forceinline__ void wg_max_to(float* out, float v) {
-  __shared__ float part[NT / 64];
-  v = wave_max(v);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float m = part[0];
-#pragma unroll
-    for (int i = 1; i < NT / 64; ++i) m = fmaxf(m, part[i]);
-    atomic_max_nonneg(out, m);
-  }
-}
-
-// g of the operand (1 for E8M0), written once per launch.
-template <int FMT>
-__device__ __forceinline__ void write_g(float* d_g, const TensorScales& ts) {
-  if (d_g && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *d_g = (FMT == FMT_E8M0) ? 1.0f : ts.g;
-}
-
-// Load 8 consecutive input elements (bf16 or fp32) as floats.
-template <bool F32>
-__device__ __forceinline__ void load8(const void* base, int64_t elem, float* v) {
-  if constexpr (F32) {
-    const uint4 a = *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(base) + elem);
-    const uint4 b = *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(base) + elem + 4);
-    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
-    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
-  } else {
-    const uint4 a = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
-    v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
-    v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
-  }
-}
-
-// Scale code and payload multiplier of one block with maximum amax_b.
-template <int FMT>
-__device__ __forceinline__ void block_scale(float amax_b, const TensorScales& ts, uint32_t& code, float& mult) {
-  if constexpr (FMT == FMT_E8M0) {
-    code = e8m0_code(amax_b);
-    mult = e8m0_inv(code);
-  } else {
-    code = enc_scale3<FMT>(amax_b * ts.s_blk);
-    if (code == 0) code = ScaleFmt<FMT>::ONE;          // zero-scale rule
-    mult = ts.s_enc / dec_scale3<FMT>(code);           // correctly rounded division
-  }
-}
-
-// Quantize n (multiple of 8) values with multiplier mult into n/8 dwords of codes.
-// SR: logical index of v[0] is i0 (multiple of 8).
-template <int N, bool SR>
-__device__ __forceinline__ void payload(const float* v, float mult, uint64_t i0, uint64_t seed, uint64_t offset,
-                                        uint32_t* words) {
-#pragma unroll
-  for (int w = 0; w < N / 8; ++w) {
-    float r[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) r[j] = v[8 * w + j] * mult;
-    if constexpr (SR) {
-      uint32_t u[8];
-      philox_u16x8((i0 >> 3) + w, seed, offset, u);
-      uint32_t word = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) word |= e2m1_sr(r[j], u[j]) << (4 * j);
-      words[w] = word;
-    } else {
-      words[w] = e2m1_pack8(r);
-    }
-  }
-}
 
 // ---------------------------------------------------------------- ROW view
 // Thread layout: TPR threads per row (a power of two, at most NT), NT / TPR rows per pass;
@@ -306,54 +221,6 @@ __global__ __launch_bounds__(NT) void k_quant_col(const void* __restrict__ x, in
 // are completed in that XCD's L2 before they are written back.
 constexpr int RT = 128;   // tokens per fused tile
 constexpr int RF = 64;    // features per fused tile
-
-// max over groups of G neighbouring lanes (G = 1, 2 or 4; groups aligned to G)
-template <int G>
-__device__ __forceinline__ float group_max(float v) {
-  if constexpr (G >= 2)
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));  // lane ^ 1
-  if constexpr (G >= 4)
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));  // lane ^ 2
-  static_assert(G == 1 || G == 2 || G == 4, "ROW blocks span 1, 2 or 4 lanes");
-  return v;
-}
-
-// Raw buffer access: a per-tile resource (base, 0x7FFFFFF0 bytes) and 32-bit lane offsets.
-// A lane whose element lies outside the matrix uses offset OOB instead: the hardware's range
-// check then returns zeros for its load and drops its store, so every memory instruction is
-// issued by every wave (no branches around them, exact wait counts).
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-constexpr uint32_t OOB = 0x80000000u;
-constexpr int RSRC_RANGE = 0x7FFFFFF0;
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, RSRC_RANGE, 0x00020000);
-}
-
-// 8 consecutive input elements as loaded (one or two 16-byte words) and as floats
-template <bool F32>
-struct Chunk8 {
-  uint4 w[F32 ? 2 : 1];
-  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) {
-#pragma unroll
-    for (int h = 0; h < (F32 ? 2 : 1); ++h) {
-      const v4u t = __builtin_amdgcn_raw_buffer_load_b128(r, off == OOB ? OOB : off + 16u * h, 0, 0);
-      w[h] = make_uint4(t[0], t[1], t[2], t[3]);
-    }
-  }
-  __device__ __forceinline__ void to_float(float* v) const {
-    if constexpr (F32) {
-      v[0] = __uint_as_float(w[0].x); v[1] = __uint_as_float(w[0].y);
-      v[2] = __uint_as_float(w[0].z); v[3] = __uint_as_float(w[0].w);
-      v[4] = __uint_as_float(w[1].x); v[5] = __uint_as_float(w[1].y);
-      v[6] = __uint_as_float(w[1].z); v[7] = __uint_as_float(w[1].w);
-    } else {
-      v[0] = bf16_lo(w[0].x); v[1] = bf16_hi(w[0].x); v[2] = bf16_lo(w[0].y); v[3] = bf16_hi(w[0].y);
-      v[4] = bf16_lo(w[0].z); v[5] = bf16_hi(w[0].z); v[6] = bf16_lo(w[0].w); v[7] = bf16_hi(w[0].w);
-    }
-  }
-};
 
 // Persistent: gridDim.x workgroups walk the tiles. When the tile count and the grid are
 // multiples of 8, workgroup w (on XCD w % 8) takes tiles k*P + w/8 + i*(gridDim.x/8) of
@@ -679,18 +546,6 @@ static hipError_t launch_col(const QuantArgs& a) {
   hipLaunchKernelGGL((k_quant_col<FMT, B, SR, F32, HN>), grid, dim3(NT), 0, a.stream, a.x, a.rows, a.cols, a.ld,
                      a.d_amax, a.T, a.seed, a.offset, a.q, a.s, a.d_amax_obs, a.d_g);
   return hipGetLastError();
-}
-
-// compute units of the current device (cached per device; 256 on MI355X)
-static int device_cu_count() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n > 0) return n;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
-  cached[dev].store(n, std::memory_order_relaxed);
-  return n;
 }
 
 template <int FMT, int B, bool SRR, bool SRC, bool F32, int HN>

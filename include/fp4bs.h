@@ -164,6 +164,34 @@ fp4_status fp4_quantize_rowcol(const void* x, int32_t x_dtype, int64_t rows, int
                                uint8_t* q, uint8_t* s, float* d_g, float* d_amax_obs_row,
                                uint8_t* q_t, uint8_t* s_t, float* d_g_t, float* d_amax_obs_col, void* stream);
 
+/*
+ * fp4_fake_quant - inference fake quantization: y = the decoded value of x's FP4 ROW-view
+ * quantization, x_hat = E2M1(q) * S * g (g = 1 for E8M0), in one pass [UE5M3 approach,
+ * training and inference setup: held-out likelihoods with FP4 fake quantization under a
+ * delayed D=50, current D=1 or frozen activation-scale policy; the policy only decides
+ * which cached amax d_amax holds for the call].
+ *   x, x_dtype, rows, cols, ld   as in fp4_quantize
+ *   cfg      view FP4_VIEW_ROW, stochastic 0, hadamard_n 0; fmt, block and T as in
+ *            fp4_quantize
+ *   d_amax   device float, the cached amax (UE5M3/E4M3; may be NULL for E8M0)
+ *   y        device, rows x cols of y_dtype (FP4_IN_FP32 or FP4_IN_BF16), row stride ldy
+ *            elements (>= cols, ldy * elem_size a multiple of 16 bytes and <= 2^24)
+ * Arithmetic: the codes and scales are exactly those fp4_quantize writes; E2M1(q) * S is
+ * exact in float32 and the product with g is one float32 multiply (nearest-even); bfloat16
+ * output rounds that float32 to nearest-even. Requires cols % B == 0.
+ */
+fp4_status fp4_fake_quant(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld,
+                          const fp4_quant_cfg* cfg, const float* d_amax, void* y, int32_t y_dtype, int64_t ldy,
+                          void* stream);
+
+/*
+ * fp4_dequantize - decode a quantized operand (any scale layout) to y [rows x k] of y_dtype
+ * (FP4_IN_FP32 or FP4_IN_BF16), row stride ldy: y = E2M1(q) * S * g with the arithmetic of
+ * fp4_fake_quant [UE5M3 approach]. For a TILE2D weight, the forward operand gives W and the
+ * transposed operand W^T. The operand's g may be NULL (1.0).
+ */
+fp4_status fp4_dequantize(const fp4_operand* a, void* y, int32_t y_dtype, int64_t ldy, void* stream);
+
 /* fp4_quantize_sizes - byte sizes of q, s and q_t for a call with these arguments (host only). */
 fp4_status fp4_quantize_sizes(int64_t rows, int64_t cols, const fp4_quant_cfg* cfg,
                               size_t* q_bytes, size_t* s_bytes, size_t* qt_bytes);

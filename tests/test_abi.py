@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_and_binding_agree():
     decl = declared_functions()
     assert set(decl) == set(_lib.EXPORTED), decl
-    assert len(decl) == 12
+    assert len(decl) == 14
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -165,4 +165,25 @@ def test_rowcol_rejects_bad_arguments(lib):
     assert rowcol(lib, r, c, a_c=0) == _lib.FP4_EINVAL                      # UE5M3 needs both amax values
     mr, mc = cfg(fmt=2, block=32, view=0, T=0.0), cfg(fmt=2, block=32, view=1, T=0.0)
     assert rowcol(lib, mr, mc, rows=48) == _lib.FP4_EINVAL                  # 48 % 32
+    assert lib.fp4_last_error().decode()
+
+
+def test_fake_quant_and_dequantize_reject_bad_arguments(lib):
+    P = ctypes.c_void_p(4096)
+    fq = lambda c, rows=64, cols=64, ld=64, ydt=0, ldy=64, y=P, amax=P: lib.fp4_fake_quant(
+        P, 0, rows, cols, ld, ctypes.byref(c), amax, y, ydt, ldy, None)
+    assert fq(cfg(view=1)) == _lib.FP4_EUNSUPPORTED                 # ROW view only
+    assert fq(cfg(sr=1)) == _lib.FP4_EUNSUPPORTED                   # nearest-even only
+    assert fq(cfg(), cols=40, ld=40, ldy=40) == _lib.FP4_EINVAL    # cols % B
+    assert fq(cfg(), ydt=5) == _lib.FP4_EINVAL
+    assert fq(cfg(), ldy=32) == _lib.FP4_EINVAL                    # ldy < cols
+    assert fq(cfg(), y=ctypes.c_void_p(4100)) == _lib.FP4_EALIGN
+    assert fq(cfg(), ldy=68) == _lib.FP4_EALIGN                    # 68 * 2 bytes
+    assert fq(cfg(), amax=None) == _lib.FP4_EINVAL                 # UE5M3 needs the cached amax
+    y = ctypes.c_void_p(4096)
+    assert lib.fp4_dequantize(ctypes.byref(op(k=96)), y, 0, 96, None) == _lib.FP4_EINVAL          # K % 64
+    assert lib.fp4_dequantize(ctypes.byref(op()), y, 7, 128, None) == _lib.FP4_EINVAL
+    assert lib.fp4_dequantize(ctypes.byref(op()), y, 0, 64, None) == _lib.FP4_EINVAL             # ldy < k
+    assert lib.fp4_dequantize(ctypes.byref(op()), None, 0, 128, None) == _lib.FP4_EINVAL
+    assert lib.fp4_dequantize(ctypes.byref(op(fmt=2, block=32, layout=1)), y, 0, 128, None) == _lib.FP4_EUNSUPPORTED
     assert lib.fp4_last_error().decode()
