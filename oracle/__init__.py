@@ -26,18 +26,22 @@ Pins (tests/test_oracle_*.py) and their strength:
 - fake quantization: decode against exact rationals, E8M0 fake-quant values against a
   brute-force nearest search over the block's scaled codebook, bfloat16 rounding against
   torch's cast, policy order-dependence and D=1 == per-request amax.
+- MXFP4 -> FP8: E4M3 codes against torch's float8_e4m3fn cast, exact round trip of the
+  values for blocks within 14 binades of their chunk's largest, the chunk scale rule and
+  the 384 ceiling, hand-worked examples.
 """
-from . import formats, philox, hadamard, quantize, gemm, exact, fakequant
+from . import formats, philox, hadamard, quantize, gemm, exact, fakequant, fp8convert
 from .formats import UE5M3, E4M3, E8M0
 from .quantize import (AmaxCache, QuantResult, quantize_1d, quantize_2d, quantize_col, tensor_amax,
                        tensor_scales, pack_codes, unpack_codes, transposed_view)
 from .gemm import gemm_model, gemm_fp64, rtz_add_f32, operand_from_quant, output_scale, expand_2d_scales
 from .fakequant import dequantize, fake_quant, f32_to_bf16_bits, FakeQuantPolicy
+from .fp8convert import mxfp4_to_fp8, fp8_values
 
 __all__ = [
-    "formats", "philox", "hadamard", "quantize", "gemm", "exact", "fakequant",
+    "formats", "philox", "hadamard", "quantize", "gemm", "exact", "fakequant", "fp8convert",
     "UE5M3", "E4M3", "E8M0", "AmaxCache", "QuantResult", "quantize_1d", "quantize_2d", "quantize_col",
     "tensor_amax", "tensor_scales", "pack_codes", "unpack_codes", "transposed_view",
     "gemm_model", "gemm_fp64", "rtz_add_f32", "operand_from_quant", "output_scale", "expand_2d_scales",
-    "dequantize", "fake_quant", "f32_to_bf16_bits", "FakeQuantPolicy",
+    "dequantize", "fake_quant", "f32_to_bf16_bits", "FakeQuantPolicy", "mxfp4_to_fp8", "fp8_values",
 ]
