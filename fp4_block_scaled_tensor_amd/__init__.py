@@ -20,7 +20,7 @@ UE5M3, E4M3, E8M0 = FP4_UE5M3, FP4_E4M3, FP4_E8M0
 ROW, COL, TILE2D = FP4_VIEW_ROW, FP4_VIEW_COL, FP4_VIEW_TILE2D
 
 __all__ = ["UE5M3", "E4M3", "E8M0", "ROW", "COL", "TILE2D", "QTensor", "AmaxCache", "quantize", "quantize_rowcol",
-           "fake_quant", "dequantize", "FakeQuantPolicy", "tensor_amax",
+           "fake_quant", "dequantize", "FakeQuantPolicy", "mxfp4_to_fp8", "tensor_amax",
            "gemm_fprop", "gemm_dgrad", "gemm_wgrad", "debug_encode", "FP4Error", "library"]
 
 
@@ -186,6 +186,18 @@ def dequantize(a: QTensor, out_dtype=torch.float32, out: torch.Tensor | None = N
     op = a.operand()
     _lib.check(lib.fp4_dequantize(ctypes.byref(op), _ptr(out), _out_dtype(out.dtype), out.stride(0), _stream()))
     return out
+
+
+def mxfp4_to_fp8(a: QTensor, transpose: bool = False):
+    """fp4_mxfp4_to_fp8: (E4M3 bytes [rows, k] or [k, rows] as uint8, chunk scale codes
+    [rows, k/128] as uint8) of an MXFP4 operand."""
+    lib = _lib.load()
+    dev = a.q.device
+    y = torch.empty((a.k, a.rows) if transpose else (a.rows, a.k), dtype=torch.uint8, device=dev)
+    s8 = torch.empty((a.rows, a.k // 128), dtype=torch.uint8, device=dev)
+    op = a.operand()
+    _lib.check(lib.fp4_mxfp4_to_fp8(ctypes.byref(op), int(bool(transpose)), _ptr(y), _ptr(s8), _stream()))
+    return y, s8
 
 
 class FakeQuantPolicy:

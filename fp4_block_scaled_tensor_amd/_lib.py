@@ -16,7 +16,7 @@ FP4_SCALES_1D, FP4_SCALES_2D, FP4_SCALES_2D_T = 0, 1, 2
 ABI_VERSION = 1
 
 EXPORTED = [
-    "fp4_quantize", "fp4_quantize_rowcol", "fp4_fake_quant", "fp4_dequantize", "fp4_quantize_sizes", "fp4_tensor_amax", "amax_cache_update", "amax_cache_reset",
+    "fp4_quantize", "fp4_quantize_rowcol", "fp4_fake_quant", "fp4_dequantize", "fp4_mxfp4_to_fp8", "fp4_quantize_sizes", "fp4_tensor_amax", "amax_cache_update", "amax_cache_reset",
     "fp4_gemm_fprop", "fp4_gemm_dgrad", "fp4_gemm_wgrad", "fp4_debug_encode", "fp4_last_error", "fp4_abi_version",
 ]
 
@@ -45,6 +45,7 @@ SIGNATURES = {
                              _P, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "fp4_fake_quant": ([_P, _I32, _I64, _I64, _I64, ctypes.POINTER(QuantCfg), _P, _P, _I32, _I64, _P], ctypes.c_int),
     "fp4_dequantize": ([ctypes.POINTER(Operand), _P, _I32, _I64, _P], ctypes.c_int),
+    "fp4_mxfp4_to_fp8": ([ctypes.POINTER(Operand), _I32, _P, _P, _P], ctypes.c_int),
     "fp4_quantize_sizes": ([_I64, _I64, ctypes.POINTER(QuantCfg), ctypes.POINTER(_SZ), ctypes.POINTER(_SZ),
                             ctypes.POINTER(_SZ)], ctypes.c_int),
     "fp4_tensor_amax": ([_P, _I32, _I64, _I64, _I64, _I32, _P, _P], ctypes.c_int),

@@ -328,6 +328,24 @@ fp4_status fp4_dequantize(const fp4_operand* a, void* y, int32_t y_dtype, int64_
   return hip_status(fp4k::run_dequantize(d), "fp4_dequantize");
 }
 
+fp4_status fp4_mxfp4_to_fp8(const fp4_operand* a, int32_t transpose, uint8_t* y, uint8_t* s8, void* stream) {
+  fp4_status st;
+  if ((st = check_operand(a, "operand")) != FP4_OK) return st;
+  if (a->fmt != FP4_E8M0 || a->scale_layout != FP4_SCALES_1D)
+    return fail(FP4_EUNSUPPORTED, "mxfp4_to_fp8: the operand must be MXFP4 (E8M0, block 32, 1D scales)");
+  if (transpose != 0 && transpose != 1) return fail(FP4_EINVAL, "transpose must be 0 or 1");
+  if (a->k % 128) return fail(FP4_EINVAL, "mxfp4_to_fp8: k must be a multiple of 128 (got %lld)", (long long)a->k);
+  if (transpose && a->rows % 16) return fail(FP4_EINVAL, "mxfp4_to_fp8: transposed output needs rows % 16 == 0");
+  if (a->k > (int64_t(1) << 23) || a->rows > (int64_t(1) << 23))
+    return fail(FP4_EUNSUPPORTED, "mxfp4_to_fp8: rows and k must be <= 2^23");
+  if (a->rows > 0 && a->k > 0) {
+    if (!y || !s8) return fail(FP4_EINVAL, "NULL y or s8");
+    if (!aligned(y, 16)) return fail(FP4_EALIGN, "y must be 16-byte aligned");
+  }
+  return hip_status(fp4k::run_mx_to_fp8(a->q, a->s, a->rows, a->k, transpose != 0, y, s8, (hipStream_t)stream),
+                    "fp4_mxfp4_to_fp8");
+}
+
 fp4_status fp4_tensor_amax(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld, int32_t hadamard_n,
                            float* d_amax_out, void* stream) {
   if (x_dtype != FP4_IN_BF16 && x_dtype != FP4_IN_FP32) return fail(FP4_EINVAL, "unknown input dtype %d", x_dtype);

@@ -18,6 +18,15 @@
 //                 made and decoded in registers.
 //   k_dequant     a quantized operand (1D, 2D or transposed-2D scales) -> x_hat, the same
 //                 tiling over its [rows x K] values.
+//   k_mx_to_fp8   MXFP4 operand -> FP8 E4M3 with one E8M0 scale per 128-element chunk
+//                 ("Practical FP4 Training for Large-Scale MoE Models on Hopper GPUs",
+//                 methodology: direct FP4 -> FP8 conversion, hierarchical scale alignment
+//                 from block 32 to block 128, transpose fused): chunk code c = e_max -
+//                 min(6, e_max) over the chunk's four block codes, element
+//                 E4M3(E2M1(q) * 2^(e_b - c)) nearest-even with subnormals, sign kept. A
+//                 256-row x 128-column tile per workgroup, 4 lanes per row chunk (64 payload
+//                 bytes), e_max by DPP, codes by a per-block v_perm_b32 table; the transposed
+//                 form goes through a 34 KB LDS byte tile.
 // Raw buffer loads and stores with out-of-range offsets for lanes outside the matrix.
 #include "quant_common.hpp"
 
@@ -161,6 +170,116 @@ __global__ __launch_bounds__(NT) void k_dequant(const uint8_t* __restrict__ q, c
   }
 }
 
+// ---------------------------------------------------------------- MXFP4 -> FP8
+constexpr int XK = 128;   // K per conversion tile (one 128-element chunk)
+constexpr int XT = 256;   // rows per conversion tile
+constexpr int XP = XT / 64;   // rows per thread (passes of 64 rows)
+constexpr int XRS = XT + 16;   // LDS byte-tile row stride (16-byte aligned, staggers banks)
+
+// max over the 4 lanes of a quad (integers)
+__device__ __forceinline__ int quad_max(int v) {
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));   // lane ^ 1
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));   // lane ^ 2
+  return v;
+}
+
+// E4M3 code (sign in bit 7) of E2M1 value a times 2^k, k <= 6 (nearest-even; exact when the
+// product is on E4M3's grid). Below 2^-20 every E2M1 value rounds to 0, so k is clamped.
+__device__ __forceinline__ uint32_t e4m3_of(float a, int k) {
+  k = k < -20 ? -20 : k;
+  const float v = a * __uint_as_float((uint32_t)(k + 127) << 23);   // exact
+  return enc_scale3<FMT_E4M3>(fabsf(v)) | ((__float_as_uint(v) >> 24) & 0x80u);
+}
+
+// 32 codes of one MXFP4 block (16 payload bytes) -> 32 E4M3 bytes (8 dwords).
+// For k >= -5 every nonzero E2M1 magnitude times 2^k is a normal E4M3 number, whose code is
+// the k = 0 code plus 8k (the exponent field moves by k): the block's 8-entry magnitude ->
+// code table is two dwords, looked up 4 bytes at a time with v_perm_b32 (even and odd
+// nibbles separately, then interleaved), and the E2M1 sign bit moves to bit 7. Smaller k
+// (a block more than 11 binades below its chunk's largest) takes the per-element path.
+__device__ __forceinline__ void block_to_fp8(const uint4& q, int k, uint32_t* out) {
+  const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+  if (k >= -5) {
+    const uint32_t add = (uint32_t)(k * 8);
+    const uint32_t t_lo = 0x3C383000u + add * 0x01010100u;   // magnitudes 0, 0.5, 1, 1.5
+    const uint32_t t_hi = 0x4C484440u + add * 0x01010101u;   // magnitudes 2, 3, 4, 6
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t w = qw[d];
+      const uint32_t ev = __builtin_amdgcn_perm(t_hi, t_lo, w & 0x07070707u) | ((w & 0x08080808u) << 4);
+      const uint32_t od = __builtin_amdgcn_perm(t_hi, t_lo, (w >> 4) & 0x07070707u) | (w & 0x80808080u);
+      out[2 * d] = __builtin_amdgcn_perm(od, ev, 0x05010400u);       // elements 0..3
+      out[2 * d + 1] = __builtin_amdgcn_perm(od, ev, 0x07030602u);   // elements 4..7
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      float v[8];
+      decode8<FMT_E8M0>(qw[d], 1.0f, 1.0f, v);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        out[2 * d + h] = e4m3_of(v[4 * h], k) | (e4m3_of(v[4 * h + 1], k) << 8) | (e4m3_of(v[4 * h + 2], k) << 16) |
+                         (e4m3_of(v[4 * h + 3], k) << 24);
+    }
+  }
+}
+
+template <bool TRANSPOSE>
+__global__ __launch_bounds__(NT) void k_mx_to_fp8(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
+                                                  int64_t rows, int64_t K, uint8_t* __restrict__ y,
+                                                  uint8_t* __restrict__ s8) {
+  __shared__ __align__(16) uint8_t tile[TRANSPOSE ? XK : 1][TRANSPOSE ? XRS : 16];
+  const int64_t nkt = K / XK;
+  const int64_t r0 = (int64_t)(blockIdx.x / nkt) * XT, k0 = (int64_t)(blockIdx.x % nkt) * XK;
+  const int b = threadIdx.x & 3, lr = threadIdx.x >> 2;        // block within the chunk, row
+  const int rl = (int)min(rows - r0, (int64_t)XT);
+  const rsrc_t rq = make_rsrc(q + r0 * (K / 2) + k0 / 2);
+  const uint32_t qrow = (uint32_t)(K / 2);
+  uint4 qv[XP];
+  int eb[XP];
+#pragma unroll
+  for (int p = 0; p < XP; ++p) {
+    const int r = p * 64 + lr;
+    const bool ok = r < rl;
+    const v4u t = __builtin_amdgcn_raw_buffer_load_b128(rq, ok ? (uint32_t)r * qrow + (uint32_t)(b * 16) : OOB, 0, 0);
+    qv[p] = make_uint4(t[0], t[1], t[2], t[3]);
+    eb[p] = ok ? (int)s[(r0 + r) * (K / 32) + k0 / 32 + b] : 0;
+  }
+  const rsrc_t ry = make_rsrc(TRANSPOSE ? y + k0 * rows + r0 : y + r0 * K + k0);
+#pragma unroll
+  for (int p = 0; p < XP; ++p) {
+    const int r = p * 64 + lr;
+    const bool ok = r < rl;
+    const int emax = quad_max(eb[p]);
+    const int c = emax - min(6, emax);
+    if (b == 0 && ok) s8[(r0 + r) * (K / XK) + k0 / XK] = (uint8_t)c;
+    uint32_t out[8];
+    block_to_fp8(qv[p], eb[p] - c, out);
+    if constexpr (!TRANSPOSE) {
+      const uint32_t off = ok ? (uint32_t)r * (uint32_t)K + (uint32_t)(b * 32) : OOB;
+      const v4u lo = {out[0], out[1], out[2], out[3]}, hi = {out[4], out[5], out[6], out[7]};
+      __builtin_amdgcn_raw_buffer_store_b128(lo, ry, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(hi, ry, off == OOB ? OOB : off + 16u, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) tile[b * 32 + j][r] = (uint8_t)(out[j >> 2] >> (8 * (j & 3)));
+    }
+  }
+  if constexpr (TRANSPOSE) {
+    __syncthreads();
+    // y_t rows k0 + kk, bytes [r0, r0 + XT) in 16-byte pieces
+#pragma unroll
+    for (int i = 0; i < XK * XT / 16 / NT; ++i) {
+      const int piece = threadIdx.x + i * NT;
+      const int kk = piece / (XT / 16), c16 = piece % (XT / 16);
+      const uint4 w = *reinterpret_cast<const uint4*>(&tile[kk][c16 * 16]);
+      const v4u wv = {w.x, w.y, w.z, w.w};
+      __builtin_amdgcn_raw_buffer_store_b128(wv, ry, c16 * 16 < rl ? (uint32_t)kk * (uint32_t)rows + (uint32_t)(c16 * 16) : OOB,
+                                             0, 0);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 template <int FMT, int B, bool F32, bool BF16>
 static hipError_t launch_fq(const FakeQuantArgs& a) {
@@ -201,6 +320,17 @@ static hipError_t dq_layout(const DequantArgs& a) {
   if (a.layout == 1) return dq_out<FMT, 16, 1>(a);
   if (a.layout == 2) return dq_out<FMT, 16, 2>(a);
   return a.block == 16 ? dq_out<FMT, 16, 0>(a) : dq_out<FMT, 32, 0>(a);
+}
+
+hipError_t run_mx_to_fp8(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t K, bool transpose, uint8_t* y,
+                         uint8_t* s8, hipStream_t stream) {
+  if (rows == 0 || K == 0) return hipSuccess;
+  const int64_t tiles = ((rows + XT - 1) / XT) * (K / XK);
+  if (transpose)
+    hipLaunchKernelGGL(k_mx_to_fp8<true>, dim3((unsigned)tiles), dim3(NT), 0, stream, q, s, rows, K, y, s8);
+  else
+    hipLaunchKernelGGL(k_mx_to_fp8<false>, dim3((unsigned)tiles), dim3(NT), 0, stream, q, s, rows, K, y, s8);
+  return hipGetLastError();
 }
 
 hipError_t run_dequantize(const DequantArgs& a) {

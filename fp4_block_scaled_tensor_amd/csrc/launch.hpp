@@ -89,6 +89,10 @@ struct DequantArgs {
   hipStream_t stream;
 };
 hipError_t run_dequantize(const DequantArgs& a);
+
+// MXFP4 operand [rows x K] -> E4M3 [rows x K] or [K x rows] plus chunk scales [rows x K/128].
+hipError_t run_mx_to_fp8(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t K, bool transpose, uint8_t* y,
+                         uint8_t* s8, hipStream_t stream);
 hipError_t run_amax(const void* x, bool f32, int64_t rows, int64_t cols, int64_t ld, int hadamard_n, float* out,
                     hipStream_t stream);
 hipError_t run_cache_update(float* amax, int32_t* valid, int32_t D, int64_t step, const float* obs, hipStream_t stream);

@@ -192,6 +192,22 @@ fp4_status fp4_fake_quant(const void* x, int32_t x_dtype, int64_t rows, int64_t 
  */
 fp4_status fp4_dequantize(const fp4_operand* a, void* y, int32_t y_dtype, int64_t ldy, void* stream);
 
+/*
+ * fp4_mxfp4_to_fp8 - direct MXFP4 -> FP8 E4M3 conversion with hierarchical scale alignment
+ * [HOPPER methodology: FP4 -> FP8 without a BF16 intermediate, block 32 -> block 128 scale
+ * alignment, transpose fused with the conversion].
+ *   a          MXFP4 operand (E8M0, block 32, FP4_SCALES_1D), rows x k, k % 128 == 0
+ *   transpose  0: y is [rows x k] E4M3 bytes; 1: y is [k x rows] (rows % 16 == 0)
+ *   y          device, rows * k bytes, 16-byte aligned
+ *   s8         device, [rows x k/128] E8M0 chunk scale codes: the chunk's FP8 values times
+ *              2^(code - 127) are its real values
+ * Arithmetic: chunk code c = e_max - min(6, e_max) over the chunk's four block codes; each
+ * element becomes E4M3(E2M1(q) * 2^(e_b - c)), nearest-even with subnormals and the sign
+ * kept (|y| <= 384). Exact whenever e_max - e_b <= 14; smaller blocks round on E4M3's
+ * subnormal grid. rows, k <= 2^23.
+ */
+fp4_status fp4_mxfp4_to_fp8(const fp4_operand* a, int32_t transpose, uint8_t* y, uint8_t* s8, void* stream);
+
 /* fp4_quantize_sizes - byte sizes of q, s and q_t for a call with these arguments (host only). */
 fp4_status fp4_quantize_sizes(int64_t rows, int64_t cols, const fp4_quant_cfg* cfg,
                               size_t* q_bytes, size_t* s_bytes, size_t* qt_bytes);

@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_and_binding_agree():
     decl = declared_functions()
     assert set(decl) == set(_lib.EXPORTED), decl
-    assert len(decl) == 14
+    assert len(decl) == 15
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -186,4 +186,16 @@ def test_fake_quant_and_dequantize_reject_bad_arguments(lib):
     assert lib.fp4_dequantize(ctypes.byref(op()), y, 0, 64, None) == _lib.FP4_EINVAL             # ldy < k
     assert lib.fp4_dequantize(ctypes.byref(op()), None, 0, 128, None) == _lib.FP4_EINVAL
     assert lib.fp4_dequantize(ctypes.byref(op(fmt=2, block=32, layout=1)), y, 0, 128, None) == _lib.FP4_EUNSUPPORTED
+    assert lib.fp4_last_error().decode()
+
+
+def test_mxfp4_to_fp8_rejects_bad_arguments(lib):
+    P = ctypes.c_void_p(4096)
+    mx = lambda **kw: op(fmt=2, block=32, **kw)
+    assert lib.fp4_mxfp4_to_fp8(ctypes.byref(op()), 0, P, P, None) == _lib.FP4_EUNSUPPORTED       # not MXFP4
+    assert lib.fp4_mxfp4_to_fp8(ctypes.byref(mx(k=192)), 0, P, P, None) == _lib.FP4_EINVAL        # k % 128
+    assert lib.fp4_mxfp4_to_fp8(ctypes.byref(mx(rows=40)), 1, P, P, None) == _lib.FP4_EINVAL      # rows % 16
+    assert lib.fp4_mxfp4_to_fp8(ctypes.byref(mx()), 2, P, P, None) == _lib.FP4_EINVAL
+    assert lib.fp4_mxfp4_to_fp8(ctypes.byref(mx()), 0, None, P, None) == _lib.FP4_EINVAL
+    assert lib.fp4_mxfp4_to_fp8(ctypes.byref(mx()), 0, ctypes.c_void_p(4104), P, None) == _lib.FP4_EALIGN
     assert lib.fp4_last_error().decode()
