@@ -29,19 +29,24 @@ Pins (tests/test_oracle_*.py) and their strength:
 - MXFP4 -> FP8: E4M3 codes against torch's float8_e4m3fn cast, exact round trip of the
   values for blocks within 14 binades of their chunk's largest, the chunk scale rule and
   the 384 ceiling, hand-worked examples.
+- tile-local scales: one stripe equals global current scaling, a power-of-two rescale of
+  one stripe changes only that stripe's g, each stripe's largest block lands on T, and the
+  stripe-alpha GEMM against the float64 product within the model tolerance.
 """
-from . import formats, philox, hadamard, quantize, gemm, exact, fakequant, fp8convert
+from . import formats, philox, hadamard, quantize, gemm, exact, fakequant, fp8convert, local
 from .formats import UE5M3, E4M3, E8M0
 from .quantize import (AmaxCache, QuantResult, quantize_1d, quantize_2d, quantize_col, tensor_amax,
                        tensor_scales, pack_codes, unpack_codes, transposed_view)
 from .gemm import gemm_model, gemm_fp64, rtz_add_f32, operand_from_quant, output_scale, expand_2d_scales
 from .fakequant import dequantize, fake_quant, f32_to_bf16_bits, FakeQuantPolicy
 from .fp8convert import mxfp4_to_fp8, fp8_values
+from .local import LocalQuant, quantize_1d_local, stripe_alpha
 
 __all__ = [
-    "formats", "philox", "hadamard", "quantize", "gemm", "exact", "fakequant", "fp8convert",
+    "formats", "philox", "hadamard", "quantize", "gemm", "exact", "fakequant", "fp8convert", "local",
     "UE5M3", "E4M3", "E8M0", "AmaxCache", "QuantResult", "quantize_1d", "quantize_2d", "quantize_col",
     "tensor_amax", "tensor_scales", "pack_codes", "unpack_codes", "transposed_view",
     "gemm_model", "gemm_fp64", "rtz_add_f32", "operand_from_quant", "output_scale", "expand_2d_scales",
     "dequantize", "fake_quant", "f32_to_bf16_bits", "FakeQuantPolicy", "mxfp4_to_fp8", "fp8_values",
+    "LocalQuant", "quantize_1d_local", "stripe_alpha",
 ]
