@@ -20,7 +20,8 @@ UE5M3, E4M3, E8M0 = FP4_UE5M3, FP4_E4M3, FP4_E8M0
 ROW, COL, TILE2D = FP4_VIEW_ROW, FP4_VIEW_COL, FP4_VIEW_TILE2D
 
 __all__ = ["UE5M3", "E4M3", "E8M0", "ROW", "COL", "TILE2D", "QTensor", "AmaxCache", "quantize", "quantize_rowcol",
-           "fake_quant", "dequantize", "FakeQuantPolicy", "mxfp4_to_fp8", "tensor_amax",
+           "fake_quant", "dequantize", "FakeQuantPolicy", "mxfp4_to_fp8", "quantize_local",
+           "tensor_amax",
            "gemm_fprop", "gemm_dgrad", "gemm_wgrad", "debug_encode", "FP4Error", "library"]
 
 
@@ -53,10 +54,11 @@ class QTensor:
     layout: int              # FP4_SCALES_*
     rows: int
     k: int
+    g_stripe: int = 0        # 0: g holds one float; else one float per stripe of g_stripe rows
 
     def operand(self) -> _lib.Operand:
         return _lib.Operand(self.q.data_ptr(), self.s.data_ptr(), self.g.data_ptr(), self.fmt, self.block,
-                            self.layout, 0, self.rows, self.k)
+                            self.layout, self.g_stripe, self.rows, self.k)
 
 
 def _cfg(fmt, block, view, stochastic, hadamard_n, T, seed, offset) -> _lib.QuantCfg:
@@ -186,6 +188,26 @@ def dequantize(a: QTensor, out_dtype=torch.float32, out: torch.Tensor | None = N
     op = a.operand()
     _lib.check(lib.fp4_dequantize(ctypes.byref(op), _ptr(out), _out_dtype(out.dtype), out.stride(0), _stream()))
     return out
+
+
+def quantize_local(x: torch.Tensor, fmt: int = E4M3, block: int = 16, stripe: int = 16, T: float = 448.0,
+                   stochastic: bool = False, seed: int = 0, offset: int = 0,
+                   amax_obs: torch.Tensor | None = None) -> QTensor:
+    """fp4_quantize_local: ROW-view operand with one tensor scale per stripe of `stripe` rows
+    (its g holds ceil(rows / stripe) floats)."""
+    lib = _lib.load()
+    _dev_check(x, amax_obs)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    rows, cols = x.shape
+    dev = x.device
+    q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    s = torch.empty((rows, cols // block), dtype=torch.uint8, device=dev)
+    g = torch.empty(max(1, -(-rows // stripe)), dtype=torch.float32, device=dev)
+    cfg = _cfg(fmt, block, ROW, stochastic, 0, T, seed, offset)
+    _lib.check(lib.fp4_quantize_local(_ptr(x), _in_dtype(x), rows, cols, x.stride(0), ctypes.byref(cfg), int(stripe),
+                                      _ptr(q), _ptr(s), _ptr(g), _ptr(amax_obs), _stream()))
+    return QTensor(q, s, g, fmt, block, FP4_SCALES_1D, rows, cols, g_stripe=int(stripe))
 
 
 def mxfp4_to_fp8(a: QTensor, transpose: bool = False):

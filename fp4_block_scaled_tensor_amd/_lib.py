@@ -16,7 +16,7 @@ FP4_SCALES_1D, FP4_SCALES_2D, FP4_SCALES_2D_T = 0, 1, 2
 ABI_VERSION = 1
 
 EXPORTED = [
-    "fp4_quantize", "fp4_quantize_rowcol", "fp4_fake_quant", "fp4_dequantize", "fp4_mxfp4_to_fp8", "fp4_quantize_sizes", "fp4_tensor_amax", "amax_cache_update", "amax_cache_reset",
+    "fp4_quantize", "fp4_quantize_rowcol", "fp4_fake_quant", "fp4_dequantize", "fp4_mxfp4_to_fp8", "fp4_quantize_local", "fp4_quantize_sizes", "fp4_tensor_amax", "amax_cache_update", "amax_cache_reset",
     "fp4_gemm_fprop", "fp4_gemm_dgrad", "fp4_gemm_wgrad", "fp4_debug_encode", "fp4_last_error", "fp4_abi_version",
 ]
 
@@ -30,7 +30,7 @@ class QuantCfg(ctypes.Structure):
 class Operand(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("s", ctypes.c_void_p), ("g", ctypes.c_void_p),
                 ("fmt", ctypes.c_int32), ("block", ctypes.c_int32), ("scale_layout", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("rows", ctypes.c_int64), ("k", ctypes.c_int64)]
+                ("g_stripe", ctypes.c_int32), ("rows", ctypes.c_int64), ("k", ctypes.c_int64)]
 
 
 class AmaxCacheC(ctypes.Structure):
@@ -46,6 +46,8 @@ SIGNATURES = {
     "fp4_fake_quant": ([_P, _I32, _I64, _I64, _I64, ctypes.POINTER(QuantCfg), _P, _P, _I32, _I64, _P], ctypes.c_int),
     "fp4_dequantize": ([ctypes.POINTER(Operand), _P, _I32, _I64, _P], ctypes.c_int),
     "fp4_mxfp4_to_fp8": ([ctypes.POINTER(Operand), _I32, _P, _P, _P], ctypes.c_int),
+    "fp4_quantize_local": ([_P, _I32, _I64, _I64, _I64, ctypes.POINTER(QuantCfg), _I32, _P, _P, _P, _P, _P],
+                           ctypes.c_int),
     "fp4_quantize_sizes": ([_I64, _I64, ctypes.POINTER(QuantCfg), ctypes.POINTER(_SZ), ctypes.POINTER(_SZ),
                             ctypes.POINTER(_SZ)], ctypes.c_int),
     "fp4_tensor_amax": ([_P, _I32, _I64, _I64, _I64, _I32, _P, _P], ctypes.c_int),

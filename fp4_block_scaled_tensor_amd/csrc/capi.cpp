@@ -104,7 +104,23 @@ fp4_status check_operand(const fp4_operand* o, const char* name) {
     if (!aligned(o->s, 2)) return fail(FP4_EALIGN, "%s: scales not 2-byte aligned", name);
   }
   if (o->g && !aligned(o->g, 4)) return fail(FP4_EALIGN, "%s: g not 4-byte aligned", name);
+  if (o->g_stripe != 0) {
+    if (o->g_stripe != 16 && o->g_stripe != 32 && o->g_stripe != 64 && o->g_stripe != 128)
+      return fail(FP4_EINVAL, "%s: g_stripe must be 0, 16, 32, 64 or 128", name);
+    if (o->fmt == FP4_E8M0 || o->scale_layout != FP4_SCALES_1D)
+      return fail(FP4_EUNSUPPORTED, "%s: tile-local g needs UE5M3/E4M3 with 1D scales", name);
+    if (o->rows > 0 && !o->g) return fail(FP4_EINVAL, "%s: tile-local g needs the g array", name);
+  }
   return FP4_OK;
+}
+
+int stripe_shift(int32_t stripe) {
+  int k = 0;
+  while (stripe > 1) {
+    stripe >>= 1;
+    ++k;
+  }
+  return k;
 }
 
 fp4_status gemm_common(const fp4_operand* a, const fp4_operand* b, float* c, int32_t canon, int32_t hadamard_n,
@@ -121,8 +137,8 @@ fp4_status gemm_common(const fp4_operand* a, const fp4_operand* b, float* c, int
     if (!aligned(c, 16)) return fail(FP4_EALIGN, "%s: output not 16-byte aligned", what);
   }
   fp4k::GemmArgs g;
-  g.a = fp4k::GemmOperand{a->q, a->s, a->g, a->scale_layout, a->rows};
-  g.b = fp4k::GemmOperand{b->q, b->s, b->g, b->scale_layout, b->rows};
+  g.a = fp4k::GemmOperand{a->q, a->s, a->g, a->scale_layout, a->rows, a->g_stripe ? stripe_shift(a->g_stripe) : 0};
+  g.b = fp4k::GemmOperand{b->q, b->s, b->g, b->scale_layout, b->rows, b->g_stripe ? stripe_shift(b->g_stripe) : 0};
   g.fmt = a->fmt;
   g.block = a->block;
   g.M = a->rows;
@@ -344,6 +360,47 @@ fp4_status fp4_mxfp4_to_fp8(const fp4_operand* a, int32_t transpose, uint8_t* y,
   }
   return hip_status(fp4k::run_mx_to_fp8(a->q, a->s, a->rows, a->k, transpose != 0, y, s8, (hipStream_t)stream),
                     "fp4_mxfp4_to_fp8");
+}
+
+fp4_status fp4_quantize_local(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld,
+                              const fp4_quant_cfg* cfg, int32_t stripe, uint8_t* q, uint8_t* s, float* d_g,
+                              float* d_amax_obs, void* stream) {
+  fp4_status st;
+  if ((st = check_cfg(cfg)) != FP4_OK) return st;
+  if (cfg->view != FP4_VIEW_ROW) return fail(FP4_EUNSUPPORTED, "quantize_local: ROW view only");
+  if (cfg->fmt == FP4_E8M0) return fail(FP4_EUNSUPPORTED, "quantize_local: UE5M3 or E4M3 (E8M0 has no tensor scale)");
+  if (stripe != 16 && stripe != 32 && stripe != 64 && stripe != 128)
+    return fail(FP4_EINVAL, "quantize_local: stripe must be 16, 32, 64 or 128");
+  if ((st = check_shape(rows, cols, cfg)) != FP4_OK) return st;
+  if (x_dtype != FP4_IN_BF16 && x_dtype != FP4_IN_FP32) return fail(FP4_EINVAL, "unknown input dtype %d", x_dtype);
+  const int64_t esz = x_dtype == FP4_IN_FP32 ? 4 : 2;
+  if (ld < cols) return fail(FP4_EINVAL, "ld (%lld) < cols (%lld)", (long long)ld, (long long)cols);
+  if (rows > 0 && cols > 0) {
+    if (!x || !q || !s || !d_g) return fail(FP4_EINVAL, "NULL x, q, s or d_g");
+    if (!aligned(x, 16) || !aligned(q, 16)) return fail(FP4_EALIGN, "x and q must be 16-byte aligned");
+    if ((ld * esz) % 16) return fail(FP4_EALIGN, "row stride must be a multiple of 16 bytes");
+  }
+  if ((d_g && !aligned(d_g, 4)) || (d_amax_obs && !aligned(d_amax_obs, 4)))
+    return fail(FP4_EALIGN, "g / amax pointers must be 4-byte aligned");
+  fp4k::LocalQuantArgs a;
+  a.x = x;
+  a.f32 = x_dtype == FP4_IN_FP32;
+  a.rows = rows;
+  a.cols = cols;
+  a.ld = ld;
+  a.fmt = cfg->fmt;
+  a.block = cfg->block;
+  a.stripe_log2 = stripe_shift(stripe);
+  a.stochastic = cfg->stochastic != 0;
+  a.T = cfg->T;
+  a.seed = cfg->seed;
+  a.offset = cfg->offset;
+  a.q = q;
+  a.s = s;
+  a.g = d_g;
+  a.amax = d_amax_obs;
+  a.stream = (hipStream_t)stream;
+  return hip_status(fp4k::run_quantize_local(a), "fp4_quantize_local");
 }
 
 fp4_status fp4_tensor_amax(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld, int32_t hadamard_n,

@@ -150,8 +150,7 @@ __device__ __forceinline__ void philox_u16x8(uint64_t blk8, uint64_t seed, uint6
 // ---- tensor scales from the cached amax (float32, nearest-even) ----
 struct TensorScales { float s_enc, s_blk, g; };
 
-__device__ __forceinline__ TensorScales tensor_scales(const float* d_amax, float T) {
-  const float A = d_amax ? *d_amax : 0.0f;
+__device__ __forceinline__ TensorScales tensor_scales_from(float A, float T) {
   TensorScales ts{1.0f, 1.0f, 1.0f};
   if (A > 0.0f && A <= 3.4028234663852886e38f) {
     const float se = (6.0f * T) / A;
@@ -162,6 +161,10 @@ __device__ __forceinline__ TensorScales tensor_scales(const float* d_amax, float
     }
   }
   return ts;
+}
+
+__device__ __forceinline__ TensorScales tensor_scales(const float* d_amax, float T) {
+  return tensor_scales_from(d_amax ? *d_amax : 0.0f, T);
 }
 
 // ---- FP32 round-mode control (MODE register bits [1:0]; [3:2] = f64/f16 stay nearest) ----

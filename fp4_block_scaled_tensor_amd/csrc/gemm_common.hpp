@@ -180,36 +180,63 @@ __device__ __forceinline__ int tile_row(int r, int l) { return (r >> 2) * 8 + (l
 // Epilogue: nearest-even mode, optional canonicalisation, scale by alpha, store float32.
 // (m0, n0) is the wave's first output row and column; tile (i, j) covers rows m0 + 32i and
 // columns n0 + 32j. pre (a power of two) undoes a constant factor the K loop carried; it is
-// exact and applied before the canonicalisation.
+// exact and applied before the canonicalisation. epi: bits 0-7 Hadamard n; bits 8-15 / 16-23
+// the log2 stripe height of A's / B's tile-local g (0: one g for the operand), in which case
+// alpha = float32(g_a[row >> sa] * g_b[col >> sb]) per output.
 template <int TM, int TN>
 __device__ __forceinline__ void store_tiles(float* __restrict__ c, int64_t M, int64_t N, int64_t m0, int64_t n0,
                                             v16f (&acc)[TM][TN], const float* ga, const float* gb, int canon,
-                                            int hadamard_n, float pre = 1.0f) {
+                                            int epi, float pre = 1.0f) {
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) pin(acc[i][j]);   // accumulation done before the switch
   mode_f32_rne();
-  float a = ga ? *ga : 1.0f;
-  float b = gb ? *gb : 1.0f;
-  asm volatile("" : "+v"(a), "+v"(b));        // keep the scale product after the mode switch
-  float alpha = a * b;
-  if (hadamard_n) alpha = alpha * (1.0f / (float)hadamard_n);
+  const int hadamard_n = epi & 0xFF, sa = (epi >> 8) & 0xFF, sb = (epi >> 16) & 0xFF;
+  const float hinv = hadamard_n ? 1.0f / (float)hadamard_n : 1.0f;
   const int l = threadIdx.x & 63;
+  if (sa == 0 && sb == 0) {
+    float a = ga ? *ga : 1.0f;
+    float b = gb ? *gb : 1.0f;
+    asm volatile("" : "+v"(a), "+v"(b));        // keep the scale product after the mode switch
+    float alpha = a * b;
+    if (hadamard_n) alpha = alpha * hinv;
 #pragma unroll
-  for (int rt = 0; rt < TM; ++rt)
+    for (int rt = 0; rt < TM; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < TN; ++ct) {
-      const int64_t col = n0 + ct * 32 + (l & 31);
+      for (int ct = 0; ct < TN; ++ct) {
+        const int64_t col = n0 + ct * 32 + (l & 31);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + rt * 32 + tile_row(r, l);
-        float v = acc[rt][ct][r] * pre;
-        if (canon) v = __builtin_rintf(v * 1024.0f) * (1.0f / 1024.0f);
-        v = v * alpha;
-        if (row < M && col < N) c[row * N + col] = v;
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + rt * 32 + tile_row(r, l);
+          float v = acc[rt][ct][r] * pre;
+          if (canon) v = __builtin_rintf(v * 1024.0f) * (1.0f / 1024.0f);
+          v = v * alpha;
+          if (row < M && col < N) c[row * N + col] = v;
+        }
       }
-    }
+  } else {
+    const float a0 = ga ? *ga : 1.0f, b0 = gb ? *gb : 1.0f;
+#pragma unroll
+    for (int rt = 0; rt < TM; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < TN; ++ct) {
+        const int64_t col = n0 + ct * 32 + (l & 31);
+        float b = (sb && col < N) ? gb[col >> sb] : b0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + rt * 32 + tile_row(r, l);
+          float a = (sa && row < M) ? ga[row >> sa] : a0;
+          asm volatile("" : "+v"(a), "+v"(b));    // after the mode switch
+          float alpha = a * b;
+          if (hadamard_n) alpha = alpha * hinv;
+          float v = acc[rt][ct][r] * pre;
+          if (canon) v = __builtin_rintf(v * 1024.0f) * (1.0f / 1024.0f);
+          v = v * alpha;
+          if (row < M && col < N) c[row * N + col] = v;
+        }
+      }
+  }
 }
 
 }  // namespace fp4k

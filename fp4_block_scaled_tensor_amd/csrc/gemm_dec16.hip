@@ -94,7 +94,7 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
                                                        const uint8_t* __restrict__ sb, int lb,
                                                        const float* __restrict__ ga, const float* __restrict__ gb,
                                                        float* __restrict__ c, int64_t M, int64_t N, int64_t K,
-                                                       int canon, int hadamard_n) {
+                                                       int canon, int epi) {
   using TL = DecTiling;
   constexpr int GT = TL::BM;        // == TL::BN
   __shared__ __attribute__((aligned(1024))) uint8_t lA[2][TL::BM * ROWB];
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
       __syncthreads();
     }
   }
-  store_tiles<2, 2>(c, M, N, m0 + wm * 64, n0 + wn * 64, acc, ga, gb, canon, hadamard_n, 64.0f);   // undo 2^-3 x 2^-3
+  store_tiles<2, 2>(c, M, N, m0 + wm * 64, n0 + wn * 64, acc, ga, gb, canon, epi, 64.0f);   // undo 2^-3 x 2^-3
 }
 
 template <int FMT, int B>
@@ -209,7 +209,8 @@ static hipError_t launch_dec16(const GemmArgs& g) {
   using TL = DecTiling;
   const int64_t tiles = ((g.M + TL::BM - 1) / TL::BM) * ((g.N + TL::BN - 1) / TL::BN);
   hipLaunchKernelGGL((k_gemm_dec16<FMT, B>), dim3((unsigned)tiles), dim3(TL::NT), 0, g.stream, g.a.q, g.a.s, g.a.layout,
-                     g.b.q, g.b.s, g.b.layout, g.a.g, g.b.g, g.c, g.M, g.N, g.K, g.canon, g.hadamard_n);
+                     g.b.q, g.b.s, g.b.layout, g.a.g, g.b.g, g.c, g.M, g.N, g.K, g.canon,
+                     epilogue_word(g.hadamard_n, g.a.g_shift, g.b.g_shift));
   return hipGetLastError();
 }
 

@@ -244,7 +244,7 @@ template <class TL>
 __global__ __launch_bounds__(TL::NT, FP4_MX_MINB) void k_gemm_mx(
     const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const uint8_t* __restrict__ qb,
     const uint8_t* __restrict__ sb, const float* __restrict__ ga, const float* __restrict__ gb, float* __restrict__ c,
-    int64_t M, int64_t N, int64_t K, int canon, int hadamard_n) {
+    int64_t M, int64_t N, int64_t K, int canon, int epi) {
   constexpr int TM = TL::TM, TN = TL::TN, BM = TL::BM, BN = TL::BN, NR = BM + BN;
   static_assert(TL::NT >= NR && BM % 64 == 0 && BN % 64 == 0, "one thread per staged scale row, whole waves");
   __shared__ __attribute__((aligned(1024))) MxSmem<TL> sm;
@@ -363,7 +363,7 @@ __global__ __launch_bounds__(TL::NT, FP4_MX_MINB) void k_gemm_mx(
       __syncthreads();
     }
   }
-  store_tiles<TM, TN>(c, M, N, m0 + wm * (TM * 32), n0 + wn * (TN * 32), acc, ga, gb, canon, hadamard_n);
+  store_tiles<TM, TN>(c, M, N, m0 + wm * (TM * 32), n0 + wn * (TN * 32), acc, ga, gb, canon, epi);
 }
 
 #ifndef FP4_MX_TILING
@@ -376,7 +376,8 @@ hipError_t run_gemm_mx(const GemmArgs& g) {
   using TL = MxTiling;
   const int64_t tiles = ((g.M + TL::BM - 1) / TL::BM) * ((g.N + TL::BN - 1) / TL::BN);
   hipLaunchKernelGGL(k_gemm_mx<TL>, dim3((unsigned)tiles), dim3(TL::NT), 0, g.stream, g.a.q, g.a.s, g.b.q, g.b.s,
-                     g.a.g, g.b.g, g.c, g.M, g.N, g.K, g.canon, g.hadamard_n);
+                     g.a.g, g.b.g, g.c, g.M, g.N, g.K, g.canon,
+                     epilogue_word(g.hadamard_n, g.a.g_shift, g.b.g_shift));
   return hipGetLastError();
 }
 

@@ -27,7 +27,14 @@ struct GemmOperand {
   const float* g;
   int layout;        // 0: 1D, 1: 2D forward view, 2: 2D transposed view
   int64_t rows;
+  int g_shift;       // 0: g is one float; k > 0: g[row >> k] (tile-local scales, stripes of 2^k rows)
 };
+
+// Epilogue word passed to the GEMM kernels: bits 0-7 Hadamard n (0, 16, 32), bits 8-15 and
+// 16-23 the A and B operands' g_shift.
+inline int epilogue_word(int hadamard_n, int a_shift, int b_shift) {
+  return hadamard_n | (a_shift << 8) | (b_shift << 16);
+}
 
 struct GemmArgs {
   GemmOperand a, b;
@@ -89,6 +96,24 @@ struct DequantArgs {
   hipStream_t stream;
 };
 hipError_t run_dequantize(const DequantArgs& a);
+
+// ROW-view quantization with one tensor scale per stripe of 2^stripe_log2 rows (current
+// scaling from the stripe's own amax).
+struct LocalQuantArgs {
+  const void* x;
+  bool f32;
+  int64_t rows, cols, ld;
+  int fmt, block, stripe_log2;
+  bool stochastic;
+  float T;
+  uint64_t seed, offset;
+  uint8_t* q;
+  uint8_t* s;
+  float* g;          // [ceil(rows / stripe)]
+  float* amax;       // optional, [ceil(rows / stripe)]
+  hipStream_t stream;
+};
+hipError_t run_quantize_local(const LocalQuantArgs& a);
 
 // MXFP4 operand [rows x K] -> E4M3 [rows x K] or [K x rows] plus chunk scales [rows x K/128].
 hipError_t run_mx_to_fp8(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t K, bool transpose, uint8_t* y,

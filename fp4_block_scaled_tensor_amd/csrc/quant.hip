@@ -398,6 +398,70 @@ __global__ __launch_bounds__(NT) void k_quant_rowcol(const void* __restrict__ x,
   if (obs_c) wg_max_to(obs_c, ocol);
 }
 
+// ---------------------------------------------------------------- ROW view, tile-local scales
+// "Format-Aware Fusion for Fast FP4 Pretraining", abstract: a cooperative-thread-array-local
+// NVFP4 scale domain. One workgroup owns a stripe of 2^stripe_log2 rows across all columns:
+// it reduces the stripe's amax (current scaling, no global pass), derives the stripe's
+// tensor scales from it with the global-scale arithmetic, then quantizes the stripe's
+// blocks (the second read of the stripe is served by the L2).
+template <int FMT, int B, bool SR, bool F32>
+__global__ __launch_bounds__(NT) void k_quant_row_local(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                        int64_t ld, int stripe_log2, float T, uint64_t seed,
+                                                        uint64_t offset, uint8_t* __restrict__ q,
+                                                        uint8_t* __restrict__ s, float* __restrict__ g_out,
+                                                        float* __restrict__ amax_out) {
+  __shared__ float part[NT / 64];
+  const int64_t r0 = (int64_t)blockIdx.x << stripe_log2;
+  const int64_t nr = min((int64_t)1 << stripe_log2, rows - r0);
+  const int64_t chunks = cols / 8;                 // 8-element chunks per row
+  // stripe amax: UL chunks per thread in flight per step
+  constexpr int UL = 8;
+  float m = 0.0f;
+  const int64_t nch = nr * chunks;
+  for (int64_t c0 = threadIdx.x; c0 < nch; c0 += UL * NT) {
+    float v[UL][8];
+#pragma unroll
+    for (int u = 0; u < UL; ++u) {
+      int64_t c = c0 + u * NT;
+      c = c < nch ? c : nch - 1;                     // clamped: a repeated chunk does not change the max
+      const int64_t r = c / chunks, k = (c - r * chunks) * 8;
+      load8<F32>(x, (r0 + r) * ld + k, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < UL; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[u][j]));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float A = part[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) A = fmaxf(A, part[i]);
+  const TensorScales ts = tensor_scales_from(A, T);
+  if (threadIdx.x == 0) {
+    g_out[blockIdx.x] = ts.g;
+    if (amax_out) amax_out[blockIdx.x] = A;
+  }
+  // the stripe's blocks, UB per thread in flight per step
+  constexpr int UB = 64 / B;
+  const int64_t nb = cols / B, nblk = nr * nb;
+  for (int64_t i0 = threadIdx.x; i0 < nblk; i0 += UB * NT) {
+    float v[UB][B];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      int64_t i = i0 + u * NT;
+      i = i < nblk ? i : nblk - 1;
+      load_block<B, F32>(x, (r0 + i / nb) * ld + (i % nb) * B, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int64_t i = i0 + u * NT;
+      if (i < nblk) quant_block_row<FMT, B, SR>(v[u], ts, r0 + i / nb, i % nb, cols, seed, offset, q, s);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- TILE2D (weights)
 constexpr int WT = 64;   // 64x64 weight tile per workgroup
 
@@ -607,6 +671,26 @@ hipError_t run_quantize_rowcol(const RowColArgs& a) {
     return e;
   }
   return a.f32 ? rowcol_fmt<true>(a) : rowcol_fmt<false>(a);
+}
+
+template <int FMT, int B, bool SR, bool F32>
+static hipError_t launch_local(const LocalQuantArgs& a) {
+  const int64_t stripes = (a.rows + ((int64_t)1 << a.stripe_log2) - 1) >> a.stripe_log2;
+  hipLaunchKernelGGL((k_quant_row_local<FMT, B, SR, F32>), dim3((unsigned)stripes), dim3(NT), 0, a.stream, a.x,
+                     a.rows, a.cols, a.ld, a.stripe_log2, a.T, a.seed, a.offset, a.q, a.s, a.g, a.amax);
+  return hipGetLastError();
+}
+
+template <int FMT, int B>
+static hipError_t local_types(const LocalQuantArgs& a) {
+  if (a.stochastic) return a.f32 ? launch_local<FMT, B, true, true>(a) : launch_local<FMT, B, true, false>(a);
+  return a.f32 ? launch_local<FMT, B, false, true>(a) : launch_local<FMT, B, false, false>(a);
+}
+
+hipError_t run_quantize_local(const LocalQuantArgs& a) {
+  if (a.rows == 0 || a.cols == 0) return hipSuccess;
+  if (a.fmt == FMT_UE5M3) return a.block == 16 ? local_types<FMT_UE5M3, 16>(a) : local_types<FMT_UE5M3, 32>(a);
+  return a.block == 16 ? local_types<FMT_E4M3, 16>(a) : local_types<FMT_E4M3, 32>(a);
 }
 
 template <int FMT, bool F32>

@@ -96,11 +96,14 @@ typedef struct {
 typedef struct {
   const uint8_t* q;    /* device, packed E2M1 [rows x k/2] */
   const uint8_t* s;    /* device, scale codes, layout per scale_layout */
-  const float* g;      /* device, tensor decode scale (1 float); NULL means 1.0 */
+  const float* g;      /* device, tensor decode scale (1 float); NULL means 1.0. With
+                          g_stripe > 0: one float per stripe of g_stripe rows */
   int32_t fmt;         /* fp4_scale_fmt */
   int32_t block;       /* 16 or 32 */
   int32_t scale_layout;/* fp4_scale_layout */
-  int32_t reserved;
+  int32_t g_stripe;    /* 0: one tensor scale; 16, 32, 64 or 128: tile-local scales, row r of
+                          the operand uses g[r / g_stripe] (fp4_quantize_local; UE5M3/E4M3
+                          with 1D scales only) [FUSION abstract: CTA-local NVFP4] */
   int64_t rows;        /* M (or N) */
   int64_t k;           /* contraction length; multiple of 64 */
 } fp4_operand;
@@ -208,6 +211,24 @@ fp4_status fp4_dequantize(const fp4_operand* a, void* y, int32_t y_dtype, int64_
  */
 fp4_status fp4_mxfp4_to_fp8(const fp4_operand* a, int32_t transpose, uint8_t* y, uint8_t* s8, void* stream);
 
+/*
+ * fp4_quantize_local - ROW-view quantization with tile-local tensor scales [FUSION abstract:
+ * cooperative-thread-array-local NVFP4 scale domain]: the rows are cut into stripes of
+ * 2^k = stripe rows (16, 32, 64 or 128; the last may be shorter), each spanning all cols; a
+ * stripe's tensor scales come from its own amax (current scaling, no cached amax and no
+ * global pass) with the fp4_quantize arithmetic and cfg->T; codes and scales are laid out
+ * as for FP4_VIEW_ROW.
+ *   cfg      view FP4_VIEW_ROW, fmt FP4_UE5M3 or FP4_E4M3, block 16 or 32, hadamard_n 0;
+ *            stochastic rounding allowed
+ *   q, s     as fp4_quantize ROW
+ *   d_g      device float[ceil(rows / stripe)]: each stripe's decode scale g
+ *   d_amax_obs  optional device float[ceil(rows / stripe)]: each stripe's amax
+ * The GEMMs take the result as an operand with g = d_g and g_stripe = stripe.
+ */
+fp4_status fp4_quantize_local(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld,
+                              const fp4_quant_cfg* cfg, int32_t stripe, uint8_t* q, uint8_t* s, float* d_g,
+                              float* d_amax_obs, void* stream);
+
 /* fp4_quantize_sizes - byte sizes of q, s and q_t for a call with these arguments (host only). */
 fp4_status fp4_quantize_sizes(int64_t rows, int64_t cols, const fp4_quant_cfg* cfg,
                               size_t* q_bytes, size_t* s_bytes, size_t* qt_bytes);
@@ -238,7 +259,8 @@ fp4_status amax_cache_reset(const fp4_amax_cache* cache, void* stream);
  *   group's partials are added in K order in float32 with round-to-nearest-even; groups
  *   are accumulated in K order with float32 round-toward-zero; optionally the result is
  *   canonicalised to round_half_even(1024 c)/1024 (canon != 0); finally
- *   c = acc * float32(g_a * g_b) [* 1/hadamard_n for wgrad], rounded to nearest-even.
+ *   c = acc * float32(g_a * g_b) [* 1/hadamard_n for wgrad], rounded to nearest-even; with
+ *   tile-local operands g_a = a->g[m / a->g_stripe], g_b = b->g[n / b->g_stripe].
  * Exact results require every block partial and group sum to stay inside the float32
  * normal range (always true for UE5M3/E4M3; for E8M0, combined block exponents within
  * about +-100).

@@ -38,8 +38,10 @@ class LocalQuant:
     stripe: int
 
 
-def quantize_1d_local(x: np.ndarray, fmt: int, block: int, stripe: int = 16, T: float = 448.0) -> LocalQuant:
-    """ROW-view quantization of x [rows, K] with one tensor scale per stripe of rows."""
+def quantize_1d_local(x: np.ndarray, fmt: int, block: int, stripe: int = 16, T: float = 448.0,
+                      rounding: str = "rne", seed: int = 0, offset: int = 0) -> LocalQuant:
+    """ROW-view quantization of x [rows, K] with one tensor scale per stripe of rows.
+    Stochastic rounding draws by the logical element index in the whole operand."""
     if stripe not in STRIPES:
         raise ValueError("stripe must be 16, 32, 64 or 128")
     x = np.asarray(x, dtype=np.float32)
@@ -52,7 +54,8 @@ def quantize_1d_local(x: np.ndarray, fmt: int, block: int, stripe: int = 16, T: 
     for i in range(n):
         rows = slice(i * stripe, min(R, (i + 1) * stripe))
         amax[i] = tensor_amax(x[rows])
-        qr = quantize_1d(x[rows], fmt, block, amax=amax[i], T=T)
+        qr = quantize_1d(x[rows], fmt, block, amax=amax[i], T=T, rounding=rounding, seed=seed, offset=offset,
+                         row0=i * stripe)
         codes[rows], scales[rows], g[i] = qr.codes, qr.scales, qr.g
     return LocalQuant(codes, scales, g, amax, fmt, block, stripe)
 

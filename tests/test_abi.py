@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_and_binding_agree():
     decl = declared_functions()
     assert set(decl) == set(_lib.EXPORTED), decl
-    assert len(decl) == 15
+    assert len(decl) == 16
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -199,3 +199,20 @@ def test_mxfp4_to_fp8_rejects_bad_arguments(lib):
     assert lib.fp4_mxfp4_to_fp8(ctypes.byref(mx()), 0, None, P, None) == _lib.FP4_EINVAL
     assert lib.fp4_mxfp4_to_fp8(ctypes.byref(mx()), 0, ctypes.c_void_p(4104), P, None) == _lib.FP4_EALIGN
     assert lib.fp4_last_error().decode()
+
+
+def test_quantize_local_and_stripe_operands_reject_bad_arguments(lib):
+    P = ctypes.c_void_p(4096)
+    ql = lambda c, stripe=16, rows=64, cols=64: lib.fp4_quantize_local(P, 0, rows, cols, cols, ctypes.byref(c), stripe,
+                                                                        P, P, P, None, None)
+    assert ql(cfg(fmt=1), stripe=8) == _lib.FP4_EINVAL
+    assert ql(cfg(fmt=2, block=32)) == _lib.FP4_EUNSUPPORTED        # E8M0 has no tensor scale
+    assert ql(cfg(fmt=1, view=1)) == _lib.FP4_EUNSUPPORTED          # ROW view only
+    assert ql(cfg(fmt=1), cols=40) == _lib.FP4_EINVAL               # cols % B
+    y = ctypes.c_void_p(4096)
+    a = _lib.Operand(4096, 4096, 4096, 1, 16, 0, 24, 64, 128)       # g_stripe 24
+    assert lib.fp4_gemm_fprop(ctypes.byref(a), ctypes.byref(op(fmt=1)), y, 0, None) == _lib.FP4_EINVAL
+    a = _lib.Operand(4096, 4096, 4096, 2, 32, 0, 16, 64, 128)       # MXFP4 with a stripe g
+    assert lib.fp4_gemm_fprop(ctypes.byref(a), ctypes.byref(op(fmt=2, block=32)), y, 0, None) == _lib.FP4_EUNSUPPORTED
+    a = _lib.Operand(4096, 4096, None, 1, 16, 0, 32, 64, 128)       # stripe g without the array
+    assert lib.fp4_gemm_fprop(ctypes.byref(a), ctypes.byref(op(fmt=1)), y, 0, None) == _lib.FP4_EINVAL
