@@ -16,7 +16,9 @@ the launch stream. ``traffic`` is the HBM bytes per GEMM launch from the FETCH_S
 WRITE_SIZE counters, scaled by the counters' reading for a plain device copy of known
 size; it is read from the profile summary under ``profiles/`` and is null when the GEMM
 kernel sources changed since those counters were taken. ``quantizer`` is the row-view
-activation quantizer's algorithmic GB/s against HBM peak. ``cpu_baseline`` times the CPU
+activation quantizer's algorithmic GB/s against HBM peak; ``quantizer_rowcol`` the fused
+ROW+COL quantizer's; ``next_rows`` the graph-timed fake-quant, decode, MXFP4->FP8 and
+tile-local quantizer kernels on the same activation. ``cpu_baseline`` times the CPU
 oracle on a bounded slice of the same workload. ``--calib-copy-mib N`` runs one plain
 N-MiB device copy before warm-up, the known-size reference for the byte counters.
 """
@@ -202,6 +204,43 @@ def graph_time_ms(torch, fn, check, reps=20):
     return best, ok
 
 
+def next_rows(torch, fp4, Xd, step_obj, args):
+    """Graph-timed kernels of the rows built past the training step, on the same 8192x4096
+    activation: inference fake quantization (bf16 out) and operand decode, MXFP4 -> FP8
+    (transposed, the backward form), tile-local quantization (E4M3, 16-row stripes). Each
+    entry: algorithmic bytes per element, average ms, GB/s and fraction of HBM peak."""
+    n = M_TOK * K_IN
+    fmt, B = step_obj.fmt, step_obj.block
+    amax = None if fmt == fp4.E8M0 else step_obj.c_x.amax
+    q_row = fp4.quantize(Xd, fmt, B, fp4.ROW, amax=amax, T=448)
+    q_mx = fp4.quantize(Xd, fp4.E8M0, 32, fp4.ROW)
+    torch.cuda.synchronize()
+    cases = {
+        "fake_quant": ("k_fake_quant (bf16 in, bf16 out)", 4.0,
+                       lambda: fp4.fake_quant(Xd, fmt, B, amax=amax, T=448, out_dtype=torch.bfloat16),
+                       lambda a, b: torch.equal(a.view(torch.int16), b.view(torch.int16))),
+        "dequantize": ("k_dequant (bf16 out)", 0.5 + 1.0 / B + 2.0,
+                       lambda: fp4.dequantize(q_row, out_dtype=torch.bfloat16),
+                       lambda a, b: torch.equal(a.view(torch.int16), b.view(torch.int16))),
+        "mxfp4_to_fp8": ("k_mx_to_fp8 (transposed out)", 0.5 + 1.0 / 32 + 1.0 + 1.0 / 128,
+                         lambda: fp4.mxfp4_to_fp8(q_mx, transpose=True),
+                         lambda a, b: torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])),
+        "quantize_local": ("k_quant_row_local (E4M3, 16-row stripes)", 2.0 + 0.5 + 1.0 / 16,
+                           lambda: fp4.quantize_local(Xd, fp4.E4M3, 16, stripe=16),
+                           lambda a, b: torch.equal(a.q, b.q) and torch.equal(a.s, b.s) and torch.equal(a.g, b.g)),
+    }
+    out = {}
+    for name, (kernel, bpe, fn, same) in cases.items():
+        ref = fn()
+        torch.cuda.synchronize()
+        ms, ok = graph_time_ms(torch, fn, lambda o: same(o, ref))
+        gbs = n * bpe / (ms * 1e-3) / 1e9
+        out[name] = {"kernel": kernel, "bytes_per_elem": round(bpe, 6), "avg_ms": round(ms, 4),
+                     "achieved": round(gbs, 1), "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "replay_matches_eager": ok}
+    return out
+
+
 def bf16_device(torch, synth, x):
     bits = synth.f32_to_bf16_bits(x)
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
@@ -309,6 +348,7 @@ def main():
     rc_ms, rc_ok = graph_time_ms(torch, rcfn, same_rc)
     rc_bpe = 2 + 2 * (0.5 + 1.0 / step_obj.block)
     rc_gbs = M_TOK * K_IN * rc_bpe / (rc_ms * 1e-3) / 1e9
+    extra = next_rows(torch, fp4, Xd, step_obj, args)
     flop_gemm = 2.0 * M_TOK * N_OUT * K_IN
     step_flops = 3 * flop_gemm
     value = step_flops / (ms_step * 1e-3) / 1e12
@@ -348,6 +388,7 @@ def main():
                              "frac": round(rc_gbs / HBM_PEAK_GBS, 4), "bytes_per_elem": rc_bpe,
                              "avg_ms": round(rc_ms, 4), "replay_matches_eager": rc_ok,
                              "in_step_avg_ms": None if args.separate else round(quant_ms_step, 4)},
+        "next_rows": extra,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:
