@@ -148,8 +148,11 @@ class LinearStep:
             e1.record()
             self.evq.append((e0, e1))
         if E8:
-            qw = fp4.quantize(self.W, self.fmt, B, fp4.ROW)
-            qwt = fp4.quantize(self.W, self.fmt, B, fp4.COL)          # W^T, blocks along out-features
+            if self.fused:   # W for fprop and W^T (blocks along out-features) for dgrad, one read
+                qw, qwt = fp4.quantize_rowcol(self.W, self.fmt, B)
+            else:
+                qw = fp4.quantize(self.W, self.fmt, B, fp4.ROW)
+                qwt = fp4.quantize(self.W, self.fmt, B, fp4.COL)
         else:
             qw, qwt = fp4.quantize(self.W, self.fmt, 16, fp4.TILE2D, amax=self.c_w.amax, T=448)
         self._timed(timed, fp4.gemm_fprop, qx, qw, out=self.Y)

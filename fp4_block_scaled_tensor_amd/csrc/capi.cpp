@@ -97,6 +97,8 @@ fp4_status check_operand(const fp4_operand* o, const char* name) {
   if (o->scale_layout != FP4_SCALES_1D) {
     if (o->fmt == FP4_E8M0 || o->block != 16) return fail(FP4_EUNSUPPORTED, "%s: 2D scales need UE5M3/E4M3 block 16", name);
     if (o->rows % 16) return fail(FP4_EINVAL, "%s: 2D-scaled operand rows must be a multiple of 16", name);
+    if ((o->rows / 16) * (o->k / 16) >= (int64_t(1) << 32))
+      return fail(FP4_EUNSUPPORTED, "%s: 2D scale grid of 2^32 codes or more", name);
   }
   if (o->rows > 0 && o->k > 0) {
     if (!o->q || !o->s) return fail(FP4_EINVAL, "%s: NULL payload or scales", name);

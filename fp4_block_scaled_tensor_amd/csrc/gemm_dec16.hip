@@ -27,18 +27,31 @@ namespace fp4k {
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
-// The decode factors of scale value S = M 2^E: 2^(E-3) as float (for the convert) and M as a
-// packed fp16 pair (for the multiply). S is a normal float32 for every UE5M3/E4M3 code.
+// The decode factors of a scale code, straight from its bit fields: a normal code (exponent
+// field e >= 1, mantissa m) has S = (1 + m/8) 2^(e - bias), giving 2^(e - bias - 3) as float
+// (for the convert) and 1 + m/8 as a packed fp16 pair (for the multiply); a subnormal code
+// has S = m q_s (q_s the subnormal quantum, 2^-17 for UE5M3, 2^-9 for E4M3), giving
+// q_s 2^-3 and m itself (0..7, exact in fp16; code 0 decodes every value to zero).
 struct DecScale {
   float p2;
   v2h m2;
 };
-__device__ __forceinline__ DecScale dec_factors(float S) {
-  const uint32_t b = __float_as_uint(S);
+template <int FMT>
+__device__ __forceinline__ DecScale dec_factors_code(uint32_t c) {
+  constexpr int SUB_EXP = FMT == FMT_UE5M3 ? 17 : 9;   // log2 of 1 / subnormal quantum
+  const uint32_t e = c >> 3, m = c & 7u;
   DecScale d;
-  d.p2 = __uint_as_float((b & 0x7F800000u) - (3u << 23));
-  const _Float16 m = (_Float16)__uint_as_float((b & 0x007FFFFFu) | 0x3F800000u);   // exact
-  d.m2 = v2h{m, m};
+  uint32_t h;
+  if (e != 0) {
+    d.p2 = __uint_as_float((e + (uint32_t)(127 - ScaleFmt<FMT>::BIAS - 3)) << 23);
+    h = 0x3C00u | (m << 7);                                  // fp16 1 + m/8
+  } else {
+    d.p2 = __uint_as_float((uint32_t)(127 - SUB_EXP - 3) << 23);
+    const _Float16 mh = (_Float16)(float)m;                  // exact
+    h = (uint32_t)__builtin_bit_cast(uint16_t, mh);
+  }
+  const uint32_t hh = h | (h << 16);
+  d.m2 = __builtin_bit_cast(v2h, hh);
   return d;
 }
 
@@ -56,25 +69,50 @@ __device__ __forceinline__ v8h decode8(uint32_t codes, const DecScale& d) {
 
 // The 16 scale codes (one per 16-wide K slice; block 32 repeats each code twice) of one
 // operand row for stage st, in the operand's scale layout. Rows past the matrix and slices
-// past K get the code of 1.0.
+// past K get the code of 1.0. With al (scale array 16-byte aligned, K % 256 == 0) a whole
+// stage of a 1D or forward-2D row is one 16-byte load (block 32: one 8-byte load, each code
+// doubled with v_perm); the transposed 2D layout, whose codes are strided, and a partial last
+// stage read byte by byte.
 template <int FMT, int B>
 __device__ __forceinline__ uint4 scale_row16(const uint8_t* __restrict__ s, int layout, int64_t row, int64_t rows,
-                                             int64_t K, int64_t st) {
+                                             int64_t K, int64_t st, bool al) {
   const uint32_t one = ScaleFmt<FMT>::ONE;
   if (row >= rows) {
     const uint32_t w = one * 0x01010101u;
     return make_uint4(w, w, w, w);
   }
   const int64_t k16 = K / 16;        // 16-wide slices per row
+  if (al && layout != 2 && (st + 1) * 16 <= k16) {
+    if (layout == 1 || B == 16) {
+      const int64_t base = layout == 1 ? (row >> 4) * k16 : row * k16;
+      return *reinterpret_cast<const uint4*>(s + base + st * 16);
+    }
+    const uint2 v = *reinterpret_cast<const uint2*>(s + row * (K / 32) + st * 8);
+    return make_uint4(__builtin_amdgcn_perm(v.x, v.x, 0x01010000u), __builtin_amdgcn_perm(v.x, v.x, 0x03030202u),
+                      __builtin_amdgcn_perm(v.y, v.y, 0x01010000u), __builtin_amdgcn_perm(v.y, v.y, 0x03030202u));
+  }
   uint32_t w[4] = {0, 0, 0, 0};
+  if (layout == 2) {
+    // the transposed grid: slice i of the row's 16-row band is at i * (rows / 16) + row / 16
+    // (32-bit offsets: the grid holds k16 * rows / 16 < 2^32 codes)
+    const uint8_t* p = s + (row >> 4);
+    const uint32_t stride = (uint32_t)(rows >> 4);
+    uint32_t off = (uint32_t)(st * 16) * stride;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t b = st * 16 + i < k16 ? (uint32_t)p[off] : one;
+      w[i >> 2] |= b << (8 * (i & 3));
+      off += stride;
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int64_t slice = st * 16 + i;
     uint32_t b = one;
     if (slice < k16) {
       if (layout == 0) b = s[row * (K / B) + slice * 16 / B];
-      else if (layout == 1) b = s[(row >> 4) * k16 + slice];
-      else b = s[slice * (rows >> 4) + (row >> 4)];
+      else b = s[(row >> 4) * k16 + slice];
     }
     w[i >> 2] |= b << (8 * (i & 3));
   }
@@ -94,7 +132,7 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
                                                        const uint8_t* __restrict__ sb, int lb,
                                                        const float* __restrict__ ga, const float* __restrict__ gb,
                                                        float* __restrict__ c, int64_t M, int64_t N, int64_t K,
-                                                       int canon, int epi) {
+                                                       int canon, int epi, int align) {
   using TL = DecTiling;
   constexpr int GT = TL::BM;        // == TL::BN
   __shared__ __attribute__((aligned(1024))) uint8_t lA[2][TL::BM * ROWB];
@@ -118,8 +156,9 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
 
   const bool srow_is_a = threadIdx.x < GT;
   const int srow = threadIdx.x & (GT - 1);
-  uint4 sreg = srow_is_a ? scale_row16<FMT, B>(sa, la, m0 + srow, M, K, 0)
-                         : scale_row16<FMT, B>(sb, lb, n0 + srow, N, K, 0);
+  const bool al_a = align & 1, al_b = align & 2;
+  uint4 sreg = srow_is_a ? scale_row16<FMT, B>(sa, la, m0 + srow, M, K, 0, al_a)
+                         : scale_row16<FMT, B>(sb, lb, n0 + srow, N, K, 0, al_b);
   StageLoader<TL::BM, TL::NW> LA;
   StageLoader<TL::BN, TL::NW> LB;
   LA.init(qa, M, K, m0);
@@ -137,8 +176,8 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
     if (st + 1 < nstages) {
       LA.issue(st + 1, lA[buf ^ 1]);
       LB.issue(st + 1, lB[buf ^ 1]);
-      sreg = srow_is_a ? scale_row16<FMT, B>(sa, la, m0 + srow, M, K, st + 1)
-                       : scale_row16<FMT, B>(sb, lb, n0 + srow, N, K, st + 1);
+      sreg = srow_is_a ? scale_row16<FMT, B>(sa, la, m0 + srow, M, K, st + 1, al_a)
+                       : scale_row16<FMT, B>(sb, lb, n0 + srow, N, K, st + 1, al_b);
     }
     uint4 scA[2], scB[2];
 #pragma unroll
@@ -159,8 +198,8 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
           const int rowb = wn * 64 + t * 32 + (l & 31);
           const uint32_t ca = *reinterpret_cast<const uint32_t*>(lA[buf] + swz(rowa, off >> 4) + (off & 15));
           const uint32_t cb = *reinterpret_cast<const uint32_t*>(lB[buf] + swz(rowb, off >> 4) + (off & 15));
-          fa[sub][t] = decode8(ca, dec_factors(dec_scale3<FMT>(byte_of(scA[t], g * 4 + sub))));
-          fb[sub][t] = decode8(cb, dec_factors(dec_scale3<FMT>(byte_of(scB[t], g * 4 + sub))));
+          fa[sub][t] = decode8(ca, dec_factors_code<FMT>(byte_of(scA[t], g * 4 + sub)));
+          fb[sub][t] = decode8(cb, dec_factors_code<FMT>(byte_of(scB[t], g * 4 + sub)));
         }
       }
 #pragma unroll
@@ -208,9 +247,12 @@ template <int FMT, int B>
 static hipError_t launch_dec16(const GemmArgs& g) {
   using TL = DecTiling;
   const int64_t tiles = ((g.M + TL::BM - 1) / TL::BM) * ((g.N + TL::BN - 1) / TL::BN);
+  // per operand: scale array 16-byte aligned and K % 256 == 0 (whole-stage vector loads)
+  const int align = (((reinterpret_cast<uintptr_t>(g.a.s) & 15) == 0 && g.K % 256 == 0) ? 1 : 0) |
+                    (((reinterpret_cast<uintptr_t>(g.b.s) & 15) == 0 && g.K % 256 == 0) ? 2 : 0);
   hipLaunchKernelGGL((k_gemm_dec16<FMT, B>), dim3((unsigned)tiles), dim3(TL::NT), 0, g.stream, g.a.q, g.a.s, g.a.layout,
                      g.b.q, g.b.s, g.b.layout, g.a.g, g.b.g, g.c, g.M, g.N, g.K, g.canon,
-                     epilogue_word(g.hadamard_n, g.a.g_shift, g.b.g_shift));
+                     epilogue_word(g.hadamard_n, g.a.g_shift, g.b.g_shift), align);
   return hipGetLastError();
 }
 

@@ -50,6 +50,21 @@ def test_group_model_stress(fmt, block, spread, M, N, K, canon):
     assert_f32_bits_equal(got, want, f"fmt={fmt} B={block} spread={spread} {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("fmt", [OF.UE5M3, OF.E4M3])
+def test_zero_and_subnormal_scale_codes(fmt):
+    """Hand-built operands whose block-scale codes include 0 (the value 0: the quantizer never
+    writes it, the format allows it) and every subnormal code."""
+    rng = np.random.default_rng(17 + fmt)
+    qa = random_operand(rng, 96, 512, fmt, 16, 3)
+    qb = random_operand(rng, 80, 512, fmt, 16, 3)
+    qa.scales[rng.random(qa.scales.shape) < 0.15] = 0
+    qb.scales[:, ::5] = rng.integers(0, 8, qb.scales[:, ::5].shape)
+    want = _oracle_y(qa, qb)
+    got = fp4.gemm_fprop(qtensor_from_oracle(qa), qtensor_from_oracle(qb))
+    torch.cuda.synchronize()
+    assert_f32_bits_equal(got, want, f"zero/subnormal scale codes fmt={fmt}")
+
+
 def test_same_sign_rtz_drift():
     """All-positive products: every cross-group add truncates in the same direction."""
     rng = np.random.default_rng(5)
