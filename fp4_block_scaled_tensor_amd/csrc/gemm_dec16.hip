@@ -119,6 +119,18 @@ __device__ __forceinline__ uint4 scale_row16(const uint8_t* __restrict__ s, int 
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// One code of a transposed-2D operand's stage, for a cooperative load: thread j of the
+// operand's 128 staging threads takes slice j / 8 of the stage and 16-row band j % 8 of the
+// tile (rows r0 .. r0 + 127; rows % 16 == 0 in this layout). Bands past the matrix and
+// slices past K get the code of 1.0.
+template <int FMT>
+__device__ __forceinline__ uint32_t band_code(const uint8_t* __restrict__ s, int64_t rows, int64_t r0, int64_t K,
+                                              int64_t st, int j) {
+  const int64_t slice = st * 16 + (j >> 3), band = (r0 >> 4) + (j & 7);
+  if (slice >= K / 16 || band >= (rows >> 4)) return ScaleFmt<FMT>::ONE;
+  return s[(uint32_t)slice * (uint32_t)(rows >> 4) + (uint32_t)band];
+}
+
 __device__ __forceinline__ uint32_t byte_of(const uint4& v, int i) {
   const uint32_t w = i < 4 ? v.x : (i < 8 ? v.y : (i < 12 ? v.z : v.w));
   return (w >> (8 * (i & 3))) & 0xFFu;
@@ -138,6 +150,7 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
   __shared__ __attribute__((aligned(1024))) uint8_t lA[2][TL::BM * ROWB];
   __shared__ __attribute__((aligned(1024))) uint8_t lB[2][TL::BN * ROWB];
   __shared__ uint4 lS[2][TL::BM + TL::BN];   // 16 slice-scale codes per row: A rows then B rows
+  __shared__ uint4 lT[2][2][TL::BM / 16];     // transposed-2D operands: 16 codes per 16-row band
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
   int64_t m0, n0;
@@ -157,8 +170,21 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
   const bool srow_is_a = threadIdx.x < GT;
   const int srow = threadIdx.x & (GT - 1);
   const bool al_a = align & 1, al_b = align & 2;
-  uint4 sreg = srow_is_a ? scale_row16<FMT, B>(sa, la, m0 + srow, M, K, 0, al_a)
-                         : scale_row16<FMT, B>(sb, lb, n0 + srow, N, K, 0, al_b);
+  // scale staging: one row's 16 codes per thread, or for a transposed-2D operand one code per
+  // thread (the operand's 128 threads cover its 8 bands x 16 slices)
+  const int lay = srow_is_a ? la : lb;
+  auto load_stage_scales = [&](int64_t st) -> uint4 {
+    if (lay == 2)
+      return make_uint4(srow_is_a ? band_code<FMT>(sa, M, m0, K, st, srow) : band_code<FMT>(sb, N, n0, K, st, srow), 0,
+                        0, 0);
+    return srow_is_a ? scale_row16<FMT, B>(sa, la, m0 + srow, M, K, st, al_a)
+                     : scale_row16<FMT, B>(sb, lb, n0 + srow, N, K, st, al_b);
+  };
+  auto store_stage_scales = [&](int buf, const uint4& v) {
+    if (lay == 2) reinterpret_cast<uint8_t*>(&lT[buf][srow_is_a ? 0 : 1][srow & 7])[srow >> 3] = (uint8_t)v.x;
+    else lS[buf][threadIdx.x] = v;
+  };
+  uint4 sreg = load_stage_scales(0);
   StageLoader<TL::BM, TL::NW> LA;
   StageLoader<TL::BN, TL::NW> LB;
   LA.init(qa, M, K, m0);
@@ -167,7 +193,7 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
     LA.issue(0, lA[0]);
     LB.issue(0, lB[0]);
   }
-  lS[0][threadIdx.x] = sreg;
+  store_stage_scales(0, sreg);
   wait_vm();
   __syncthreads();
 
@@ -176,14 +202,14 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
     if (st + 1 < nstages) {
       LA.issue(st + 1, lA[buf ^ 1]);
       LB.issue(st + 1, lB[buf ^ 1]);
-      sreg = srow_is_a ? scale_row16<FMT, B>(sa, la, m0 + srow, M, K, st + 1, al_a)
-                       : scale_row16<FMT, B>(sb, lb, n0 + srow, N, K, st + 1, al_b);
+      sreg = load_stage_scales(st + 1);
     }
     uint4 scA[2], scB[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      scA[t] = lS[buf][wm * 64 + t * 32 + (l & 31)];
-      scB[t] = lS[buf][GT + wn * 64 + t * 32 + (l & 31)];
+      const int ra = wm * 64 + t * 32 + (l & 31), rb = wn * 64 + t * 32 + (l & 31);
+      scA[t] = la == 2 ? lT[buf][0][ra >> 4] : lS[buf][ra];
+      scB[t] = lb == 2 ? lT[buf][1][rb >> 4] : lS[buf][GT + rb];
     }
     const int g_end = (int)((ngroups - st * SGR) < SGR ? (ngroups - st * SGR) : SGR);
     for (int g = 0; g < g_end; ++g) {
@@ -235,7 +261,7 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
         }
     }
     if (st + 1 < nstages) {
-      lS[buf ^ 1][threadIdx.x] = sreg;
+      store_stage_scales(buf ^ 1, sreg);
       wait_vm();
       __syncthreads();
     }
