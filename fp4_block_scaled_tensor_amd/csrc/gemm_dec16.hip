@@ -131,9 +131,18 @@ __device__ __forceinline__ uint32_t band_code(const uint8_t* __restrict__ s, int
   return s[(uint32_t)slice * (uint32_t)(rows >> 4) + (uint32_t)band];
 }
 
-__device__ __forceinline__ uint32_t byte_of(const uint4& v, int i) {
-  const uint32_t w = i < 4 ? v.x : (i < 8 ? v.y : (i < 12 ? v.z : v.w));
-  return (w >> (8 * (i & 3))) & 0xFFu;
+// The decode-table entry of the scale code in byte `sub` of a word of codes:
+// one 8-byte LDS read. The byte offset is made opaque so that the table's base address is
+// added in the read's immediate offset rather than OR-ed into the address register, which
+// would split the read in two.
+__device__ __forceinline__ DecScale dec_entry(const uint2* table, uint32_t word, int sub) {
+  uint32_t off = ((word >> (8 * sub)) & 0xFFu) << 3;
+  asm("" : "+v"(off));
+  const uint2 e = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(table) + off);
+  DecScale d;
+  d.p2 = __uint_as_float(e.x);
+  d.m2 = __builtin_bit_cast(v2h, e.y);
+  return d;
 }
 
 using DecTiling = Tiling<2, 2, 2, 2>;   // 128x128 workgroup tile, 4 waves of 64x64
@@ -147,10 +156,12 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
                                                        int canon, int epi, int align) {
   using TL = DecTiling;
   constexpr int GT = TL::BM;        // == TL::BN
+  __shared__ __attribute__((aligned(4096))) uint2 lDec[256];   // decode factors of every scale code (p2 bits, M pair)
   __shared__ __attribute__((aligned(1024))) uint8_t lA[2][TL::BM * ROWB];
   __shared__ __attribute__((aligned(1024))) uint8_t lB[2][TL::BN * ROWB];
   __shared__ uint4 lS[2][TL::BM + TL::BN];   // 16 slice-scale codes per row: A rows then B rows
   __shared__ uint4 lT[2][2][TL::BM / 16];     // transposed-2D operands: 16 codes per 16-row band
+  static_assert(TL::NT == 256, "one decode-table entry per thread");
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
   int64_t m0, n0;
@@ -184,6 +195,10 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
     if (lay == 2) reinterpret_cast<uint8_t*>(&lT[buf][srow_is_a ? 0 : 1][srow & 7])[srow >> 3] = (uint8_t)v.x;
     else lS[buf][threadIdx.x] = v;
   };
+  {
+    const DecScale d = dec_factors_code<FMT>(threadIdx.x);
+    lDec[threadIdx.x] = make_uint2(__float_as_uint(d.p2), __builtin_bit_cast(uint32_t, d.m2));
+  }
   uint4 sreg = load_stage_scales(0);
   StageLoader<TL::BM, TL::NW> LA;
   StageLoader<TL::BN, TL::NW> LB;
@@ -204,15 +219,31 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
       LB.issue(st + 1, lB[buf ^ 1]);
       sreg = load_stage_scales(st + 1);
     }
-    uint4 scA[2], scB[2];
+    // the stage's scale codes of this lane's rows: word g holds the codes of group g's four slices
+    const uint32_t* scA[2];
+    const uint32_t* scB[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int ra = wm * 64 + t * 32 + (l & 31), rb = wn * 64 + t * 32 + (l & 31);
-      scA[t] = la == 2 ? lT[buf][0][ra >> 4] : lS[buf][ra];
-      scB[t] = lb == 2 ? lT[buf][1][rb >> 4] : lS[buf][GT + rb];
+      scA[t] = reinterpret_cast<const uint32_t*>(la == 2 ? &lT[buf][0][ra >> 4] : &lS[buf][ra]);
+      scB[t] = reinterpret_cast<const uint32_t*>(lb == 2 ? &lT[buf][1][rb >> 4] : &lS[buf][GT + rb]);
     }
     const int g_end = (int)((ngroups - st * SGR) < SGR ? (ngroups - st * SGR) : SGR);
+    uint32_t nwa[2], nwb[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      nwa[t] = scA[t][0];
+      nwb[t] = scB[t][0];
+    }
     for (int g = 0; g < g_end; ++g) {
+      uint32_t wa[2], wb[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        wa[t] = nwa[t];
+        wb[t] = nwb[t];
+        nwa[t] = scA[t][(g + 1) & 3];
+        nwb[t] = scB[t][(g + 1) & 3];
+      }
       // decoded fp16 fragments (times 2^-3) of the group's four 16-wide slices
       v8h fa[4][2], fb[4][2];
 #pragma unroll
@@ -224,8 +255,8 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
           const int rowb = wn * 64 + t * 32 + (l & 31);
           const uint32_t ca = *reinterpret_cast<const uint32_t*>(lA[buf] + swz(rowa, off >> 4) + (off & 15));
           const uint32_t cb = *reinterpret_cast<const uint32_t*>(lB[buf] + swz(rowb, off >> 4) + (off & 15));
-          fa[sub][t] = decode8(ca, dec_factors_code<FMT>(byte_of(scA[t], g * 4 + sub)));
-          fb[sub][t] = decode8(cb, dec_factors_code<FMT>(byte_of(scB[t], g * 4 + sub)));
+          fa[sub][t] = decode8(ca, dec_entry(lDec, wa[t], sub));
+          fb[sub][t] = decode8(cb, dec_entry(lDec, wb[t], sub));
         }
       }
 #pragma unroll
