@@ -102,26 +102,33 @@ __device__ __forceinline__ uint32_t e2m1_pack8(const float* r) {
 }
 
 // ---- stochastic E2M1 ----
-// With a = |r| < 6, let lo <= a < hi be the neighbouring codebook values (grid step 0.5
-// below 2, 1 below 4, 2 below 6); round up iff u16 < 65536 * (a - lo) / (hi - lo). All
-// quantities are exact in float32 (Sterbenz subtraction, power-of-two scaling).
+// With lo <= |r| < hi the neighbouring codebook values, round up iff u16 < 65536 (|r| - lo) /
+// (hi - lo); |r| >= 6 gives 6. Branch-free form: with a = min(|r|, 6) and k the binary
+// exponent of a clamped to [1, 3] (frexp convention, so a in [2, 4) has k = 2 and a in
+// [4, 6] has k = 3), t = a 2^(2-k) is exact and lies in [0, 4). Below 2, t = 2a and floor(t)
+// is the code of lo; in [2, 4) t = a and in [4, 6] t = a / 2, and floor(t) is 2 below that
+// code. So code = floor(t) + 2 (k - 1) + up, where frac(t) = (|r| - lo) / (hi - lo) exactly.
+// a = 6 (any |r| >= 6) gives k = 3, t = 3, frac 0: code 7.
 __device__ __forceinline__ uint32_t e2m1_sr(float r, uint32_t u16) {
-  const float a = fabsf(r);
+  const float a = fminf(fabsf(r), 6.0f);
+  const int k = min(max(__builtin_amdgcn_frexp_expf(a), 1), 3);
+  const float t = __builtin_amdgcn_ldexpf(a, 2 - k);
+  const float frac = __builtin_amdgcn_fractf(t);
+  const uint32_t up = (float)u16 < frac * 65536.0f ? 1u : 0u;
   const uint32_t sign = (__float_as_uint(r) >> 28) & 8u;
-  if (!(a < 6.0f)) return sign | 7u;
-  float t;
-  uint32_t base;
-  if (a < 2.0f) { t = a * 2.0f; base = 0; }
-  else if (a < 4.0f) { t = a - 2.0f; base = 4; }
-  else { t = (a - 4.0f) * 0.5f; base = 6; }
-  const float fl = __builtin_floorf(t);
-  const float frac = t - fl;
-  const uint32_t up = ((float)u16 < frac * 65536.0f) ? 1u : 0u;
-  return sign | (base + (uint32_t)fl + up);
+  return sign | ((uint32_t)t + 2u * (uint32_t)k - 2u + up);
 }
 
 // ---- Philox-4x32-10 (Salmon et al., SC'11) ----
 struct u4 { uint32_t x, y, z, w; };
+
+// a ^ b ^ k in one v_bitop3_b32 (truth table 0x96); k must be wave-uniform (a scalar
+// operand: the Philox key, derived from the seed argument)
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t k) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+  return r;
+}
 
 __device__ __forceinline__ u4 philox4x32_10(u4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
@@ -131,7 +138,7 @@ __device__ __forceinline__ u4 philox4x32_10(u4 c, uint32_t k0, uint32_t k1) {
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
     const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
     const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
-    c = u4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+    c = u4{xor3(hi1, c.y, k0), lo1, xor3(hi0, c.w, k1), lo0};
   }
   return c;
 }
