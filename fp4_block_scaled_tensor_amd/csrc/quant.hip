@@ -60,19 +60,24 @@ __device__ __forceinline__ float quant_block_row(const float (&v)[B], const Tens
   return amax_b;
 }
 
-template <int FMT, int B, bool SR, bool F32>
+// LOCAL (tile-local tensor scales): d_amax holds one amax per stripe of 2^stripe_log2 rows and
+// row r uses the tensor scales of d_amax[r >> stripe_log2]; g is not written (the caller
+// turns the stripe maxima into g afterwards) and d_amax_obs is not used.
+template <int FMT, int B, bool SR, bool F32, bool LOCAL = false>
 __global__ __launch_bounds__(NT) void k_quant_row(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
                                                   int tpr_log2, const float* __restrict__ d_amax, float T,
                                                   uint64_t seed, uint64_t offset, uint8_t* __restrict__ q,
                                                   uint8_t* __restrict__ s, float* __restrict__ d_amax_obs,
-                                                  float* __restrict__ d_g) {
+                                                  float* __restrict__ d_g, int stripe_log2 = 0) {
   const int tpr = 1 << tpr_log2;
   const int half_rows = NT >> tpr_log2;                // rows per pass
   const int64_t nbr = cols / B;
   const int64_t b = (int64_t)blockIdx.x * tpr + (threadIdx.x & (tpr - 1));
   TensorScales ts{1.0f, 1.0f, 1.0f};
-  if constexpr (FMT != FMT_E8M0) ts = tensor_scales(d_amax, T);
-  write_g<FMT>(d_g, ts);
+  if constexpr (!LOCAL) {
+    if constexpr (FMT != FMT_E8M0) ts = tensor_scales(d_amax, T);
+    write_g<FMT>(d_g, ts);
+  }
   float obs = 0.0f;
   if (b < nbr) {
     // row groups of 2 * half_rows rows, strided over the grid (one group per workgroup
@@ -81,14 +86,19 @@ __global__ __launch_bounds__(NT) void k_quant_row(const void* __restrict__ x, in
       const int64_t r0 = rg * (2 * half_rows) + (threadIdx.x >> tpr_log2);
       const int64_t r1 = r0 + half_rows;
       const bool has0 = r0 < rows, has1 = r1 < rows;
+      TensorScales ts0 = ts, ts1 = ts;
+      if constexpr (LOCAL) {
+        ts0 = tensor_scales_from(has0 ? d_amax[r0 >> stripe_log2] : 0.0f, T);
+        ts1 = tensor_scales_from(has1 ? d_amax[r1 >> stripe_log2] : 0.0f, T);
+      }
       float v0[B], v1[B];
       if (has0) load_block<B, F32>(x, r0 * ld + b * B, v0);
       if (has1) load_block<B, F32>(x, r1 * ld + b * B, v1);
-      if (has0) obs = fmaxf(obs, quant_block_row<FMT, B, SR>(v0, ts, r0, b, cols, seed, offset, q, s));
-      if (has1) obs = fmaxf(obs, quant_block_row<FMT, B, SR>(v1, ts, r1, b, cols, seed, offset, q, s));
+      if (has0) obs = fmaxf(obs, quant_block_row<FMT, B, SR>(v0, ts0, r0, b, cols, seed, offset, q, s));
+      if (has1) obs = fmaxf(obs, quant_block_row<FMT, B, SR>(v1, ts1, r1, b, cols, seed, offset, q, s));
     }
   }
-  if (d_amax_obs) wg_max_to(d_amax_obs, obs);
+  if (!LOCAL && d_amax_obs) wg_max_to(d_amax_obs, obs);
 }
 
 // ---------------------------------------------------------------- COL view (wgrad operands)
@@ -462,6 +472,51 @@ __global__ __launch_bounds__(NT) void k_quant_row_local(const void* __restrict__
   }
 }
 
+// Two-pass form for stripes too few to fill the chip with one workgroup each: the stripe
+// maxima are reduced by workgroups of (column chunk, stripe) into amax[stripe] (zeroed first;
+// one atomic per workgroup), the row quantizer then reads them (LOCAL mode), and
+// k_stripe_finalize turns each maximum into the stripe's g (and copies it out if asked).
+template <bool F32>
+__global__ __launch_bounds__(NT) void k_stripe_amax(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                    int64_t ld, int stripe_log2, int64_t chunk_cols,
+                                                    float* __restrict__ amax) {
+  const int64_t r0 = (int64_t)blockIdx.y << stripe_log2;
+  const int64_t nr = min((int64_t)1 << stripe_log2, rows - r0);
+  const int64_t c0 = (int64_t)blockIdx.x * chunk_cols;
+  const int64_t cw = min(chunk_cols, cols - c0) / 8;        // 8-element chunks per row of the piece
+  const int64_t n = nr * cw;
+  constexpr int UL = 4;
+  float m = 0.0f;
+  for (int64_t i0 = threadIdx.x; i0 < n; i0 += UL * NT) {
+    float v[UL][8];
+#pragma unroll
+    for (int u = 0; u < UL; ++u) {
+      int64_t i = i0 + u * NT;
+      i = i < n ? i : n - 1;                                 // a repeated chunk does not change the max
+      const int64_t r = i / cw, k = (i - r * cw) * 8;
+      load8<F32>(x, (r0 + r) * ld + c0 + k, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < UL; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[u][j]));
+  }
+  wg_max_to(amax + blockIdx.y, m);
+}
+
+__global__ void k_fill_n(float* __restrict__ p, float v, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+// g[i] holds stripe i's amax on entry and its decode scale g on exit.
+__global__ void k_stripe_finalize(float* __restrict__ g, float* __restrict__ amax_out, int64_t n, float T) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const float A = g[i];
+    if (amax_out) amax_out[i] = A;
+    g[i] = tensor_scales_from(A, T).g;
+  }
+}
+
 // ---------------------------------------------------------------- TILE2D (weights)
 constexpr int WT = 64;   // 64x64 weight tile per workgroup
 
@@ -676,8 +731,35 @@ hipError_t run_quantize_rowcol(const RowColArgs& a) {
 template <int FMT, int B, bool SR, bool F32>
 static hipError_t launch_local(const LocalQuantArgs& a) {
   const int64_t stripes = (a.rows + ((int64_t)1 << a.stripe_log2) - 1) >> a.stripe_log2;
-  hipLaunchKernelGGL((k_quant_row_local<FMT, B, SR, F32>), dim3((unsigned)stripes), dim3(NT), 0, a.stream, a.x,
-                     a.rows, a.cols, a.ld, a.stripe_log2, a.T, a.seed, a.offset, a.q, a.s, a.g, a.amax);
+  if (stripes >= 2 * (int64_t)device_cu_count()) {
+    // enough stripes to fill the chip: one workgroup per stripe, one pass
+    hipLaunchKernelGGL((k_quant_row_local<FMT, B, SR, F32>), dim3((unsigned)stripes), dim3(NT), 0, a.stream, a.x,
+                       a.rows, a.cols, a.ld, a.stripe_log2, a.T, a.seed, a.offset, a.q, a.s, a.g, a.amax);
+    return hipGetLastError();
+  }
+  // few large stripes: stripe maxima into g by (column chunk, stripe) workgroups, the row
+  // quantizer with per-stripe scales, then g from the maxima
+  hipError_t e;
+  const unsigned fb = (unsigned)((stripes + NT - 1) / NT);
+  hipLaunchKernelGGL(k_fill_n, dim3(fb), dim3(NT), 0, a.stream, a.g, 0.0f, stripes);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  int64_t chunk = 512;                                   // columns per amax workgroup (multiple of 8)
+  while (chunk > 64 && stripes * ((a.cols + chunk - 1) / chunk) < 4 * (int64_t)device_cu_count()) chunk /= 2;
+  const int64_t nchunks = (a.cols + chunk - 1) / chunk;
+  hipLaunchKernelGGL((k_stripe_amax<F32>), dim3((unsigned)nchunks, (unsigned)stripes), dim3(NT), 0, a.stream, a.x,
+                     a.rows, a.cols, a.ld, a.stripe_log2, chunk, a.g);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t nbr = a.cols / B;
+  int tpr_log2 = 0;
+  while ((1 << tpr_log2) < nbr && (1 << tpr_log2) < NT) ++tpr_log2;
+  const int64_t rows_per_wg = 2 * (NT >> tpr_log2);
+  const int64_t groups = (a.rows + rows_per_wg - 1) / rows_per_wg;
+  const unsigned gy = (unsigned)(groups < 65535 ? groups : 65535);
+  dim3 grid((unsigned)((nbr + (1 << tpr_log2) - 1) >> tpr_log2), gy);
+  hipLaunchKernelGGL((k_quant_row<FMT, B, SR, F32, true>), grid, dim3(NT), 0, a.stream, a.x, a.rows, a.cols, a.ld,
+                     tpr_log2, a.g, a.T, a.seed, a.offset, a.q, a.s, nullptr, nullptr, a.stripe_log2);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_stripe_finalize, dim3(fb), dim3(NT), 0, a.stream, a.g, a.amax, stripes, a.T);
   return hipGetLastError();
 }
 

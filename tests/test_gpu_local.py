@@ -48,6 +48,23 @@ def test_quantize_local_matches_oracle(name, rows, cols, dtype, fmt, block, stri
     assert_f32_bits_equal(obs, ref.amax, f"{name} amax")
 
 
+def test_quantize_local_single_and_two_pass_forms():
+    """Both launch forms against the oracle: one workgroup per stripe when there are at least
+    two stripes per compute unit, and the two-pass form (stripe maxima by (column chunk,
+    stripe) workgroups, then the row quantizer with per-stripe scales) below that."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for name, rows, cols, stripe in (("single_pass", 2 * cus * 16, 64, 16), ("two_pass", 384, 2048, 128)):
+        t = _tensor(rows, cols, "bf16", 6100 + rows)
+        ref = oracle.quantize_1d_local(t.values, OF.E4M3, 16, stripe=stripe, T=448.0)
+        obs = torch.empty(len(ref.g), dtype=torch.float32, device="cuda")
+        got = fp4.quantize_local(dev_input(t), OF.E4M3, 16, stripe=stripe, amax_obs=obs)
+        torch.cuda.synchronize()
+        assert_bytes_equal(got.q, oracle.pack_codes(ref.codes), f"{name} payload")
+        assert_bytes_equal(got.s, ref.scales, f"{name} scales")
+        assert_f32_bits_equal(got.g, ref.g, f"{name} g")
+        assert_f32_bits_equal(obs, ref.amax, f"{name} amax")
+
+
 def _oracle_operand(lq):
     return OF.decode_e2m1(lq.codes), OF.SCALE_VALUES[lq.fmt][lq.scales.astype(np.int64)]
 
