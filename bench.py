@@ -210,7 +210,7 @@ def graph_time_ms(torch, fn, check, reps=20):
 def next_rows(torch, fp4, Xd, step_obj, args):
     """Graph-timed kernels of the rows built past the training step, on the same 8192x4096
     activation: inference fake quantization (bf16 out) and operand decode, MXFP4 -> FP8
-    (transposed, the backward form), tile-local quantization (E4M3, 16-row stripes). Each
+    (transposed, the backward form), tile-local quantization (E4M3, 16- and 128-row stripes). Each
     entry: algorithmic bytes per element, average ms, GB/s and fraction of HBM peak."""
     n = M_TOK * K_IN
     fmt, B = step_obj.fmt, step_obj.block
@@ -231,6 +231,9 @@ def next_rows(torch, fp4, Xd, step_obj, args):
         "quantize_local": ("k_quant_row_local (E4M3, 16-row stripes)", 2.0 + 0.5 + 1.0 / 16,
                            lambda: fp4.quantize_local(Xd, fp4.E4M3, 16, stripe=16),
                            lambda a, b: torch.equal(a.q, b.q) and torch.equal(a.s, b.s) and torch.equal(a.g, b.g)),
+        "quantize_local_s128": ("k_stripe_amax + k_quant_row (E4M3, 128-row stripes, two-pass)", 2.0 + 0.5 + 1.0 / 16,
+                                lambda: fp4.quantize_local(Xd, fp4.E4M3, 16, stripe=128),
+                                lambda a, b: torch.equal(a.q, b.q) and torch.equal(a.s, b.s) and torch.equal(a.g, b.g)),
     }
     out = {}
     for name, (kernel, bpe, fn, same) in cases.items():

@@ -182,7 +182,8 @@ __device__ __forceinline__ int tile_row(int r, int l) { return (r >> 2) * 8 + (l
 // columns n0 + 32j. pre (a power of two) undoes a constant factor the K loop carried; it is
 // exact and applied before the canonicalisation. epi: bits 0-7 Hadamard n; bits 8-15 / 16-23
 // the log2 stripe height of A's / B's tile-local g (0: one g for the operand), in which case
-// alpha = float32(g_a[row >> sa] * g_b[col >> sb]) per output.
+// alpha = float32(g_a[row >> sa] * g_b[col >> sb]) per output. The float32 outputs are stored
+// non-temporal: they stream past the L2, which keeps the operand tiles other workgroups reuse.
 template <int TM, int TN>
 __device__ __forceinline__ void store_tiles(float* __restrict__ c, int64_t M, int64_t N, int64_t m0, int64_t n0,
                                             v16f (&acc)[TM][TN], const float* ga, const float* gb, int canon,
@@ -212,7 +213,7 @@ __device__ __forceinline__ void store_tiles(float* __restrict__ c, int64_t M, in
           float v = acc[rt][ct][r] * pre;
           if (canon) v = __builtin_rintf(v * 1024.0f) * (1.0f / 1024.0f);
           v = v * alpha;
-          if (row < M && col < N) c[row * N + col] = v;
+          if (row < M && col < N) __builtin_nontemporal_store(v, &c[row * N + col]);
         }
       }
   } else {
@@ -233,7 +234,7 @@ __device__ __forceinline__ void store_tiles(float* __restrict__ c, int64_t M, in
           float v = acc[rt][ct][r] * pre;
           if (canon) v = __builtin_rintf(v * 1024.0f) * (1.0f / 1024.0f);
           v = v * alpha;
-          if (row < M && col < N) c[row * N + col] = v;
+          if (row < M && col < N) __builtin_nontemporal_store(v, &c[row * N + col]);
         }
       }
   }

@@ -221,16 +221,18 @@ __global__ __launch_bounds__(NT) void k_quant_col(const void* __restrict__ x, in
 // operand (COL view, optionally Hadamard-rotated), each with its own cached amax, T and
 // rounding.
 //
-// A workgroup owns a 128-token x 64-feature tile. Lane l of a pass loads the 8 elements
-// [8(l%8), 8(l%8)+8) of token row l/8 (eight lanes read one 128-byte line), so the ROW
-// blocks are finished in registers: a block spans B/8 neighbouring lanes, whose maxima
-// are combined with DPP quad permutes. The tile is then written to LDS in the input's own
-// type (bf16 or float; 16 or 32 KB) for the COL view, whose payload is transposed through
-// a small LDS tile as in the COL kernel. Workgroups are ordered so that each XCD walks
-// the feature tiles of a token stripe in turn: the partial 128-byte lines each tile writes
-// are completed in that XCD's L2 before they are written back.
-constexpr int RT = 128;   // tokens per fused tile
-constexpr int RF = 64;    // features per fused tile
+// A workgroup owns a 64-token x 128-feature tile. Lane l of a pass loads the 8 elements
+// [8(l%16), 8(l%16)+8) of token row l/16 (sixteen lanes read one 256-byte bf16 row segment;
+// wider segments read faster than the 128-byte ones of a 128 x 64 tile, and 64 tokens still
+// hold two 32-token COL units), so the ROW blocks are finished in registers: a block spans
+// B/8 neighbouring lanes, whose maxima are combined with DPP quad permutes. The tile is then
+// written to LDS in the input's own type (bf16 or float; 16 or 32 KB) for the COL view,
+// whose payload is transposed through a small LDS tile as in the COL kernel. Workgroups are
+// ordered so that each XCD walks the feature tiles of a token stripe in turn: the partial
+// 128-byte lines each tile writes are completed in that XCD's L2 before they are written
+// back.
+constexpr int RT = 64;    // tokens per fused tile
+constexpr int RF = 128;   // features per fused tile
 
 // Persistent: gridDim.x workgroups walk the tiles. When the tile count and the grid are
 // multiples of 8, workgroup w (on XCD w % 8) takes tiles k*P + w/8 + i*(gridDim.x/8) of
@@ -249,7 +251,8 @@ __global__ __launch_bounds__(NT) void k_quant_rowcol(const void* __restrict__ x,
                                                      float* __restrict__ obs_c) {
   constexpr int U = (HN > B) ? HN : B;          // COL tokens per thread unit
   constexpr int UNITS = RT / U;
-  constexpr int RPP = NT / 8;                   // token rows per load pass
+  constexpr int LPR = RF / 8;                   // lanes per tile row (8 elements each)
+  constexpr int RPP = NT / LPR;                 // token rows per load pass
   constexpr int PASSES = RT / RPP;
   constexpr int LB = B / 8;                     // lanes per ROW block
   constexpr int ESZ = F32 ? 4 : 2;
@@ -280,8 +283,8 @@ __global__ __launch_bounds__(NT) void k_quant_rowcol(const void* __restrict__ x,
   write_g<FMT>(g_r, tr);
   write_g<FMT>(g_c, tc);
 
-  const int lc = threadIdx.x & 7, lr = threadIdx.x >> 3;
-  const int f = threadIdx.x & 63;
+  const int lc = threadIdx.x % LPR, lr = threadIdx.x / LPR;
+  const int f = threadIdx.x % RF;
   const uint32_t ld_b = (uint32_t)(ld * ESZ);
   const uint32_t qcols = (uint32_t)(cols / 2), scols = (uint32_t)(cols / B);
   const uint32_t qrows = (uint32_t)(rows / 2), srows = (uint32_t)(rows / B);
@@ -353,7 +356,7 @@ __global__ __launch_bounds__(NT) void k_quant_rowcol(const void* __restrict__ x,
     __syncthreads();
 
     // COL view: thread -> (feature f, unit u) of U consecutive tokens
-    for (int u = threadIdx.x >> 6; u < UNITS; u += NT / 64) {
+    for (int u = threadIdx.x / RF; u < UNITS; u += NT / RF) {
       if (u * U >= rl) break;                   // rows % U == 0: units are whole
       float c[U];
 #pragma unroll
