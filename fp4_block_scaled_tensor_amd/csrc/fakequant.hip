@@ -12,12 +12,12 @@
 // rounded from that float32, nearest-even.
 //
 // Kernels:
-//   k_fake_quant  x -> x_hat in one pass (ROW view, nearest-even): a 128-row x 64-column tile
-//                 per workgroup, 8 lanes per 64-element row segment (one 128-byte bf16 line),
+//   k_fake_quant  x -> x_hat in one pass (ROW view, nearest-even): a 64-row x 128-column tile
+//                 per workgroup, 16 lanes per 128-element row segment (256 bytes of bf16),
 //                 a block of B elements spans B/8 lanes whose maxima combine by DPP, codes are
 //                 made and decoded in registers.
 //   k_dequant     a quantized operand (1D, 2D or transposed-2D scales) -> x_hat, the same
-//                 tiling over its [rows x K] values.
+//                 lane layout on 32-row x 256-column tiles (128 payload bytes per row).
 //   k_mx_to_fp8   MXFP4 operand -> FP8 E4M3 with one E8M0 scale per 128-element chunk
 //                 ("Practical FP4 Training for Large-Scale MoE Models on Hopper GPUs",
 //                 methodology: direct FP4 -> FP8 conversion, hierarchical scale alignment
@@ -32,10 +32,18 @@
 
 namespace fp4k {
 
-constexpr int FT = 128;   // rows per tile
-constexpr int FF = 64;    // columns per tile
-constexpr int FPP = NT / 8;          // rows per pass
+// Tile shapes (measured at 8192 x 4096: wider rows read and write longer contiguous
+// segments; decode, with its 4-byte payload reads, gains most from 256-column tiles).
+constexpr int FT = 64;    // fake quant: rows per tile
+constexpr int FF = 128;   // fake quant: columns per tile
+constexpr int FLR = FF / 8;          // lanes per tile row (8 elements each)
+constexpr int FPP = NT / FLR;        // rows per pass
 constexpr int FPASSES = FT / FPP;
+constexpr int DT = 32;    // decode: rows per tile
+constexpr int DF = 256;   // decode: columns per tile
+constexpr int DLR = DF / 8;
+constexpr int DPP = NT / DLR;
+constexpr int DPASSES = DT / DPP;
 
 // nearest-even float32 -> bfloat16 bits (finite inputs; overflow rounds to infinity)
 __device__ __forceinline__ uint32_t bf16_rne(float v) {
@@ -97,7 +105,7 @@ __global__ __launch_bounds__(NT) void k_fake_quant(const void* __restrict__ x, i
   const int64_t t0 = (int64_t)(blockIdx.x / nft) * FT, f0 = (int64_t)(blockIdx.x % nft) * FF;
   TensorScales ts{1.0f, 1.0f, 1.0f};
   if constexpr (FMT != FMT_E8M0) ts = tensor_scales(d_amax, T);
-  const int lc = threadIdx.x & 7, lr = threadIdx.x >> 3;
+  const int lc = threadIdx.x % FLR, lr = threadIdx.x / FLR;
   const int rl = (int)min(rows - t0, (int64_t)FT), cl = (int)min(cols - f0, (int64_t)FF);
   const bool cok = lc * 8 < cl;
   const rsrc_t rx = make_rsrc(reinterpret_cast<const char*>(x) + (t0 * ld + f0) * ESZ);
@@ -143,27 +151,27 @@ __global__ __launch_bounds__(NT) void k_dequant(const uint8_t* __restrict__ q, c
                                                 const float* __restrict__ d_g, int64_t rows, int64_t K,
                                                 void* __restrict__ y, int64_t ldy) {
   constexpr int OSZ = BF16 ? 2 : 4;
-  const int64_t nft = (K + FF - 1) / FF;
-  const int64_t t0 = (int64_t)(blockIdx.x / nft) * FT, f0 = (int64_t)(blockIdx.x % nft) * FF;
+  const int64_t nft = (K + DF - 1) / DF;
+  const int64_t t0 = (int64_t)(blockIdx.x / nft) * DT, f0 = (int64_t)(blockIdx.x % nft) * DF;
   const float g = (FMT == FMT_E8M0 || d_g == nullptr) ? 1.0f : *d_g;
-  const int lc = threadIdx.x & 7, lr = threadIdx.x >> 3;
-  const int rl = (int)min(rows - t0, (int64_t)FT), cl = (int)min(K - f0, (int64_t)FF);
+  const int lc = threadIdx.x % DLR, lr = threadIdx.x / DLR;
+  const int rl = (int)min(rows - t0, (int64_t)DT), cl = (int)min(K - f0, (int64_t)DF);
   const bool cok = lc * 8 < cl;
   const rsrc_t rq = make_rsrc(q + t0 * (K / 2) + f0 / 2);
   const rsrc_t ry = make_rsrc(reinterpret_cast<char*>(y) + (t0 * ldy + f0) * OSZ);
   const uint32_t qrow = (uint32_t)(K / 2), ldy_b = (uint32_t)(ldy * OSZ);
-  uint32_t w[FPASSES];
-  uint32_t sc[FPASSES];
+  uint32_t w[DPASSES];
+  uint32_t sc[DPASSES];
 #pragma unroll
-  for (int p = 0; p < FPASSES; ++p) {
-    const int r = p * FPP + lr;
+  for (int p = 0; p < DPASSES; ++p) {
+    const int r = p * DPP + lr;
     const bool ok = cok && r < rl;
     w[p] = __builtin_amdgcn_raw_buffer_load_b32(rq, ok ? (uint32_t)r * qrow + (uint32_t)(lc * 4) : OOB, 0, 0);
     sc[p] = ok ? s[scale_index<LAYOUT, B>(t0 + r, f0 + lc * 8, rows, K)] : 127u;
   }
 #pragma unroll
-  for (int p = 0; p < FPASSES; ++p) {
-    const int r = p * FPP + lr;
+  for (int p = 0; p < DPASSES; ++p) {
+    const int r = p * DPP + lr;
     float out[8];
     decode8<FMT>(w[p], scale_value<FMT>(sc[p]), g, out);
     store8<BF16>(ry, (cok && r < rl) ? (uint32_t)r * ldy_b + (uint32_t)(lc * 8 * OSZ) : OOB, out);
@@ -304,7 +312,7 @@ hipError_t run_fake_quant(const FakeQuantArgs& a) {
 
 template <int FMT, int B, int LAYOUT, bool BF16>
 static hipError_t launch_dq(const DequantArgs& a) {
-  const int64_t tiles = ((a.rows + FT - 1) / FT) * ((a.K + FF - 1) / FF);
+  const int64_t tiles = ((a.rows + DT - 1) / DT) * ((a.K + DF - 1) / DF);
   hipLaunchKernelGGL((k_dequant<FMT, B, LAYOUT, BF16>), dim3((unsigned)tiles), dim3(NT), 0, a.stream, a.q, a.s, a.g,
                      a.rows, a.K, a.y, a.ldy);
   return hipGetLastError();
