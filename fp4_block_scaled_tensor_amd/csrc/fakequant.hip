@@ -23,10 +23,11 @@
 //                 methodology: direct FP4 -> FP8 conversion, hierarchical scale alignment
 //                 from block 32 to block 128, transpose fused): chunk code c = e_max -
 //                 min(6, e_max) over the chunk's four block codes, element
-//                 E4M3(E2M1(q) * 2^(e_b - c)) nearest-even with subnormals, sign kept. A
-//                 256-row x 128-column tile per workgroup, 4 lanes per row chunk (64 payload
-//                 bytes), e_max by DPP, codes by a per-block v_perm_b32 table; the transposed
-//                 form goes through a 34 KB LDS byte tile.
+//                 E4M3(E2M1(q) * 2^(e_b - c)) nearest-even with subnormals, sign kept. One
+//                 lane per 32-element block, 4 lanes per 128-element chunk (e_max by DPP),
+//                 codes by a per-block v_perm_b32 table; 128-row x 256-column tiles in the
+//                 row-major form, 256-row x 128-column tiles in the transposed form, which
+//                 goes through a 34 KB LDS byte tile.
 // Raw buffer loads and stores with out-of-range offsets for lanes outside the matrix.
 #include "quant_common.hpp"
 
@@ -179,10 +180,20 @@ __global__ __launch_bounds__(NT) void k_dequant(const uint8_t* __restrict__ q, c
 }
 
 // ---------------------------------------------------------------- MXFP4 -> FP8
-constexpr int XK = 128;   // K per conversion tile (one 128-element chunk)
-constexpr int XT = 256;   // rows per conversion tile
-constexpr int XP = XT / 64;   // rows per thread (passes of 64 rows)
-constexpr int XRS = XT + 16;   // LDS byte-tile row stride (16-byte aligned, staggers banks)
+constexpr int XC = 128;   // FP8 scale chunk
+// Conversion tile (measured at 8192 x 4096): the row-major form reads and writes longer row
+// segments with two chunks per tile row (128 x 256); the transposed form keeps one chunk
+// per row and 256 rows (its LDS byte tile's column writes conflict more as K grows, and
+// its output rows are XT bytes long).
+template <bool TRANSPOSE>
+struct XTile {
+  static constexpr int K = TRANSPOSE ? 128 : 256;   // K per tile (a multiple of XC)
+  static constexpr int T = TRANSPOSE ? 256 : 128;   // rows per tile
+  static constexpr int L = K / 32;                  // lanes per tile row (one 32-element block each)
+  static constexpr int PP = NT / L;                 // rows per pass
+  static constexpr int P = T / PP;                  // rows per thread
+  static constexpr int RS = T + 16;                 // LDS byte-tile row stride (16-byte aligned, staggers banks)
+};
 
 // max over the 4 lanes of a quad (integers)
 __device__ __forceinline__ int quad_max(int v) {
@@ -236,19 +247,23 @@ template <bool TRANSPOSE>
 __global__ __launch_bounds__(NT) void k_mx_to_fp8(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
                                                   int64_t rows, int64_t K, uint8_t* __restrict__ y,
                                                   uint8_t* __restrict__ s8) {
+  using X = XTile<TRANSPOSE>;
+  constexpr int XK = X::K, XT = X::T, XL = X::L, XPP = X::PP, XP = X::P, XRS = X::RS;
   __shared__ __align__(16) uint8_t tile[TRANSPOSE ? XK : 1][TRANSPOSE ? XRS : 16];
-  const int64_t nkt = K / XK;
+  const int64_t nkt = (K + XK - 1) / XK;
   const int64_t r0 = (int64_t)(blockIdx.x / nkt) * XT, k0 = (int64_t)(blockIdx.x % nkt) * XK;
-  const int b = threadIdx.x & 3, lr = threadIdx.x >> 2;        // block within the chunk, row
+  const int b = threadIdx.x % XL, lr = threadIdx.x / XL;       // block within the tile row, row
   const int rl = (int)min(rows - r0, (int64_t)XT);
+  const int kc = (int)min(K - k0, (int64_t)XK);                // K % 128 == 0: whole chunks
+  const bool kok = b * 32 < kc;
   const rsrc_t rq = make_rsrc(q + r0 * (K / 2) + k0 / 2);
   const uint32_t qrow = (uint32_t)(K / 2);
   uint4 qv[XP];
   int eb[XP];
 #pragma unroll
   for (int p = 0; p < XP; ++p) {
-    const int r = p * 64 + lr;
-    const bool ok = r < rl;
+    const int r = p * XPP + lr;
+    const bool ok = kok && r < rl;
     const v4u t = __builtin_amdgcn_raw_buffer_load_b128(rq, ok ? (uint32_t)r * qrow + (uint32_t)(b * 16) : OOB, 0, 0);
     qv[p] = make_uint4(t[0], t[1], t[2], t[3]);
     eb[p] = ok ? (int)s[(r0 + r) * (K / 32) + k0 / 32 + b] : 0;
@@ -256,11 +271,11 @@ __global__ __launch_bounds__(NT) void k_mx_to_fp8(const uint8_t* __restrict__ q,
   const rsrc_t ry = make_rsrc(TRANSPOSE ? y + k0 * rows + r0 : y + r0 * K + k0);
 #pragma unroll
   for (int p = 0; p < XP; ++p) {
-    const int r = p * 64 + lr;
-    const bool ok = r < rl;
-    const int emax = quad_max(eb[p]);
+    const int r = p * XPP + lr;
+    const bool ok = kok && r < rl;
+    const int emax = quad_max(eb[p]);                          // the chunk's four blocks: lanes 4j..4j+3
     const int c = emax - min(6, emax);
-    if (b == 0 && ok) s8[(r0 + r) * (K / XK) + k0 / XK] = (uint8_t)c;
+    if ((b & 3) == 0 && ok) s8[(r0 + r) * (K / XC) + k0 / XC + b / 4] = (uint8_t)c;
     uint32_t out[8];
     block_to_fp8(qv[p], eb[p] - c, out);
     if constexpr (!TRANSPOSE) {
@@ -282,8 +297,8 @@ __global__ __launch_bounds__(NT) void k_mx_to_fp8(const uint8_t* __restrict__ q,
       const int kk = piece / (XT / 16), c16 = piece % (XT / 16);
       const uint4 w = *reinterpret_cast<const uint4*>(&tile[kk][c16 * 16]);
       const v4u wv = {w.x, w.y, w.z, w.w};
-      __builtin_amdgcn_raw_buffer_store_b128(wv, ry, c16 * 16 < rl ? (uint32_t)kk * (uint32_t)rows + (uint32_t)(c16 * 16) : OOB,
-                                             0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(
+          wv, ry, (kk < kc && c16 * 16 < rl) ? (uint32_t)kk * (uint32_t)rows + (uint32_t)(c16 * 16) : OOB, 0, 0);
     }
   }
 }
@@ -333,7 +348,10 @@ static hipError_t dq_layout(const DequantArgs& a) {
 hipError_t run_mx_to_fp8(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t K, bool transpose, uint8_t* y,
                          uint8_t* s8, hipStream_t stream) {
   if (rows == 0 || K == 0) return hipSuccess;
-  const int64_t tiles = ((rows + XT - 1) / XT) * (K / XK);
+  using XA = XTile<true>;
+  using XB = XTile<false>;
+  const int64_t tiles = transpose ? ((rows + XA::T - 1) / XA::T) * ((K + XA::K - 1) / XA::K)
+                                  : ((rows + XB::T - 1) / XB::T) * ((K + XB::K - 1) / XB::K);
   if (transpose)
     hipLaunchKernelGGL(k_mx_to_fp8<true>, dim3((unsigned)tiles), dim3(NT), 0, stream, q, s, rows, K, y, s8);
   else
