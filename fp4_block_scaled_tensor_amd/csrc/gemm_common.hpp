@@ -100,6 +100,18 @@ struct StageLoader {
     off_e = (uint32_t)((l >> 3) * ldq) + pos_e * 16;
     off_o = (uint32_t)((l >> 3) * ldq) + (pos_e ^ 4) * 16;
   }
+  // stage st into lds when every row of the tile is inside the matrix and K is a multiple
+  // of 256 (no clamping): scalar piece base + per-lane offset
+  __device__ __forceinline__ void issue_interior(int64_t st, uint8_t* lds) const {
+    const int w = wave_id();
+    const uint8_t* b = base + st * ROWB;
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const int piece = w * P + j;
+      const bool odd = (P % 2 == 0) ? (j & 1) : (piece & 1);
+      lds_dma16(b + (int64_t)piece * 8 * ldq, odd ? off_o : off_e, lds_offset(lds + piece * 1024));
+    }
+  }
   // stage st into lds; only the last stage of a K that is not a multiple of 256 clamps chunks
   __device__ __forceinline__ void issue(int64_t st, uint8_t* lds) const {
     const int w = wave_id();

@@ -21,8 +21,9 @@
 // |e0 - e1| of its 64 rows. While the A rows' and B rows' largest gaps sum to at most 10,
 // every group of the stage passes and the tile runs branch-free stages whose additions are
 // plain float adds (the K loop runs in round-toward-zero mode and contains no other
-// rounding-sensitive operation). From the first stage that fails, the tile finishes in a
-// simple loop that tests each group.
+// rounding-sensitive operation). A stage that fails runs as a simple loop that tests each
+// group, and the next stage goes back to the stage test (outlier channels fail only the
+// stages that hold them).
 //
 // The per-group float32 add bounds this kernel: 16 v_add_f32 per lane per 32x32x64 MFMA,
 // which the vector ALU issues in about the time the matrix core takes for the MFMA, and
@@ -80,8 +81,15 @@ struct ScaleStager {
     }
     return make_uint4(h[0], h[1], h[2], h[3]);
   }
+  // interior form (K a multiple of 256, 8-byte aligned scales): the stage's 8 bytes in one
+  // load, as two words (groups 0-1, groups 2-3)
+  __device__ __forceinline__ uint4 load8(int64_t st) const {
+    const uint2 v = *reinterpret_cast<const uint2*>(p + st * SCB);
+    return make_uint4(v.x, v.y, 0u, 0u);
+  }
+  template <bool INTERIOR>
   __device__ __forceinline__ static void split(uint4 q, uint32_t& h0, uint32_t& h1, int& gap) {
-    const uint32_t x = q.x | (q.y << 16), y = q.z | (q.w << 16);
+    const uint32_t x = INTERIOR ? q.x : (q.x | (q.y << 16)), y = INTERIOR ? q.y : (q.z | (q.w << 16));
     h0 = __builtin_amdgcn_perm(y, x, 0x06040200u);
     h1 = __builtin_amdgcn_perm(y, x, 0x07050301u);
     gap = 0;
@@ -199,7 +207,9 @@ __device__ __forceinline__ void plain_stage(const uint8_t* la, const uint8_t* lb
                                             const uint32_t (&sa)[TM], const uint32_t (&sb)[TN], bool check,
                                             int g_end, const uint32_t* sw, int nr, int ra0, int rb0, int bm,
                                             int half, v16f (&acc)[TM][TN]) {
-  for (int g = 0; g < g_end; ++g) {
+#pragma unroll
+  for (int g = 0; g < SGR; ++g) {
+    if (g >= g_end) break;
     const bool gf = !check || group_gap_sum<TM, TN>(sw, nr, ra0, rb0, bm, g) <= 10;
     if (gf) {
       v8i fa[TM], fb[TN];
@@ -240,7 +250,9 @@ struct MxSmem {
   int gmax[2][NR / 64];       // [buf][staging wave] largest in-group exponent gap of its rows
 };
 
-template <class TL>
+// INTERIOR: every tile lies inside the matrix, K is a multiple of 256 and the scale rows are
+// 8-byte aligned, so loads need no clamping.
+template <class TL, bool INTERIOR>
 __global__ __launch_bounds__(TL::NT, FP4_MX_MINB) void k_gemm_mx(
     const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const uint8_t* __restrict__ qb,
     const uint8_t* __restrict__ sb, const float* __restrict__ ga, const float* __restrict__ gb, float* __restrict__ c,
@@ -271,13 +283,23 @@ __global__ __launch_bounds__(TL::NT, FP4_MX_MINB) void k_gemm_mx(
   else SS.init(sb, n0 + t - BM, N, nblk);
   uint4 sraw = make_uint4(0, 0, 0, 0);   // the next stage's scale bytes, in flight during a stage
   auto load_scales = [&](int64_t st) {
-    if (stager) sraw = SS.load(st);
+    if (stager) sraw = INTERIOR ? SS.load8(st) : SS.load(st);
+  };
+  auto issue_stage = [&](int64_t st, int buf) {
+    if (INTERIOR) {
+      LA.issue_interior(st, sm.a[buf]);
+      LB.issue_interior(st, sm.b[buf]);
+    } else {
+      LA.issue(st, sm.a[buf]);
+      LB.issue(st, sm.b[buf]);
+    }
+    load_scales(st);
   };
   auto store_scales = [&](int buf) {
     if (stager) {
       uint32_t h0, h1;
       int gap;
-      ScaleStager::split(sraw, h0, h1, gap);
+      ScaleStager::split<INTERIOR>(sraw, h0, h1, gap);
       sm.sw[buf][0][t] = h0;
       sm.sw[buf][1][t] = h1;
       const int gm = wave_max_i(gap);
@@ -294,11 +316,8 @@ __global__ __launch_bounds__(TL::NT, FP4_MX_MINB) void k_gemm_mx(
     return __builtin_amdgcn_readfirstlane(gA) + __builtin_amdgcn_readfirstlane(gB) <= 10;
   };
 
-  if (nstages > 0) {
-    LA.issue(0, sm.a[0]);
-    LB.issue(0, sm.b[0]);
-  }
-  load_scales(0);
+  if (nstages > 0) issue_stage(0, 0);
+  else load_scales(0);
   store_scales(0);
   wait_vm();
   __syncthreads();
@@ -316,17 +335,13 @@ __global__ __launch_bounds__(TL::NT, FP4_MX_MINB) void k_gemm_mx(
 #pragma unroll
     for (int j = 0; j < TN; ++j) pin(acc[i][j]);   // additions after the switch
 
-  int64_t st = 0;
-  // full stages whose every group passes: one MFMA per group partial
-  for (; st < nfull; ++st) {
+  // A full stage whose every group passes: one MFMA per group partial. Returns false, having
+  // done nothing, when the stage fails the test.
+  auto fast_step = [&](int64_t st) -> bool {
     const int buf = (int)(st & 1);
-    if (!stage_passes(buf)) break;
+    if (!stage_passes(buf)) return false;
     const bool more = st + 1 < nstages;
-    if (more) {
-      LA.issue(st + 1, sm.a[buf ^ 1]);
-      LB.issue(st + 1, sm.b[buf ^ 1]);
-      load_scales(st + 1);
-    }
+    if (more) issue_stage(st + 1, buf ^ 1);
     uint32_t s4a[TM], s4b[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) s4a[i] = sm.sw[buf][half][ra0 + i * 32];
@@ -338,17 +353,21 @@ __global__ __launch_bounds__(TL::NT, FP4_MX_MINB) void k_gemm_mx(
       wait_vm();
       __syncthreads();
     }
-  }
-  // the rest (a stage that failed, then every later one, and a partial last stage): each
-  // group tested on its own
-  for (; st < nstages; ++st) {
+    return true;
+  };
+
+  int64_t st = 0;
+  for (;;) {
+    // full stages that pass
+    for (; st < nfull; ++st) {
+      if (!fast_step(st)) break;
+    }
+    if (st >= nstages) break;
+    // one stage that failed the test (or the partial last stage): each group tested on its
+    // own; the stage after it goes back to the test above
     const int buf = (int)(st & 1);
     const bool more = st + 1 < nstages;
-    if (more) {
-      LA.issue(st + 1, sm.a[buf ^ 1]);
-      LB.issue(st + 1, sm.b[buf ^ 1]);
-      load_scales(st + 1);
-    }
+    if (more) issue_stage(st + 1, buf ^ 1);
     uint32_t s4a[TM], s4b[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) s4a[i] = sm.sw[buf][half][ra0 + i * 32];
@@ -362,6 +381,7 @@ __global__ __launch_bounds__(TL::NT, FP4_MX_MINB) void k_gemm_mx(
       wait_vm();
       __syncthreads();
     }
+    ++st;
   }
   store_tiles<TM, TN>(c, M, N, m0 + wm * (TM * 32), n0 + wn * (TN * 32), acc, ga, gb, canon, epi);
 }
@@ -375,9 +395,11 @@ hipError_t run_gemm_mx(const GemmArgs& g) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
   using TL = MxTiling;
   const int64_t tiles = ((g.M + TL::BM - 1) / TL::BM) * ((g.N + TL::BN - 1) / TL::BN);
-  hipLaunchKernelGGL(k_gemm_mx<TL>, dim3((unsigned)tiles), dim3(TL::NT), 0, g.stream, g.a.q, g.a.s, g.b.q, g.b.s,
-                     g.a.g, g.b.g, g.c, g.M, g.N, g.K, g.canon,
-                     epilogue_word(g.hadamard_n, g.a.g_shift, g.b.g_shift));
+  const bool interior = g.M % TL::BM == 0 && g.N % TL::BN == 0 && g.K > 0 && g.K % KS == 0 &&
+                        reinterpret_cast<uintptr_t>(g.a.s) % 8 == 0 && reinterpret_cast<uintptr_t>(g.b.s) % 8 == 0;
+  auto kern = interior ? k_gemm_mx<TL, true> : k_gemm_mx<TL, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(TL::NT), 0, g.stream, g.a.q, g.a.s, g.b.q, g.b.s, g.a.g,
+                     g.b.g, g.c, g.M, g.N, g.K, g.canon, epilogue_word(g.hadamard_n, g.a.g_shift, g.b.g_shift));
   return hipGetLastError();
 }
 
