@@ -362,6 +362,12 @@ def main():
     rc_bpe = 2 + 2 * (0.5 + 1.0 / step_obj.block)
     rc_gbs = M_TOK * K_IN * rc_bpe / (rc_ms * 1e-3) / 1e9
     extra = next_rows(torch, fp4, Xrot, step_obj, args)
+    # measured HBM reference on the same rotated inputs: a plain device copy of the activation
+    # (2 B/elem read + 2 written)
+    cp_ms, _ = graph_time_ms(torch, lambda i: Xrot[i].clone(), lambda o: True)
+    hbm_ref = {"copy_GBps": round(M_TOK * K_IN * 4 / (cp_ms * 1e-3) / 1e9, 1),
+               "kernel": "device copy of the 8192x4096 bf16 activation (torch clone)",
+               "timing": f"graph replay of 20 calls, inputs rotated over {NROT} copies"}
     del Xrot
     flop_gemm = 2.0 * M_TOK * N_OUT * K_IN
     step_flops = 3 * flop_gemm
@@ -403,6 +409,7 @@ def main():
                              "avg_ms": round(rc_ms, 4), "replay_matches_eager": rc_ok,
                              "in_step_avg_ms": None if args.separate else round(quant_ms_step, 4)},
         "next_rows": extra,
+        "hbm_reference": hbm_ref,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:

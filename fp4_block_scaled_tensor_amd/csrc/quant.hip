@@ -21,8 +21,8 @@
 //   k_quant_2d    TILE2D: a 64x64 tile in LDS; tile amaxes by lane shuffles; both the forward
 //                 payload (row segments) and the transposed payload (column segments).
 //   k_amax_*      max|x| (plain, or along-token FWHT for Hadamard views): a workgroup max, then
-//                 one atomicMax per workgroup on the float bits (non-negative floats order like
-//                 unsigned integers).
+//                 at most one atomicMax per workgroup on the float bits (non-negative floats
+//                 order like unsigned integers), skipped when the result already holds more.
 // The quantize kernels also write the operand's g (workgroup 0, thread 0) and, if asked,
 // fold their block maxima into the observed amax (one atomic per workgroup).
 #include <type_traits>
@@ -581,17 +581,39 @@ __global__ __launch_bounds__(NT) void k_quant_2d(const void* __restrict__ x, int
 }
 
 // ---------------------------------------------------------------- amax
+// Each thread reads AMAX_P consecutive 8-element pieces (64 contiguous bytes of bf16) of AMAX_R
+// adjacent rows per pass, all AMAX_R * AMAX_P loads issued before any is used: a wave covers
+// 4 KB runs of a row, as the quantizers do.
+constexpr int AMAX_P = 4;
+constexpr int AMAX_R = 2;
+
 template <bool F32>
 __global__ __launch_bounds__(NT) void k_amax_plain(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
                                                    float* __restrict__ out) {
   float m = 0.0f;
   const int64_t chunks = cols / 8;            // cols % 8 == 0 (validated)
-  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
-    for (int64_t c = (int64_t)blockIdx.x * NT + threadIdx.x; c < chunks; c += (int64_t)gridDim.x * NT) {
-      float v[8];
-      load8<F32>(x, r * ld + c * 8, v);
+  const int64_t ry = (int64_t)gridDim.y * AMAX_R;
+  for (int64_t p0 = ((int64_t)blockIdx.x * NT + threadIdx.x) * AMAX_P; p0 < chunks;
+       p0 += (int64_t)gridDim.x * NT * AMAX_P) {
+    for (int64_t r = (int64_t)blockIdx.y * AMAX_R; r < rows; r += ry) {
+      float v[AMAX_R][AMAX_P][8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+      for (int u = 0; u < AMAX_R; ++u)
+#pragma unroll
+        for (int p = 0; p < AMAX_P; ++p) {
+          if (r + u < rows && p0 + p < chunks) {
+            load8<F32>(x, (r + u) * ld + (p0 + p) * 8, v[u][p]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[u][p][j] = 0.0f;
+          }
+        }
+#pragma unroll
+      for (int u = 0; u < AMAX_R; ++u)
+#pragma unroll
+        for (int p = 0; p < AMAX_P; ++p)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[u][p][j]));
     }
   }
   wg_max_to(out, m);
@@ -831,11 +853,13 @@ hipError_t run_amax(const void* x, bool f32, int64_t rows, int64_t cols, int64_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || rows == 0 || cols == 0) return e;
   if (hadamard_n == 0) {
-    // a bounded grid (at most 16 x 256 workgroups), each striding over many rows: one atomic
-    // per workgroup
+    // a bounded grid (at most 16 x 2048 workgroups), each thread taking AMAX_P pieces of
+    // AMAX_R rows per pass: at most one atomic per workgroup
     const int64_t chunks = cols / 8;
-    const unsigned gx = (unsigned)((chunks + NT - 1) / NT > 16 ? 16 : (chunks + NT - 1) / NT);
-    const unsigned gy = (unsigned)(rows < 256 ? rows : 256);
+    const int64_t cx = (chunks + (int64_t)NT * AMAX_P - 1) / ((int64_t)NT * AMAX_P);
+    const unsigned gx = (unsigned)(cx > 16 ? 16 : cx);
+    const int64_t ry = (rows + AMAX_R - 1) / AMAX_R;
+    const unsigned gy = (unsigned)(ry < 2048 ? ry : 2048);
     if (f32) hipLaunchKernelGGL(k_amax_plain<true>, dim3(gx, gy), dim3(NT), 0, stream, x, rows, cols, ld, out);
     else hipLaunchKernelGGL(k_amax_plain<false>, dim3(gx, gy), dim3(NT), 0, stream, x, rows, cols, ld, out);
     return hipGetLastError();

@@ -15,8 +15,13 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// The atomic is skipped when the word already holds at least v (a relaxed device-scope read:
+// the word only grows, so a stale read can only cause an unneeded atomic). Same-address atomics
+// from many workgroups serialise; most workgroups of a large grid now issue none.
 __device__ __forceinline__ void atomic_max_nonneg(float* p, float v) {
-  atomicMax(reinterpret_cast<unsigned int*>(p), __float_as_uint(v));
+  unsigned int* w = reinterpret_cast<unsigned int*>(p);
+  const unsigned int cur = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (__float_as_uint(v) > cur) atomicMax(w, __float_as_uint(v));
 }
 
 // Workgroup max of a non-negative value folded into *out with one atomic (all NT threads call).

@@ -50,6 +50,24 @@ def test_group_model_stress(fmt, block, spread, M, N, K, canon):
     assert_f32_bits_equal(got, want, f"fmt={fmt} B={block} spread={spread} {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(256, 128, 2048), (200, 136, 1280), (128, 384, 4096)])
+def test_mxfp4_outlier_blocks_then_fast_stages(M, N, K):
+    """MXFP4 operands with narrow scale spreads except a few K-blocks of A raised by 2^7 (an
+    outlier channel): the stages holding them fail the exponent-gap test and run group by
+    group, the stages after them pass again. Covers whole-tile shapes (the unclamped interior
+    form) and ragged ones."""
+    rng = np.random.default_rng(M + N + K)
+    qa = random_operand(rng, M, K, OF.E8M0, 32, 1, zero_frac=0.05)
+    qb = random_operand(rng, N, K, OF.E8M0, 32, 2)
+    nb = K // 32
+    for blk in sorted(set(rng.integers(0, nb, 3).tolist()) | {nb // 2 + 1}):
+        qa.scales[:, blk] = (qa.scales[:, blk].astype(np.int32) + 7).astype(np.uint8)
+    want = _oracle_y(qa, qb)
+    got = fp4.gemm_fprop(qtensor_from_oracle(qa), qtensor_from_oracle(qb))
+    torch.cuda.synchronize()
+    assert_f32_bits_equal(got, want, f"outlier blocks {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("fmt", [OF.UE5M3, OF.E4M3])
 def test_zero_and_subnormal_scale_codes(fmt):
     """Hand-built operands whose block-scale codes include 0 (the value 0: the quantizer never
