@@ -240,9 +240,9 @@ fp4_status fp4_quantize_rowcol(const void* x, int32_t x_dtype, int64_t rows, int
       return fail(FP4_EALIGN, "x, q and q_t must be 16-byte aligned");
     if ((ld * esz) % 16) return fail(FP4_EALIGN, "row stride must be a multiple of 16 bytes");
   }
-  // 32-bit lane offsets inside a 128 x 64 tile
-  if (ld * esz > (int64_t(1) << 24) || rows > (int64_t(1) << 25) || cols > (int64_t(1) << 25))
-    return fail(FP4_EUNSUPPORTED, "rowcol: needs ld*elem_size <= 2^24 bytes and rows, cols <= 2^25");
+  // 32-bit lane offsets inside a tile (at most 128 token rows, 256 feature rows of x^T)
+  if (ld * esz > (int64_t(1) << 24) || rows > (int64_t(1) << 24) || cols > (int64_t(1) << 25))
+    return fail(FP4_EUNSUPPORTED, "rowcol: needs ld*elem_size <= 2^24 bytes, rows <= 2^24 and cols <= 2^25");
   if (cfg_row->fmt != FP4_E8M0 && (!d_amax_row || !d_amax_col))
     return fail(FP4_EINVAL, "UE5M3/E4M3 need the cached amax of both views");
   for (const float* p : {(const float*)d_amax_row, (const float*)d_amax_col, (const float*)d_g, (const float*)d_g_t,

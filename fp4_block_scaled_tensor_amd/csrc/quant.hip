@@ -221,18 +221,35 @@ __global__ __launch_bounds__(NT) void k_quant_col(const void* __restrict__ x, in
 // operand (COL view, optionally Hadamard-rotated), each with its own cached amax, T and
 // rounding.
 //
-// A workgroup owns a 64-token x 128-feature tile. Lane l of a pass loads the 8 elements
-// [8(l%16), 8(l%16)+8) of token row l/16 (sixteen lanes read one 256-byte bf16 row segment;
-// wider segments read faster than the 128-byte ones of a 128 x 64 tile, and 64 tokens still
-// hold two 32-token COL units), so the ROW blocks are finished in registers: a block spans
-// B/8 neighbouring lanes, whose maxima are combined with DPP quad permutes. The tile is then
-// written to LDS in the input's own type (bf16 or float; 16 or 32 KB) for the COL view,
-// whose payload is transposed through a small LDS tile as in the COL kernel. Workgroups are
-// ordered so that each XCD walks the feature tiles of a token stripe in turn: the partial
-// 128-byte lines each tile writes are completed in that XCD's L2 before they are written
-// back.
-constexpr int RT = 64;    // tokens per fused tile
-constexpr int RF = 128;   // features per fused tile
+// A workgroup owns a tile of RT tokens x RF features (RcTile below). Lane l of a pass loads
+// the 8 elements [8(l%L), 8(l%L)+8) of token row l/L, L = RF/8 lanes per row (a nearest-even
+// tile reads 512-byte bf16 row segments, which stream from HBM faster than narrower ones),
+// so the ROW blocks are finished in registers: a block spans B/8 neighbouring lanes, whose
+// maxima are combined with DPP quad permutes. The tile is then written to LDS in the
+// input's own type for the COL view, whose payload is transposed through a small LDS tile as
+// in the COL kernel. Workgroups are ordered so that each XCD walks the feature tiles of a
+// token stripe in turn: the partial 128-byte lines each tile writes are completed in that
+// XCD's L2 before they are written back.
+// Tile shape (tokens x features): nearest-even tiles of 64 x 256 (512-byte row segments; the
+// loads dominate, and wider segments stream faster from HBM); stochastic ones, bound by the
+// Philox and rounding arithmetic, 128 x 64.
+#ifndef FP4_RC_RT
+#define FP4_RC_RT 64
+#endif
+#ifndef FP4_RC_RF
+#define FP4_RC_RF 256
+#endif
+#ifndef FP4_RC_RT_SR
+#define FP4_RC_RT_SR 128
+#endif
+#ifndef FP4_RC_RF_SR
+#define FP4_RC_RF_SR 64
+#endif
+template <bool SR>
+struct RcTile {
+  static constexpr int T = SR ? FP4_RC_RT_SR : FP4_RC_RT;   // tokens per fused tile
+  static constexpr int F = SR ? FP4_RC_RF_SR : FP4_RC_RF;   // features per fused tile
+};
 
 // Persistent: gridDim.x workgroups walk the tiles. When the tile count and the grid are
 // multiples of 8, workgroup w (on XCD w % 8) takes tiles k*P + w/8 + i*(gridDim.x/8) of
@@ -249,8 +266,12 @@ __global__ __launch_bounds__(NT) void k_quant_rowcol(const void* __restrict__ x,
                                                      float* __restrict__ obs_r, uint8_t* __restrict__ qt,
                                                      uint8_t* __restrict__ st, float* __restrict__ g_c,
                                                      float* __restrict__ obs_c) {
+  constexpr int RT = RcTile<SRR || SRC>::T, RF = RcTile<SRR || SRC>::F;
   constexpr int U = (HN > B) ? HN : B;          // COL tokens per thread unit
   constexpr int UNITS = RT / U;
+  static_assert(RF <= NT && NT % RF == 0 && RT % U == 0 && RT % 16 == 0, "COL units: whole features per thread");
+  static_assert((RF * (RT / 16)) % NT == 0 && (RF * (RT / B)) % NT == 0, "COL stores: whole passes");
+  static_assert(NT % (RF / 8) == 0 && RT % (NT / (RF / 8)) == 0, "ROW loads: whole passes");
   constexpr int LPR = RF / 8;                   // lanes per tile row (8 elements each)
   constexpr int RPP = NT / LPR;                 // token rows per load pass
   constexpr int PASSES = RT / RPP;
@@ -694,6 +715,7 @@ static hipError_t launch_col(const QuantArgs& a) {
 
 template <int FMT, int B, bool SRR, bool SRC, bool F32, int HN>
 static hipError_t launch_rowcol(const RowColArgs& a) {
+  constexpr int RT = RcTile<SRR || SRC>::T, RF = RcTile<SRR || SRC>::F;
   const int64_t tiles = ((a.rows + RT - 1) / RT) * ((a.cols + RF - 1) / RF);
   // one resident wave of workgroups (rounded down to a multiple of 8 XCDs), or fewer
   static const int per_cu = [] {

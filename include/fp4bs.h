@@ -158,7 +158,7 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t co
  *   d_g, d_g_t, d_amax_obs_row, d_amax_obs_col  optional device float outputs, as in
  *            fp4_quantize
  * Requires the shape conditions of both views: cols % B == 0, rows % B == 0 and
- * rows % hadamard_n == 0; also ld * elem_size <= 2^24 bytes and rows, cols <= 2^25
+ * rows % hadamard_n == 0; also ld * elem_size <= 2^24 bytes, rows <= 2^24 and cols <= 2^25
  * (FP4_EUNSUPPORTED otherwise). Empty tensors are a no-op (g values are still written).
  */
 fp4_status fp4_quantize_rowcol(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld,
