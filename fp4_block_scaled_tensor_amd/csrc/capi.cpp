@@ -151,7 +151,9 @@ fp4_status gemm_common(const fp4_operand* a, const fp4_operand* b, float* c, int
   g.hadamard_n = hadamard_n;
   g.stream = (hipStream_t)stream;
   if (g.M == 0 || g.N == 0) return ok();
-  const hipError_t e = (g.fmt == FP4_E8M0) ? fp4k::run_gemm_mx(g) : fp4k::run_gemm_dec16(g);
+  // K = 0: every output is an empty sum, +0 after canonicalisation and the output scale
+  const hipError_t e = g.K == 0 ? fp4k::run_fill(c, 0.0f, g.M * g.N, g.stream)
+                                : (g.fmt == FP4_E8M0) ? fp4k::run_gemm_mx(g) : fp4k::run_gemm_dec16(g);
   return hip_status(e, what);
 }
 

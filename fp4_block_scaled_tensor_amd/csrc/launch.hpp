@@ -3,7 +3,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace fp4k {
+
+// compute units of the current device (cached per device; 256 on MI355X)
+inline int device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 struct QuantArgs {
   const void* x;
@@ -125,6 +139,7 @@ hipError_t run_cache_reset(int32_t* valid, hipStream_t stream);
 hipError_t run_debug_encode(const float* x, const uint16_t* u16, int64_t n, int which, uint8_t* out,
                             hipStream_t stream);
 hipError_t run_gemm_mx(const GemmArgs& g);      // E8M0, block 32
+hipError_t run_fill(float* p, float v, int64_t n, hipStream_t stream);   // p[0, n) = v (a kernel, no memset)
 hipError_t run_gemm_dec16(const GemmArgs& g);   // UE5M3 / E4M3, block 16 or 32
 
 }  // namespace fp4k

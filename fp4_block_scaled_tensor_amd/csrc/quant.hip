@@ -532,6 +532,13 @@ __global__ void k_fill_n(float* __restrict__ p, float v, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
+hipError_t run_fill(float* p, float v, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + NT - 1) / NT;
+  hipLaunchKernelGGL(k_fill_n, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(NT), 0, stream, p, v, n);
+  return hipGetLastError();
+}
+
 // g[i] holds stripe i's amax on entry and its decode scale g on exit.
 __global__ void k_stripe_finalize(float* __restrict__ g, float* __restrict__ amax_out, int64_t n, float T) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {

@@ -143,16 +143,5 @@ struct Chunk8 {
   }
 };
 
-// compute units of the current device (cached per device; 256 on MI355X)
-inline int device_cu_count() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n > 0) return n;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
-  cached[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
 
 }  // namespace fp4k

@@ -263,7 +263,7 @@ fp4_status amax_cache_reset(const fp4_amax_cache* cache, void* stream);
  *   tile-local operands g_a = a->g[m / a->g_stripe], g_b = b->g[n / b->g_stripe].
  * Exact results require every block partial and group sum to stay inside the float32
  * normal range (always true for UE5M3/E4M3; for E8M0, combined block exponents within
- * about +-100).
+ * about +-100). K = 0 writes +0 to every output (an empty sum).
  *
  * fp4_gemm_fprop: Y = X . W^T. x: ROW-view activation (1D scales); w: weight forward view
  *                 (TILE2D q with FP4_SCALES_2D, or a ROW-view weight with 1D scales).

@@ -68,6 +68,17 @@ def test_mxfp4_outlier_blocks_then_fast_stages(M, N, K):
     assert_f32_bits_equal(got, want, f"outlier blocks {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("fmt,block", [(OF.UE5M3, 16), (OF.E8M0, 32)])
+def test_empty_k_writes_zeros(fmt, block):
+    """K = 0: every output is an empty sum, +0 (the output buffer starts non-zero)."""
+    qa = random_operand(np.random.default_rng(3), 64, 0, fmt, block, 1)
+    qb = random_operand(np.random.default_rng(4), 40, 0, fmt, block, 1)
+    out = torch.full((64, 40), 7.0, dtype=torch.float32, device="cuda")
+    got = fp4.gemm_fprop(qtensor_from_oracle(qa), qtensor_from_oracle(qb), out=out)
+    torch.cuda.synchronize()
+    assert_f32_bits_equal(got, np.zeros((64, 40), np.float32), f"K=0 fmt={fmt}")
+
+
 @pytest.mark.parametrize("fmt", [OF.UE5M3, OF.E4M3])
 def test_zero_and_subnormal_scale_codes(fmt):
     """Hand-built operands whose block-scale codes include 0 (the value 0: the quantizer never
