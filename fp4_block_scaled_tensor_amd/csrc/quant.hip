@@ -496,6 +496,80 @@ __global__ __launch_bounds__(NT) void k_quant_row_local(const void* __restrict__
   }
 }
 
+// Register-resident form for bf16 stripes of at most 65536 elements (e.g. 16 rows of 4096),
+// 1024-thread workgroups: each thread loads up to 64 / B whole blocks of the stripe once
+// (16-byte chunks, lanes on consecutive blocks), reduces the stripe maximum from the
+// registers (the magnitude of a bf16 orders like its low 15 bits, so a packed 16-bit integer
+// max gives it two elements at a time), then quantizes the same registers: the stripe is
+// read from HBM once.
+constexpr int NTL = 1024;
+constexpr int LOCAL_REG_ELEMS = NTL * 64;
+template <int FMT, int B, bool SR>
+__global__ __launch_bounds__(NTL) void k_quant_row_local_reg(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                               int64_t ld, int stripe_log2, float T, uint64_t seed,
+                                                               uint64_t offset, uint8_t* __restrict__ q,
+                                                               uint8_t* __restrict__ s, float* __restrict__ g_out,
+                                                               float* __restrict__ amax_out) {
+  constexpr int BPT = 64 / B;    // blocks per thread
+  constexpr int CPB = B / 8;     // 16-byte chunks per block
+  __shared__ uint32_t part[NTL / 64];
+  const int64_t r0 = (int64_t)blockIdx.x << stripe_log2;
+  const int64_t nr = min((int64_t)1 << stripe_log2, rows - r0);
+  const int64_t nb = cols / B, nblk = nr * nb;   // nblk <= BPT * NTL (checked by the launcher)
+  uint4 raw[BPT][CPB];
+#pragma unroll
+  for (int u = 0; u < BPT; ++u) {
+    // 32-bit index arithmetic: i < nblk <= 65536 / B
+    const uint32_t i = (uint32_t)(u * NTL) + threadIdx.x, rr = i / (uint32_t)nb, bb = i - rr * (uint32_t)nb;
+    if (i < (uint32_t)nblk) {
+      const uint16_t* p = reinterpret_cast<const uint16_t*>(x) + (r0 + rr) * ld + (int64_t)bb * B;
+#pragma unroll
+      for (int c = 0; c < CPB; ++c) raw[u][c] = *reinterpret_cast<const uint4*>(p + 8 * c);
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPB; ++c) raw[u][c] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  uint32_t mm = 0;
+#pragma unroll
+  for (int u = 0; u < BPT; ++u)
+#pragma unroll
+    for (int c = 0; c < CPB; ++c) {
+      const uint4 w = raw[u][c];
+      const uint32_t a = pk_max_u16(w.x & 0x7FFF7FFFu, w.y & 0x7FFF7FFFu);
+      const uint32_t b = pk_max_u16(w.z & 0x7FFF7FFFu, w.w & 0x7FFF7FFFu);
+      mm = pk_max_u16(mm, pk_max_u16(a, b));
+    }
+  uint32_t m = max(mm & 0xFFFFu, mm >> 16);   // bf16 magnitude bits
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, k));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  uint32_t mb = part[0];
+#pragma unroll
+  for (int i = 1; i < NTL / 64; ++i) mb = max(mb, part[i]);
+  const float A = __uint_as_float(mb << 16);
+  const TensorScales ts = tensor_scales_from(A, T);
+  if (threadIdx.x == 0) {
+    g_out[blockIdx.x] = ts.g;
+    if (amax_out) amax_out[blockIdx.x] = A;
+  }
+#pragma unroll
+  for (int u = 0; u < BPT; ++u) {
+    const uint32_t i = (uint32_t)(u * NTL) + threadIdx.x, rr = i / (uint32_t)nb, bb = i - rr * (uint32_t)nb;
+    if (i < (uint32_t)nblk) {
+      float v[B];
+#pragma unroll
+      for (int c = 0; c < CPB; ++c) {
+        const uint4 w = raw[u][c];
+        v[8 * c + 0] = bf16_lo(w.x); v[8 * c + 1] = bf16_hi(w.x); v[8 * c + 2] = bf16_lo(w.y); v[8 * c + 3] = bf16_hi(w.y);
+        v[8 * c + 4] = bf16_lo(w.z); v[8 * c + 5] = bf16_hi(w.z); v[8 * c + 6] = bf16_lo(w.w); v[8 * c + 7] = bf16_hi(w.w);
+      }
+      quant_block_row<FMT, B, SR>(v, ts, r0 + rr, (int64_t)bb, cols, seed, offset, q, s);
+    }
+  }
+}
+
 // Two-pass form for stripes too few to fill the chip with one workgroup each: the stripe
 // maxima are reduced by workgroups of (column chunk, stripe) into amax[stripe] (zeroed first;
 // one atomic per workgroup), the row quantizer then reads them (LOCAL mode), and
@@ -508,16 +582,17 @@ __global__ __launch_bounds__(NT) void k_stripe_amax(const void* __restrict__ x, 
   const int64_t nr = min((int64_t)1 << stripe_log2, rows - r0);
   const int64_t c0 = (int64_t)blockIdx.x * chunk_cols;
   const int64_t cw = min(chunk_cols, cols - c0) / 8;        // 8-element chunks per row of the piece
-  const int64_t n = nr * cw;
+  // 32-bit index arithmetic: n <= 128 rows x 64 chunks
+  const uint32_t n = (uint32_t)(nr * cw), cw32 = (uint32_t)cw;
   constexpr int UL = 4;
   float m = 0.0f;
-  for (int64_t i0 = threadIdx.x; i0 < n; i0 += UL * NT) {
+  for (uint32_t i0 = threadIdx.x; i0 < n; i0 += UL * NT) {
     float v[UL][8];
 #pragma unroll
     for (int u = 0; u < UL; ++u) {
-      int64_t i = i0 + u * NT;
+      uint32_t i = i0 + u * NT;
       i = i < n ? i : n - 1;                                 // a repeated chunk does not change the max
-      const int64_t r = i / cw, k = (i - r * cw) * 8;
+      const uint32_t r = i / cw32, k = (i - r * cw32) * 8;
       load8<F32>(x, (r0 + r) * ld + c0 + k, v[u]);
     }
 #pragma unroll
@@ -785,6 +860,13 @@ hipError_t run_quantize_rowcol(const RowColArgs& a) {
 template <int FMT, int B, bool SR, bool F32>
 static hipError_t launch_local(const LocalQuantArgs& a) {
   const int64_t stripes = (a.rows + ((int64_t)1 << a.stripe_log2) - 1) >> a.stripe_log2;
+  if (stripes >= 2 * (int64_t)device_cu_count() && !F32 &&
+      ((int64_t)1 << a.stripe_log2) * a.cols <= (int64_t)LOCAL_REG_ELEMS) {
+    // enough stripes to fill the chip, each small enough to stay in registers: one read
+    hipLaunchKernelGGL((k_quant_row_local_reg<FMT, B, SR>), dim3((unsigned)stripes), dim3(NTL), 0, a.stream, a.x,
+                       a.rows, a.cols, a.ld, a.stripe_log2, a.T, a.seed, a.offset, a.q, a.s, a.g, a.amax);
+    return hipGetLastError();
+  }
   if (stripes >= 2 * (int64_t)device_cu_count()) {
     // enough stripes to fill the chip: one workgroup per stripe, one pass
     hipLaunchKernelGGL((k_quant_row_local<FMT, B, SR, F32>), dim3((unsigned)stripes), dim3(NT), 0, a.stream, a.x,

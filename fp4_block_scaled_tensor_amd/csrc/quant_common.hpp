@@ -24,6 +24,13 @@ __device__ __forceinline__ void atomic_max_nonneg(float* p, float v) {
   if (__float_as_uint(v) > cur) atomicMax(w, __float_as_uint(v));
 }
 
+// Maximum of each unsigned 16-bit lane of two words (v_pk_max_u16).
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a), __builtin_bit_cast(u16x2_t, b)));
+}
+
 // Workgroup max of a non-negative value folded into *out with one atomic (all NT threads call).
 __device__ __forceinline__ void wg_max_to(float* out, float v) {
   __shared__ float part[NT / 64];

@@ -117,6 +117,27 @@ def test_local_activation_with_global_2d_weight_and_dgrad():
     assert_f32_bits_equal(dx, want, "dgrad local dY x global W^T")
 
 
+@pytest.mark.parametrize("fmt,block,cols,extra_rows,sr,T", [(OF.UE5M3, 32, 256, 5, False, 2048.0),
+                                                          (OF.E4M3, 16, 512, 0, True, 448.0),
+                                                          (OF.UE5M3, 16, 1024, 16, False, 448.0)])
+def test_quantize_local_register_form(fmt, block, cols, extra_rows, sr, T):
+    """At least two 16-row bf16 stripes per compute unit, each at most 65536 elements: the
+    form that keeps a stripe in registers between its maximum and its quantization. Ragged
+    last stripe, block 32, stochastic rounding; every byte, g and the stripe maxima."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rows = 2 * cus * 16 + extra_rows
+    t = _tensor(rows, cols, "bf16", 6200 + cols + extra_rows)
+    ref = oracle.quantize_1d_local(t.values, fmt, block, stripe=16, T=T, rounding="sr" if sr else "rne",
+                                   seed=7, offset=3)
+    obs = torch.empty(len(ref.g), dtype=torch.float32, device="cuda")
+    got = fp4.quantize_local(dev_input(t), fmt, block, stripe=16, T=T, stochastic=sr, seed=7, offset=3, amax_obs=obs)
+    torch.cuda.synchronize()
+    assert_bytes_equal(got.q, oracle.pack_codes(ref.codes), "payload")
+    assert_bytes_equal(got.s, ref.scales, "scales")
+    assert_f32_bits_equal(got.g, ref.g, "g")
+    assert_f32_bits_equal(obs, ref.amax, "stripe amax")
+
+
 def test_full_size_activation_tile_local_sampled():
     """8192 x 4096 activation quantized with stripes of 16 rows (512 stripes) by the
     library; stripes 0-7 and 504-511 checked against the oracle."""
