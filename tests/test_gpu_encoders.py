@@ -42,6 +42,23 @@ def test_e2m1_payload_encoder():
     assert np.array_equal(_run(x, 0), OF.encode_e2m1(x))
 
 
+def test_e2m1_payload_encoder_every_float_in_decision_range():
+    """Every float32 with magnitude in [2^-4, 2^4) (all 2^27 bit patterns of those eight
+    binades, both signs): every E2M1 decision boundary, tie and the saturation edge lies
+    inside this range; outside it the code is 0 or 6 (covered by the sweep above)."""
+    mant = np.arange(1 << 23, dtype=np.uint32)
+    for e in range(-4, 4):
+        for sign in (0, 1):
+            bits = (np.uint32(sign << 31) | (np.uint32(e + 127) << np.uint32(23))) | mant
+            x = bits.view(np.float32)
+            got = _run(x, 0)
+            want = OF.encode_e2m1(x)
+            if not np.array_equal(got, want):
+                bad = np.flatnonzero(got != want)
+                raise AssertionError(f"binade 2^{e} sign {sign}: {bad.size} codes differ, first x={x[bad[0]]!r} "
+                                     f"got {got[bad[0]]} want {want[bad[0]]}")
+
+
 @pytest.mark.parametrize("fmt,which,lo,hi", [(OF.UE5M3, 1, -24, 18), (OF.E4M3, 2, -14, 11)])
 def test_scale_encoders(fmt, which, lo, hi):
     x = np.concatenate([_sweep(lo, hi, 1 << 15, 2 + which), _around(OF.SCALE_VALUES[fmt]),
