@@ -387,7 +387,7 @@ __global__ __launch_bounds__(TL::NT, FP4_MX_MINB) void k_gemm_mx(
 }
 
 #ifndef FP4_MX_TILING
-#define FP4_MX_TILING 2, 4, 2, 1
+#define FP4_MX_TILING 4, 2, 1, 2
 #endif
 using MxTiling = Tiling<FP4_MX_TILING>;
 
