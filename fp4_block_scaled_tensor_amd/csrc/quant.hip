@@ -684,26 +684,23 @@ __global__ __launch_bounds__(NT) void k_quant_2d(const void* __restrict__ x, int
 }
 
 // ---------------------------------------------------------------- amax
-// Each thread reads AMAX_P consecutive 8-element pieces (64 contiguous bytes of bf16) of AMAX_R
-// adjacent rows per pass, all AMAX_R * AMAX_P loads issued before any is used: a wave covers
-// 4 KB runs of a row, as the quantizers do.
-constexpr int AMAX_P = 4;
-constexpr int AMAX_R = 2;
-
-template <bool F32>
+// Each thread reads P consecutive 8-element pieces (16 P contiguous bytes of bf16) of R
+// adjacent rows per pass, all R * P = 8 loads issued before any is used. P is chosen so that
+// NT * P pieces span about one row (no idle lanes on narrow rows), R = 8 / P.
+template <bool F32, int P>
 __global__ __launch_bounds__(NT) void k_amax_plain(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
                                                    float* __restrict__ out) {
+  constexpr int R = 8 / P;
   float m = 0.0f;
   const int64_t chunks = cols / 8;            // cols % 8 == 0 (validated)
-  const int64_t ry = (int64_t)gridDim.y * AMAX_R;
-  for (int64_t p0 = ((int64_t)blockIdx.x * NT + threadIdx.x) * AMAX_P; p0 < chunks;
-       p0 += (int64_t)gridDim.x * NT * AMAX_P) {
-    for (int64_t r = (int64_t)blockIdx.y * AMAX_R; r < rows; r += ry) {
-      float v[AMAX_R][AMAX_P][8];
+  const int64_t ry = (int64_t)gridDim.y * R;
+  for (int64_t p0 = ((int64_t)blockIdx.x * NT + threadIdx.x) * P; p0 < chunks; p0 += (int64_t)gridDim.x * NT * P) {
+    for (int64_t r = (int64_t)blockIdx.y * R; r < rows; r += ry) {
+      float v[R][P][8];
 #pragma unroll
-      for (int u = 0; u < AMAX_R; ++u)
+      for (int u = 0; u < R; ++u)
 #pragma unroll
-        for (int p = 0; p < AMAX_P; ++p) {
+        for (int p = 0; p < P; ++p) {
           if (r + u < rows && p0 + p < chunks) {
             load8<F32>(x, (r + u) * ld + (p0 + p) * 8, v[u][p]);
           } else {
@@ -712,14 +709,25 @@ __global__ __launch_bounds__(NT) void k_amax_plain(const void* __restrict__ x, i
           }
         }
 #pragma unroll
-      for (int u = 0; u < AMAX_R; ++u)
+      for (int u = 0; u < R; ++u)
 #pragma unroll
-        for (int p = 0; p < AMAX_P; ++p)
+        for (int p = 0; p < P; ++p)
 #pragma unroll
           for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[u][p][j]));
     }
   }
   wg_max_to(out, m);
+}
+
+template <bool F32, int P>
+static void launch_amax(const void* x, int64_t rows, int64_t cols, int64_t ld, float* out, hipStream_t stream) {
+  // a bounded grid (at most 16 x 2048 workgroups): at most one atomic per workgroup
+  const int64_t chunks = cols / 8;
+  const int64_t cx = (chunks + (int64_t)NT * P - 1) / ((int64_t)NT * P);
+  const unsigned gx = (unsigned)(cx > 16 ? 16 : cx);
+  const int64_t ry = (rows + 8 / P - 1) / (8 / P);
+  const unsigned gy = (unsigned)(ry < 2048 ? ry : 2048);
+  hipLaunchKernelGGL((k_amax_plain<F32, P>), dim3(gx, gy), dim3(NT), 0, stream, x, rows, cols, ld, out);
 }
 
 template <bool F32, int HN>
@@ -964,15 +972,17 @@ hipError_t run_amax(const void* x, bool f32, int64_t rows, int64_t cols, int64_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || rows == 0 || cols == 0) return e;
   if (hadamard_n == 0) {
-    // a bounded grid (at most 16 x 2048 workgroups), each thread taking AMAX_P pieces of
-    // AMAX_R rows per pass: at most one atomic per workgroup
     const int64_t chunks = cols / 8;
-    const int64_t cx = (chunks + (int64_t)NT * AMAX_P - 1) / ((int64_t)NT * AMAX_P);
-    const unsigned gx = (unsigned)(cx > 16 ? 16 : cx);
-    const int64_t ry = (rows + AMAX_R - 1) / AMAX_R;
-    const unsigned gy = (unsigned)(ry < 2048 ? ry : 2048);
-    if (f32) hipLaunchKernelGGL(k_amax_plain<true>, dim3(gx, gy), dim3(NT), 0, stream, x, rows, cols, ld, out);
-    else hipLaunchKernelGGL(k_amax_plain<false>, dim3(gx, gy), dim3(NT), 0, stream, x, rows, cols, ld, out);
+    if (chunks >= 4 * NT) {
+      if (f32) launch_amax<true, 4>(x, rows, cols, ld, out, stream);
+      else launch_amax<false, 4>(x, rows, cols, ld, out, stream);
+    } else if (chunks >= 2 * NT) {
+      if (f32) launch_amax<true, 2>(x, rows, cols, ld, out, stream);
+      else launch_amax<false, 2>(x, rows, cols, ld, out, stream);
+    } else {
+      if (f32) launch_amax<true, 1>(x, rows, cols, ld, out, stream);
+      else launch_amax<false, 1>(x, rows, cols, ld, out, stream);
+    }
     return hipGetLastError();
   }
   dim3 grid((unsigned)((rows + CT - 1) / CT), (unsigned)((cols + CF - 1) / CF));
