@@ -306,13 +306,19 @@ __global__ __launch_bounds__(TL::NT, FP4_MX_MINB) void k_gemm_mx(
       if (l == 0) sm.gmax[buf][w] = gm;
     }
   };
-  // every group of the stage in buffer buf passes the gap test (wave-uniform)
+  // every group of the stage in buffer buf passes the gap test (wave-uniform).
+  // The test is per wave: it covers the staging waves that hold this wave's TM*32 A rows and
+  // TN*32 B rows (64 rows each), so a wave whose own rows pass runs the fast stage even when
+  // another wave of the workgroup does not. Both stage forms issue the same loads, scale
+  // stores and barrier, so waves may take different forms in the same stage.
   auto stage_passes = [&](int buf) {
+    constexpr int SA = TM * 32 >= 64 ? TM * 32 / 64 : 1, SB = TN * 32 >= 64 ? TN * 32 / 64 : 1;
+    const int a0 = (wm * TM * 32) >> 6, b0 = (BM + wn * TN * 32) >> 6;
     int gA = 0, gB = 0;
 #pragma unroll
-    for (int i = 0; i < BM / 64; ++i) gA = max(gA, sm.gmax[buf][i]);
+    for (int i = 0; i < SA; ++i) gA = max(gA, sm.gmax[buf][a0 + i]);
 #pragma unroll
-    for (int i = BM / 64; i < NR / 64; ++i) gB = max(gB, sm.gmax[buf][i]);
+    for (int i = 0; i < SB; ++i) gB = max(gB, sm.gmax[buf][b0 + i]);
     return __builtin_amdgcn_readfirstlane(gA) + __builtin_amdgcn_readfirstlane(gB) <= 10;
   };
 
