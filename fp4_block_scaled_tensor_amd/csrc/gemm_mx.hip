@@ -247,7 +247,7 @@ struct MxSmem {
   uint8_t a[2][TL::BM * ROWB];
   uint8_t b[2][TL::BN * ROWB];
   uint32_t sw[2][2][NR];      // [buf][K-half][A rows, then B rows]
-  int gmax[2][NR / 64];       // [buf][staging wave] largest in-group exponent gap of its rows
+  int gmax[2][NR / 32];       // [buf][32-row half of a staging wave] largest in-group exponent gap of its rows
 };
 
 // INTERIOR: every tile lies inside the matrix, K is a multiple of 256 and the scale rows are
@@ -302,18 +302,24 @@ __global__ __launch_bounds__(TL::NT, FP4_MX_MINB) void k_gemm_mx(
       ScaleStager::split<INTERIOR>(sraw, h0, h1, gap);
       sm.sw[buf][0][t] = h0;
       sm.sw[buf][1][t] = h1;
-      const int gm = wave_max_i(gap);
-      if (l == 0) sm.gmax[buf][w] = gm;
+      // maxima of the two 32-lane halves (32 rows each)
+      int d = gap;
+      d = max(d, __builtin_amdgcn_ds_swizzle(d, (1 << 10) | 0x1F));
+      d = max(d, __builtin_amdgcn_ds_swizzle(d, (2 << 10) | 0x1F));
+      d = max(d, __builtin_amdgcn_ds_swizzle(d, (4 << 10) | 0x1F));
+      d = max(d, __builtin_amdgcn_ds_swizzle(d, (8 << 10) | 0x1F));
+      d = max(d, __builtin_amdgcn_ds_swizzle(d, (16 << 10) | 0x1F));
+      if ((l & 31) == 0) sm.gmax[buf][2 * w + (l >> 5)] = d;
     }
   };
   // every group of the stage in buffer buf passes the gap test (wave-uniform).
-  // The test is per wave: it covers the staging waves that hold this wave's TM*32 A rows and
-  // TN*32 B rows (64 rows each), so a wave whose own rows pass runs the fast stage even when
+  // The test is per wave: it covers the 32-row staging maxima of this wave's TM*32 A rows and
+  // TN*32 B rows, so a wave whose own rows pass runs the fast stage even when
   // another wave of the workgroup does not. Both stage forms issue the same loads, scale
   // stores and barrier, so waves may take different forms in the same stage.
   auto stage_passes = [&](int buf) {
-    constexpr int SA = TM * 32 >= 64 ? TM * 32 / 64 : 1, SB = TN * 32 >= 64 ? TN * 32 / 64 : 1;
-    const int a0 = (wm * TM * 32) >> 6, b0 = (BM + wn * TN * 32) >> 6;
+    const int a0 = (wm * TM * 32) >> 5, b0 = (BM + wn * TN * 32) >> 5;   // 32-row maxima
+    constexpr int SA = TM, SB = TN;
     int gA = 0, gB = 0;
 #pragma unroll
     for (int i = 0; i < SA; ++i) gA = max(gA, sm.gmax[buf][a0 + i]);
