@@ -140,13 +140,17 @@ struct StageLoader {
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+#ifndef FP4_GEMM_GM
+#define FP4_GEMM_GM 8   // M tiles per group of the tile order
+#endif
+
 // Workgroup id -> (m tile, n tile), XCD-aware grouped order.
 __device__ __forceinline__ void tile_coords(int64_t M, int64_t N, int BM, int BN, int64_t& m0, int64_t& n0) {
   const int64_t ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
   const int64_t T = ntm * ntn;
   int64_t id = blockIdx.x;
   if ((T & 7) == 0) id = (id & 7) * (T >> 3) + (id >> 3);
-  const int64_t GM = 8;
+  const int64_t GM = FP4_GEMM_GM;
   const int64_t gsize = GM * ntn;
   const int64_t gid = id / gsize;
   const int64_t first = gid * GM;
@@ -214,20 +218,38 @@ __device__ __forceinline__ void store_tiles(float* __restrict__ c, int64_t M, in
     asm volatile("" : "+v"(a), "+v"(b));        // keep the scale product after the mode switch
     float alpha = a * b;
     if (hadamard_n) alpha = alpha * hinv;
+    auto value = [&](int rt, int ct, int r) {
+      float v = acc[rt][ct][r] * pre;
+      if (canon) v = __builtin_rintf(v * 1024.0f) * (1.0f / 1024.0f);
+      return v * alpha;
+    };
+    if (m0 + TM * 32 <= M && n0 + TN * 32 <= N) {
+      // the wave's outputs all lie inside C: one per-lane base, and every register's row
+      // offset is a compile-time multiple of N (a scalar product)
+      float* base = c + (m0 + (l >> 5) * 4) * N + n0 + (l & 31);
 #pragma unroll
-    for (int rt = 0; rt < TM; ++rt)
+      for (int rt = 0; rt < TM; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < TN; ++ct) {
-        const int64_t col = n0 + ct * 32 + (l & 31);
+        for (int ct = 0; ct < TN; ++ct)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = m0 + rt * 32 + tile_row(r, l);
-          float v = acc[rt][ct][r] * pre;
-          if (canon) v = __builtin_rintf(v * 1024.0f) * (1.0f / 1024.0f);
-          v = v * alpha;
-          if (row < M && col < N) __builtin_nontemporal_store(v, &c[row * N + col]);
+          for (int r = 0; r < 16; ++r) {
+            const int64_t k = rt * 32 + (r >> 2) * 8 + (r & 3);   // tile_row(r, l) - 4 (l >> 5)
+            __builtin_nontemporal_store(value(rt, ct, r), base + k * N + ct * 32);
+          }
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < TM; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < TN; ++ct) {
+          const int64_t col = n0 + ct * 32 + (l & 31);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t row = m0 + rt * 32 + tile_row(r, l);
+            const float v = value(rt, ct, r);
+            if (row < M && col < N) __builtin_nontemporal_store(v, &c[row * N + col]);
+          }
         }
-      }
+    }
   } else {
     const float a0 = ga ? *ga : 1.0f, b0 = gb ? *gb : 1.0f;
 #pragma unroll
