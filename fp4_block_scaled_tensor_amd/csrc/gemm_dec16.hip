@@ -145,9 +145,15 @@ __device__ __forceinline__ DecScale dec_entry(const uint2* table, uint32_t word,
   return d;
 }
 
+#ifndef FP4_DEC_UNROLL
+#define FP4_DEC_UNROLL 1   // the group loop unrolled (interior stages always hold four groups)
+#endif
+
 using DecTiling = Tiling<2, 2, 2, 2>;   // 128x128 workgroup tile, 4 waves of 64x64
 
-template <int FMT, int B>
+// INTERIOR: every tile lies inside the matrix and K is a multiple of 256 (no clamped loads;
+// every stage holds four groups).
+template <int FMT, int B, bool INTERIOR>
 __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
                                                        int la, const uint8_t* __restrict__ qb,
                                                        const uint8_t* __restrict__ sb, int lb,
@@ -205,8 +211,13 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
   LA.init(qa, M, K, m0);
   LB.init(qb, N, K, n0);
   if (nstages > 0) {
-    LA.issue(0, lA[0]);
-    LB.issue(0, lB[0]);
+    if (INTERIOR) {
+      LA.issue_interior(0, lA[0]);
+      LB.issue_interior(0, lB[0]);
+    } else {
+      LA.issue(0, lA[0]);
+      LB.issue(0, lB[0]);
+    }
   }
   store_stage_scales(0, sreg);
   wait_vm();
@@ -215,8 +226,13 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
   for (int64_t st = 0; st < nstages; ++st) {
     const int buf = (int)(st & 1);
     if (st + 1 < nstages) {
-      LA.issue(st + 1, lA[buf ^ 1]);
-      LB.issue(st + 1, lB[buf ^ 1]);
+      if (INTERIOR) {
+        LA.issue_interior(st + 1, lA[buf ^ 1]);
+        LB.issue_interior(st + 1, lB[buf ^ 1]);
+      } else {
+        LA.issue(st + 1, lA[buf ^ 1]);
+        LB.issue(st + 1, lB[buf ^ 1]);
+      }
       sreg = load_stage_scales(st + 1);
     }
     // the stage's scale codes of this lane's rows: word g holds the codes of group g's four slices
@@ -228,13 +244,16 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
       scA[t] = reinterpret_cast<const uint32_t*>(la == 2 ? &lT[buf][0][ra >> 4] : &lS[buf][ra]);
       scB[t] = reinterpret_cast<const uint32_t*>(lb == 2 ? &lT[buf][1][rb >> 4] : &lS[buf][GT + rb]);
     }
-    const int g_end = (int)((ngroups - st * SGR) < SGR ? (ngroups - st * SGR) : SGR);
+    const int g_end = INTERIOR ? SGR : (int)((ngroups - st * SGR) < SGR ? (ngroups - st * SGR) : SGR);
     uint32_t nwa[2], nwb[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       nwa[t] = scA[t][0];
       nwb[t] = scB[t][0];
     }
+#if FP4_DEC_UNROLL
+#pragma unroll
+#endif
     for (int g = 0; g < g_end; ++g) {
       uint32_t wa[2], wb[2];
 #pragma unroll
@@ -307,8 +326,10 @@ static hipError_t launch_dec16(const GemmArgs& g) {
   // per operand: scale array 16-byte aligned and K % 256 == 0 (whole-stage vector loads)
   const int align = (((reinterpret_cast<uintptr_t>(g.a.s) & 15) == 0 && g.K % 256 == 0) ? 1 : 0) |
                     (((reinterpret_cast<uintptr_t>(g.b.s) & 15) == 0 && g.K % 256 == 0) ? 2 : 0);
-  hipLaunchKernelGGL((k_gemm_dec16<FMT, B>), dim3((unsigned)tiles), dim3(TL::NT), 0, g.stream, g.a.q, g.a.s, g.a.layout,
-                     g.b.q, g.b.s, g.b.layout, g.a.g, g.b.g, g.c, g.M, g.N, g.K, g.canon,
+  const bool interior = g.M % TL::BM == 0 && g.N % TL::BN == 0 && g.K > 0 && g.K % KS == 0;
+  auto kern = interior ? k_gemm_dec16<FMT, B, true> : k_gemm_dec16<FMT, B, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(TL::NT), 0, g.stream, g.a.q, g.a.s, g.a.layout, g.b.q, g.b.s,
+                     g.b.layout, g.a.g, g.b.g, g.c, g.M, g.N, g.K, g.canon,
                      epilogue_word(g.hadamard_n, g.a.g_shift, g.b.g_shift), align);
   return hipGetLastError();
 }
