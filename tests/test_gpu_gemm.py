@@ -33,6 +33,9 @@ STRESS = [
     (OF.E8M0, 32, 2, 200, 136, 320, False),
     (OF.E8M0, 32, 6, 128, 128, 512, False),
     (OF.E8M0, 32, 24, 160, 96, 1024, True),
+    # whole 128 x 128 tiles with a partial last K stage (the clamped, not the interior, form)
+    (OF.UE5M3, 16, 2, 128, 256, 320, False),
+    (OF.E8M0, 32, 3, 256, 128, 576, False),
 ]
 
 
