@@ -18,12 +18,12 @@
 // Scales: per stage (4 groups) the thread that owns an operand row loads the row's 8 E8M0
 // bytes and stages them as two words, one per K-half (byte g = group g, the byte the MFMA
 // picks with op_sel g); each staging wave also stores the largest in-group exponent gap
-// |e0 - e1| of its 64 rows. While the A rows' and B rows' largest gaps sum to at most 10,
-// every group of the stage passes and the tile runs branch-free stages whose additions are
-// plain float adds (the K loop runs in round-toward-zero mode and contains no other
-// rounding-sensitive operation). A stage that fails runs as a simple loop that tests each
-// group, and the next stage goes back to the stage test (outlier channels fail only the
-// stages that hold them).
+// |e0 - e1| of each 32 of its rows. While the largest gaps of a wave's own A rows and B rows
+// sum to at most 10, every group of the stage passes for that wave, which runs a
+// branch-free stage whose additions are plain float adds (the K loop runs in
+// round-toward-zero mode and contains no other rounding-sensitive operation). A stage that
+// fails runs as a simple loop that tests each group, and the next stage goes back to the
+// stage test (outlier channels fail only the stages that hold them).
 //
 // The per-group float32 add bounds this kernel: 16 v_add_f32 per lane per 32x32x64 MFMA,
 // which the vector ALU issues in about the time the matrix core takes for the MFMA, and
