@@ -163,6 +163,7 @@ def test_rowcol_rejects_bad_arguments(lib):
     assert rowcol(lib, r, c, q=4100) == _lib.FP4_EALIGN
     assert rowcol(lib, r, c, ld=68) == _lib.FP4_EALIGN
     assert rowcol(lib, r, c, a_c=0) == _lib.FP4_EINVAL                      # UE5M3 needs both amax values
+    assert rowcol(lib, r, c, rows=(1 << 24) + 32) == _lib.FP4_EUNSUPPORTED  # 32-bit in-tile offsets
     mr, mc = cfg(fmt=2, block=32, view=0, T=0.0), cfg(fmt=2, block=32, view=1, T=0.0)
     assert rowcol(lib, mr, mc, rows=48) == _lib.FP4_EINVAL                  # 48 % 32
     assert lib.fp4_last_error().decode()
