@@ -33,18 +33,28 @@
 
 namespace fp4k {
 
-// Tile shapes (measured at 8192 x 4096: wider rows read and write longer contiguous
-// segments; decode, with its 4-byte payload reads, gains most from 256-column tiles).
-constexpr int FT = 64;    // fake quant: rows per tile
-constexpr int FF = 128;   // fake quant: columns per tile
+// Tile shapes (measured at 8192 x 4096 with inputs streamed from HBM: wider rows read and
+// write longer contiguous segments; fake quant 16 x 512 against 64 x 128: 24.2 vs 26.9 us,
+// decode 32 x 512 against 32 x 256: 19.9 vs 20.7 us).
+#ifndef FP4_FQ_TILE
+#define FP4_FQ_TILE 16, 512
+#endif
+#ifndef FP4_DQ_TILE
+#define FP4_DQ_TILE 32, 512
+#endif
+constexpr int FQ_TILE[2] = {FP4_FQ_TILE}, DQ_TILE[2] = {FP4_DQ_TILE};
+constexpr int FT = FQ_TILE[0];       // fake quant: rows per tile
+constexpr int FF = FQ_TILE[1];       // fake quant: columns per tile
 constexpr int FLR = FF / 8;          // lanes per tile row (8 elements each)
 constexpr int FPP = NT / FLR;        // rows per pass
 constexpr int FPASSES = FT / FPP;
-constexpr int DT = 32;    // decode: rows per tile
-constexpr int DF = 256;   // decode: columns per tile
+constexpr int DT = DQ_TILE[0];       // decode: rows per tile
+constexpr int DF = DQ_TILE[1];       // decode: columns per tile
 constexpr int DLR = DF / 8;
 constexpr int DPP = NT / DLR;
 constexpr int DPASSES = DT / DPP;
+static_assert(FLR <= NT && NT % FLR == 0 && FPASSES >= 1 && FPASSES * FPP == FT, "fake-quant tile");
+static_assert(DLR <= NT && NT % DLR == 0 && DPASSES >= 1 && DPASSES * DPP == DT && DT % 16 == 0, "decode tile");
 
 // nearest-even float32 -> bfloat16 bits (finite inputs; overflow rounds to infinity)
 __device__ __forceinline__ uint32_t bf16_rne(float v) {
