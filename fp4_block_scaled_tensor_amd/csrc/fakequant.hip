@@ -195,10 +195,14 @@ constexpr int XC = 128;   // FP8 scale chunk
 // segments with two chunks per tile row (128 x 256); the transposed form keeps one chunk
 // per row and 256 rows (its LDS byte tile's column writes conflict more as K grows, and
 // its output rows are XT bytes long).
+#ifndef FP4_XT_TR
+#define FP4_XT_TR 128, 256   // transposed form: K, rows per tile
+#endif
+constexpr int XT_TR[2] = {FP4_XT_TR};
 template <bool TRANSPOSE>
 struct XTile {
-  static constexpr int K = TRANSPOSE ? 128 : 256;   // K per tile (a multiple of XC)
-  static constexpr int T = TRANSPOSE ? 256 : 128;   // rows per tile
+  static constexpr int K = TRANSPOSE ? XT_TR[0] : 256;   // K per tile (a multiple of XC)
+  static constexpr int T = TRANSPOSE ? XT_TR[1] : 128;   // rows per tile
   static constexpr int L = K / 32;                  // lanes per tile row (one 32-element block each)
   static constexpr int PP = NT / L;                 // rows per pass
   static constexpr int P = T / PP;                  // rows per thread
