@@ -36,6 +36,8 @@ ROW_CASES = [
     ("sweep_mx", 2048, 2048, "bf16", OF.E8M0, 32, False, 0),
     ("sr_ue5m3", 512, 1024, "bf16", OF.UE5M3, 16, True, 2048),
     ("sr_mx", 64, 4096, "fp32", OF.E8M0, 32, True, 0),
+    ("ragged_tiles_sr_fp32", 9, 1056, "fp32", OF.E4M3, 16, True, 448),
+    ("ragged_tiles_ue5m3_b32", 17, 2080, "bf16", OF.UE5M3, 32, False, 2048),
 ]
 
 
@@ -52,6 +54,27 @@ def test_row_view(name, rows, cols, dtype, fmt, block, sr, T):
     assert_bytes_equal(got.s, ref.scales, f"{name} scales")
     assert got.g.item() == np.float32(ref.g)
     assert obs.item() == A
+
+
+@pytest.mark.parametrize("dtype,ld", [("bf16", 1096), ("bf16", (1 << 23) + 64), ("fp32", (1 << 22) + 32)],
+                         ids=["bf16_ld1096", "bf16_ld_over_2^23", "fp32_ld_over_2^22"])
+def test_row_view_strided_input(dtype, ld):
+    """x as a view with row stride ld > cols: a short stride, and strides whose row offsets
+    no longer fit the 32-bit in-tile addressing (the per-block-thread form runs then)."""
+    rows, cols = 5, 1024
+    t = _tensor(rows, cols, dtype, 1500 + ld % 97, "t")
+    A = oracle.tensor_amax(t.values)
+    ref = oracle.quantize_1d(t.values, OF.UE5M3, 16, amax=A, T=448, rounding="sr", seed=9, offset=2)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    base = torch.zeros(rows, ld, dtype=tdt, device="cuda")
+    base[:, :cols] = dev_input(t)
+    x = base[:, :cols]
+    assert x.stride(0) == ld
+    got = fp4.quantize(x, OF.UE5M3, 16, fp4.ROW, amax=dev_scalar(A), T=448, stochastic=True, seed=9, offset=2)
+    torch.cuda.synchronize()
+    assert_bytes_equal(got.q, ref.packed, "payload")
+    assert_bytes_equal(got.s, ref.scales, "scales")
+    assert got.g.item() == np.float32(ref.g)
 
 
 def test_row_view_full_size_activation_sampled_rows():
