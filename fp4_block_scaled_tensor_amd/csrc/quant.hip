@@ -28,6 +28,7 @@
 //                 order like unsigned integers), skipped when the result already holds more.
 // The quantize kernels also write the operand's g (workgroup 0, thread 0) and, if asked,
 // fold their block maxima into the observed amax (one atomic per workgroup).
+#include <algorithm>
 #include <type_traits>
 
 #include "quant_common.hpp"
@@ -117,19 +118,20 @@ __global__ __launch_bounds__(NT) void k_quant_row(const void* __restrict__ x, in
 #endif
 // Stripe-maximum pieces of the two-pass tile-local quantizer: at most this many columns
 // and at least 2^FP4_SAMAX_MIN_ROWS_LOG2 rows per workgroup, about FP4_SAMAX_WPC workgroups
-// per CU, FP4_SAMAX_UL 16-byte loads in flight per thread. The tensor maximum's grid has at
-// most FP4_AMAX_GY workgroup rows. Both end in one atomic max per workgroup, and atomics on
-// one address serialize across the chip: at 8192 x 4096 bf16 the tensor maximum takes 25.6 us
-// with 2048 workgroup rows against 21.1 with 512, and the 128-row stripe quantizer 49 us with
-// 4 stripe-maximum workgroups per CU against 38 with one (and 8 loads in flight per thread).
+// per CU, FP4_SAMAX_UL 16-byte loads in flight per thread. The tensor maximum's grid has about
+// FP4_AMAX_WPC workgroups per CU. Both end in one atomic max per workgroup, and atomics on one
+// address serialize across the chip: at 8192 x 4096 bf16 the tensor maximum takes 25.6 us with
+// 2048 workgroups, 21.3 with 512, 17.8 with 768 (three per CU), and the 128-row stripe
+// quantizer 49 us with 4 stripe-maximum workgroups per CU against 38 with one (and 8 loads in
+// flight per thread).
 #ifndef FP4_SAMAX_COLS
 #define FP4_SAMAX_COLS 4096
 #endif
 #ifndef FP4_SAMAX_MIN_ROWS_LOG2
 #define FP4_SAMAX_MIN_ROWS_LOG2 0
 #endif
-#ifndef FP4_AMAX_GY
-#define FP4_AMAX_GY 512
+#ifndef FP4_AMAX_WPC
+#define FP4_AMAX_WPC 3
 #endif
 #ifndef FP4_SAMAX_UL
 #define FP4_SAMAX_UL 8
@@ -827,12 +829,13 @@ __global__ __launch_bounds__(NT) void k_amax_plain(const void* __restrict__ x, i
 
 template <bool F32, int P>
 static void launch_amax(const void* x, int64_t rows, int64_t cols, int64_t ld, float* out, hipStream_t stream) {
-  // a bounded grid (at most 16 x FP4_AMAX_GY workgroups): at most one atomic per workgroup
+  // a bounded grid (about FP4_AMAX_WPC workgroups per CU): one atomic per workgroup
   const int64_t chunks = cols / 8;
   const int64_t cx = (chunks + (int64_t)NT * P - 1) / ((int64_t)NT * P);
   const unsigned gx = (unsigned)(cx > 16 ? 16 : cx);
   const int64_t ry = (rows + 8 / P - 1) / (8 / P);
-  const unsigned gy = (unsigned)(ry < FP4_AMAX_GY ? ry : FP4_AMAX_GY);
+  const int64_t cap = std::max<int64_t>(1, (int64_t)FP4_AMAX_WPC * device_cu_count() / gx);
+  const unsigned gy = (unsigned)(ry < cap ? ry : cap);
   hipLaunchKernelGGL((k_amax_plain<F32, P>), dim3(gx, gy), dim3(NT), 0, stream, x, rows, cols, ld, out);
 }
 
