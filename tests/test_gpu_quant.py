@@ -226,3 +226,19 @@ def test_stochastic_rounding_unbiased_over_a_million_draws(r):
     f = (np.float64(np.float32(r)) - lo) / (hi - lo)
     sigma = (hi - lo) * np.sqrt(f * (1 - f) / vals.size)
     assert abs(vals.mean() - np.float64(np.float32(r))) <= 3 * sigma + (hi - lo) * 2.0 ** -16
+
+
+@pytest.mark.parametrize("rows,cols,dtype", [(7001, 12296, "bf16"), (4099, 2056, "fp32"), (9000, 4096, "bf16")])
+def test_tensor_amax_grid_stride(rows, cols, dtype):
+    """Shapes where the tensor maximum's workgroups each loop over several row groups and
+    column pieces (ragged in both); the single largest magnitude is planted in the last rows
+    and last columns, then moved to the first element."""
+    t = _tensor(rows, cols, dtype, 4000 + rows, "normal")
+    v = t.values.copy()
+    for r, c in ((rows - 1, cols - 3), (0, 0)):
+        w = v.copy()
+        w[r, c] = -1000.0
+        tt = synth.Tensor("x", w, dtype)
+        got = fp4.tensor_amax(dev_input(tt))
+        torch.cuda.synchronize()
+        assert got.item() == oracle.tensor_amax(w) == np.float32(1000.0), (r, c)
