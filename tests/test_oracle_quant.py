@@ -144,3 +144,52 @@ def test_amax_cache_sample_and_hold():
     assert float(c.update(123, 7.0)) == 7.0 and float(c.update(124, 9.0)) == 7.0
     d1 = oracle.AmaxCache(1)
     assert [float(d1.update(s, s * 2.0)) for s in range(3)] == [0.0, 2.0, 4.0]
+
+
+def _max_element_block(view_vals, codes, scale_vals, block, two_d=False):
+    """(scale value, E2M1 code) of the block holding the largest |value| of an operand view."""
+    i, k = np.unravel_index(np.argmax(np.abs(view_vals)), view_vals.shape)
+    s = scale_vals[i // 16, k // 16] if two_d else scale_vals[i, k // block]
+    return float(s), int(codes[i, k]), float(view_vals[i, k])
+
+
+@pytest.mark.parametrize("fmt,T", [(F.UE5M3, 448.0), (F.UE5M3, 2048.0), (F.E4M3, 448.0)])
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_true_amax_maps_to_scale_T_and_payload_6(fmt, T, sign):
+    """Tensor-scale pin, independent of the formula's own restatement. With the cached amax
+    equal to the true max|x|, the block holding that element gets block-scale value exactly
+    T (the headroom figures 61440/448 and 61440/2048 of the key-contributions section say the
+    cached amax sits at scale value T), and the element itself gets E2M1 code +-6 (0x7 /
+    0xF), the codebook's largest magnitude, so the payload range is fully used. Its decoded
+    value 6 * T * g then reproduces the amax within float32 rounding, which pins g. A
+    tensor scale built as T/A instead of 6T/A would give code +-1 here, and a g of 1/s_blk
+    a decoded value 6 times too large."""
+    rng = np.random.default_rng(31)
+    x = (rng.standard_t(3, (128, 256)) * 0.37).astype(np.float32)
+    i, k = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    x[i, k] = np.float32(sign) * np.abs(x[i, k])
+    want_code = 0x7 | (0x8 if sign < 0 else 0)
+    for view in ("row", "col", "col16", "2d"):
+        if view == "row":
+            A = oracle.tensor_amax(x)
+            q = oracle.quantize_1d(x, fmt, 16, amax=A, T=T)
+            vals, two_d = x, False
+        elif view.startswith("col"):
+            hn = 16 if view == "col16" else 0
+            A = oracle.tensor_amax(x, hn)
+            q = oracle.quantize_col(x, fmt, 16, amax=A, T=T, hadamard_n=hn)
+            vals, two_d = oracle.transposed_view(x, hn), False
+        else:
+            A = oracle.tensor_amax(x)
+            q = oracle.quantize_2d(x, fmt, amax=A, T=T)
+            vals, two_d = x, True
+        if view == "col16":      # the rotated maximum's sign is whatever the FWHT made it
+            v_sign = np.sign(vals.ravel()[np.argmax(np.abs(vals))])
+            want = 0x7 | (0x8 if v_sign < 0 else 0)
+        else:
+            want = want_code
+        S, code, v = _max_element_block(vals, q.codes, q.scale_values(), 16, two_d)
+        assert S == T, (view, S)
+        assert code == want, (view, hex(code))
+        decoded = 6.0 * T * float(q.g)
+        assert abs(decoded - abs(v)) <= 4 * 2.0 ** -24 * abs(v), (view, decoded, v)
