@@ -68,13 +68,16 @@ def _cfg(fmt, block, view, stochastic, hadamard_n, T, seed, offset) -> _lib.Quan
 
 def quantize(x: torch.Tensor, fmt: int = UE5M3, block: int = 16, view: int = ROW, amax: torch.Tensor | None = None,
              T: float = 448.0, stochastic: bool = False, seed: int = 0, offset: int = 0, hadamard_n: int = 0,
-             amax_obs: torch.Tensor | None = None):
+             amax_obs: torch.Tensor | None = None, stats: torch.Tensor | None = None):
     """fp4_quantize. x: bf16 or fp32 [rows, cols] on the GPU (row stride x.stride(0)).
+    stats: optional int32 device tensor of 3 receiving the call's health counts (saturated,
+    zero-scale, non-finite blocks).
 
     Returns a QTensor; for TILE2D a pair (forward operand [rows x cols], dgrad operand
     [cols x rows]) sharing the 2D scale grid and g."""
     lib = _lib.load()
-    _dev_check(x, amax, amax_obs)
+    _dev_check(x, amax, amax_obs, stats)
+    _stats_check(stats)
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     if x.dtype == torch.bfloat16:
@@ -101,13 +104,24 @@ def quantize(x: torch.Tensor, fmt: int = UE5M3, block: int = 16, view: int = ROW
     qt = torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev) if view == TILE2D else None
     g = torch.empty(1, dtype=torch.float32, device=dev)
     _lib.check(lib.fp4_quantize(_ptr(x), dt, rows, cols, x.stride(0), ctypes.byref(cfg), _ptr(amax), _ptr(q), _ptr(s),
-                                _ptr(qt), _ptr(g), _ptr(amax_obs), _stream()))
+                                _ptr(qt), _ptr(g), _ptr(amax_obs), _ptr(stats), _stream()))
     if view == ROW:
         return QTensor(q, s, g, fmt, block, FP4_SCALES_1D, rows, cols)
     if view == COL:
         return QTensor(q, s, g, fmt, block, FP4_SCALES_1D, cols, rows)
     return (QTensor(q, s, g, fmt, 16, FP4_SCALES_2D, rows, cols),
             QTensor(qt, s, g, fmt, 16, FP4_SCALES_2D_T, cols, rows))
+
+
+def _stats_check(stats):
+    if stats is not None and (stats.dtype != torch.int32 or stats.numel() < 3 or not stats.is_contiguous()):
+        raise ValueError("stats must be a contiguous int32 device tensor of at least 3 elements")
+
+
+def new_stats(device="cuda") -> torch.Tensor:
+    """A device buffer for the health counts of one quantize call (int32 x 3: saturated,
+    zero-scale and non-finite blocks)."""
+    return torch.zeros(3, dtype=torch.int32, device=device)
 
 
 def _in_dtype(x: torch.Tensor) -> int:
@@ -122,11 +136,15 @@ def quantize_rowcol(x: torch.Tensor, fmt: int = UE5M3, block: int = 16, amax_row
                     amax_col: torch.Tensor | None = None, T_row: float = 448.0, T_col: float = 448.0,
                     stochastic_row: bool = False, stochastic_col: bool = False, seed_row: int = 0,
                     offset_row: int = 0, seed_col: int = 0, offset_col: int = 0, hadamard_n: int = 0,
-                    amax_obs_row: torch.Tensor | None = None, amax_obs_col: torch.Tensor | None = None):
+                    amax_obs_row: torch.Tensor | None = None, amax_obs_col: torch.Tensor | None = None,
+                    stats_row: torch.Tensor | None = None, stats_col: torch.Tensor | None = None):
     """fp4_quantize_rowcol: (ROW operand [rows x cols], COL operand x^T [cols x rows]) from one pass
-    over x; each equals the matching fp4_quantize call. hadamard_n rotates the COL view only."""
+    over x; each equals the matching fp4_quantize call. hadamard_n rotates the COL view only;
+    stats_row / stats_col receive each view's health counts as in quantize()."""
     lib = _lib.load()
-    _dev_check(x, amax_row, amax_col, amax_obs_row, amax_obs_col)
+    _dev_check(x, amax_row, amax_col, amax_obs_row, amax_obs_col, stats_row, stats_col)
+    _stats_check(stats_row)
+    _stats_check(stats_col)
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     dt = _in_dtype(x)
@@ -146,7 +164,8 @@ def quantize_rowcol(x: torch.Tensor, fmt: int = UE5M3, block: int = 16, amax_row
     gt = torch.empty(1, dtype=torch.float32, device=dev)
     _lib.check(lib.fp4_quantize_rowcol(_ptr(x), dt, rows, cols, x.stride(0), ctypes.byref(cr), ctypes.byref(cc),
                                        _ptr(amax_row), _ptr(amax_col), _ptr(q), _ptr(s), _ptr(g), _ptr(amax_obs_row),
-                                       _ptr(qt), _ptr(st), _ptr(gt), _ptr(amax_obs_col), _stream()))
+                                       _ptr(qt), _ptr(st), _ptr(gt), _ptr(amax_obs_col), _ptr(stats_row),
+                                       _ptr(stats_col), _stream()))
     return (QTensor(q, s, g, fmt, block, FP4_SCALES_1D, rows, cols),
             QTensor(qt, st, gt, fmt, block, FP4_SCALES_1D, cols, rows))
 

@@ -13,7 +13,7 @@ FP4_UE5M3, FP4_E4M3, FP4_E8M0 = 0, 1, 2
 FP4_VIEW_ROW, FP4_VIEW_COL, FP4_VIEW_TILE2D = 0, 1, 2
 FP4_IN_BF16, FP4_IN_FP32 = 0, 1
 FP4_SCALES_1D, FP4_SCALES_2D, FP4_SCALES_2D_T = 0, 1, 2
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 EXPORTED = [
     "fp4_quantize", "fp4_quantize_rowcol", "fp4_fake_quant", "fp4_dequantize", "fp4_mxfp4_to_fp8", "fp4_quantize_local", "fp4_quantize_sizes", "fp4_tensor_amax", "amax_cache_update", "amax_cache_reset",
@@ -40,9 +40,10 @@ class AmaxCacheC(ctypes.Structure):
 _P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 
 SIGNATURES = {
-    "fp4_quantize": ([_P, _I32, _I64, _I64, _I64, ctypes.POINTER(QuantCfg), _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "fp4_quantize": ([_P, _I32, _I64, _I64, _I64, ctypes.POINTER(QuantCfg), _P, _P, _P, _P, _P, _P, _P, _P],
+                     ctypes.c_int),
     "fp4_quantize_rowcol": ([_P, _I32, _I64, _I64, _I64, ctypes.POINTER(QuantCfg), ctypes.POINTER(QuantCfg), _P, _P,
-                             _P, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+                             _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "fp4_fake_quant": ([_P, _I32, _I64, _I64, _I64, ctypes.POINTER(QuantCfg), _P, _P, _I32, _I64, _P], ctypes.c_int),
     "fp4_dequantize": ([ctypes.POINTER(Operand), _P, _I32, _I64, _P], ctypes.c_int),
     "fp4_mxfp4_to_fp8": ([ctypes.POINTER(Operand), _I32, _P, _P, _P], ctypes.c_int),

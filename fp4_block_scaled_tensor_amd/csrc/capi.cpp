@@ -177,7 +177,7 @@ fp4_status fp4_quantize_sizes(int64_t rows, int64_t cols, const fp4_quant_cfg* c
 
 fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld,
                         const fp4_quant_cfg* cfg, const float* d_amax, uint8_t* q, uint8_t* s, uint8_t* q_t,
-                        float* d_g, float* d_amax_obs, void* stream) {
+                        float* d_g, float* d_amax_obs, uint32_t* d_stats, void* stream) {
   fp4_status st;
   if ((st = check_cfg(cfg)) != FP4_OK) return st;
   if ((st = check_shape(rows, cols, cfg)) != FP4_OK) return st;
@@ -196,6 +196,7 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t co
   if (cfg->fmt != FP4_E8M0 && !d_amax) return fail(FP4_EINVAL, "UE5M3/E4M3 need the cached amax d_amax");
   if ((d_amax && !aligned(d_amax, 4)) || (d_g && !aligned(d_g, 4)) || (d_amax_obs && !aligned(d_amax_obs, 4)))
     return fail(FP4_EALIGN, "amax / g pointers must be 4-byte aligned");
+  if (d_stats && !aligned(d_stats, 4)) return fail(FP4_EALIGN, "d_stats must be 4-byte aligned");
   fp4k::QuantArgs a;
   a.x = x;
   a.f32 = x_dtype == FP4_IN_FP32;
@@ -216,6 +217,7 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t co
   a.qt = q_t;
   a.d_g = d_g;
   a.d_amax_obs = d_amax_obs;
+  a.stats = d_stats;
   a.stream = (hipStream_t)stream;
   return hip_status(fp4k::run_quantize(a), "fp4_quantize");
 }
@@ -223,7 +225,8 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t co
 fp4_status fp4_quantize_rowcol(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld,
                                const fp4_quant_cfg* cfg_row, const fp4_quant_cfg* cfg_col, const float* d_amax_row,
                                const float* d_amax_col, uint8_t* q, uint8_t* s, float* d_g, float* d_amax_obs_row,
-                               uint8_t* q_t, uint8_t* s_t, float* d_g_t, float* d_amax_obs_col, void* stream) {
+                               uint8_t* q_t, uint8_t* s_t, float* d_g_t, float* d_amax_obs_col,
+                               uint32_t* d_stats_row, uint32_t* d_stats_col, void* stream) {
   fp4_status st;
   if ((st = check_cfg(cfg_row)) != FP4_OK) return st;
   if ((st = check_cfg(cfg_col)) != FP4_OK) return st;
@@ -250,6 +253,8 @@ fp4_status fp4_quantize_rowcol(const void* x, int32_t x_dtype, int64_t rows, int
   for (const float* p : {(const float*)d_amax_row, (const float*)d_amax_col, (const float*)d_g, (const float*)d_g_t,
                          (const float*)d_amax_obs_row, (const float*)d_amax_obs_col})
     if (p && !aligned(p, 4)) return fail(FP4_EALIGN, "amax / g pointers must be 4-byte aligned");
+  if ((d_stats_row && !aligned(d_stats_row, 4)) || (d_stats_col && !aligned(d_stats_col, 4)))
+    return fail(FP4_EALIGN, "stats pointers must be 4-byte aligned");
   fp4k::RowColArgs a;
   a.x = x;
   a.f32 = x_dtype == FP4_IN_FP32;
@@ -277,6 +282,8 @@ fp4_status fp4_quantize_rowcol(const void* x, int32_t x_dtype, int64_t rows, int
   a.g_c = d_g_t;
   a.obs_r = d_amax_obs_row;
   a.obs_c = d_amax_obs_col;
+  a.stats_r = d_stats_row;
+  a.stats_c = d_stats_col;
   a.stream = (hipStream_t)stream;
   return hip_status(fp4k::run_quantize_rowcol(a), "fp4_quantize_rowcol");
 }

@@ -12,12 +12,12 @@
 // rounded from that float32, nearest-even.
 //
 // Kernels:
-//   k_fake_quant  x -> x_hat in one pass (ROW view, nearest-even): a 64-row x 128-column tile
-//                 per workgroup, 16 lanes per 128-element row segment (256 bytes of bf16),
-//                 a block of B elements spans B/8 lanes whose maxima combine by DPP, codes are
-//                 made and decoded in registers.
+//   k_fake_quant  x -> x_hat in one pass (ROW view, nearest-even): a 16-row x 512-column tile
+//                 per workgroup, 64 lanes per 512-element row segment (1 KB of bf16), a block
+//                 of B elements spans B/8 lanes whose maxima combine by DPP, codes are made and
+//                 decoded in registers.
 //   k_dequant     a quantized operand (1D, 2D or transposed-2D scales) -> x_hat, the same
-//                 lane layout on 32-row x 256-column tiles (128 payload bytes per row).
+//                 lane layout on 32-row x 512-column tiles (256 payload bytes per row).
 //   k_mx_to_fp8   MXFP4 operand -> FP8 E4M3 with one E8M0 scale per 128-element chunk
 //                 ("Practical FP4 Training for Large-Scale MoE Models on Hopper GPUs",
 //                 methodology: direct FP4 -> FP8 conversion, hierarchical scale alignment
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(NT) void k_fake_quant(const void* __restrict__ x, i
     c[p].to_float(v);
     float am = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(v[j]));
+    for (int j = 0; j < 8; ++j) am = mag_max(am, fabsf(v[j]));
     am = group_max<LB>(am);
     uint32_t code;
     float mult;

@@ -32,8 +32,12 @@ struct QuantArgs {
   uint8_t* qt;
   float* d_g;
   float* d_amax_obs;
+  uint32_t* stats;    // optional health counts (FP4_STATS_WORDS words), overwritten
   hipStream_t stream;
 };
+
+// words of a health-count output: saturated, zero-scale, non-finite blocks
+constexpr int FP4_STATS_WORDS = 3;
 
 struct GemmOperand {
   const uint8_t* q;
@@ -78,6 +82,7 @@ struct RowColArgs {
   uint8_t *q, *s, *qt, *st;
   float *g_r, *g_c;
   float *obs_r, *obs_c;   // observed amax outputs (max-accumulated; cleared by the caller side)
+  uint32_t *stats_r, *stats_c;   // optional health counts of each view, overwritten
   hipStream_t stream;
 };
 hipError_t run_quantize_rowcol(const RowColArgs& a);

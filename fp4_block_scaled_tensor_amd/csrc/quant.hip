@@ -48,13 +48,13 @@ __device__ __forceinline__ void load_block(const void* x, int64_t elem, float (&
 template <int FMT, int B, bool SR>
 __device__ __forceinline__ float quant_block_row(const float (&v)[B], const TensorScales& ts, int64_t r, int64_t b,
                                                  int64_t cols, uint64_t seed, uint64_t offset, uint8_t* __restrict__ q,
-                                                 uint8_t* __restrict__ s) {
+                                                 uint8_t* __restrict__ s, Health& h) {
   float amax_b = 0.0f;
 #pragma unroll
-  for (int j = 0; j < B; ++j) amax_b = fmaxf(amax_b, fabsf(v[j]));
+  for (int j = 0; j < B; ++j) amax_b = mag_max(amax_b, fabsf(v[j]));
   uint32_t code;
   float mult;
-  block_scale<FMT>(amax_b, ts, code, mult);
+  block_scale<FMT>(amax_b, ts, code, mult, h);
   uint32_t words[B / 8];
   payload<B, SR>(v, mult, (uint64_t)(r * cols + b * B), seed, offset, words);
   uint8_t* qp = q + r * (cols / 2) + b * (B / 2);
@@ -72,7 +72,8 @@ __global__ __launch_bounds__(NT) void k_quant_row(const void* __restrict__ x, in
                                                   int tpr_log2, const float* __restrict__ d_amax, float T,
                                                   uint64_t seed, uint64_t offset, uint8_t* __restrict__ q,
                                                   uint8_t* __restrict__ s, float* __restrict__ d_amax_obs,
-                                                  float* __restrict__ d_g, int stripe_log2 = 0) {
+                                                  float* __restrict__ d_g, int stripe_log2 = 0,
+                                                  uint32_t* __restrict__ stats = nullptr) {
   const int tpr = 1 << tpr_log2;
   const int half_rows = NT >> tpr_log2;                // rows per pass
   const int64_t nbr = cols / B;
@@ -83,6 +84,7 @@ __global__ __launch_bounds__(NT) void k_quant_row(const void* __restrict__ x, in
     write_g<FMT>(d_g, ts);
   }
   float obs = 0.0f;
+  Health h;
   if (b < nbr) {
     // row groups of 2 * half_rows rows, strided over the grid (one group per workgroup
     // unless the matrix has more than 65535 groups)
@@ -98,11 +100,12 @@ __global__ __launch_bounds__(NT) void k_quant_row(const void* __restrict__ x, in
       float v0[B], v1[B];
       if (has0) load_block<B, F32>(x, r0 * ld + b * B, v0);
       if (has1) load_block<B, F32>(x, r1 * ld + b * B, v1);
-      if (has0) obs = fmaxf(obs, quant_block_row<FMT, B, SR>(v0, ts0, r0, b, cols, seed, offset, q, s));
-      if (has1) obs = fmaxf(obs, quant_block_row<FMT, B, SR>(v1, ts1, r1, b, cols, seed, offset, q, s));
+      if (has0) obs = mag_max(obs, quant_block_row<FMT, B, SR>(v0, ts0, r0, b, cols, seed, offset, q, s, h));
+      if (has1) obs = mag_max(obs, quant_block_row<FMT, B, SR>(v1, ts1, r1, b, cols, seed, offset, q, s, h));
     }
   }
   if (!LOCAL && d_amax_obs) wg_max_to(d_amax_obs, obs);
+  if (!LOCAL) health_flush(stats, h);
 }
 
 // ROW view on QT x QF tiles (8 x 1024; with HBM-streamed inputs at 8192 x 4096: UE5M3 18.1 us
@@ -155,7 +158,7 @@ __global__ __launch_bounds__(NT) void k_quant_row_t(const void* __restrict__ x, 
                                                     int64_t ld, const float* __restrict__ d_amax, float T,
                                                     uint64_t seed, uint64_t offset, uint8_t* __restrict__ q,
                                                     uint8_t* __restrict__ s, float* __restrict__ d_amax_obs,
-                                                    float* __restrict__ d_g) {
+                                                    float* __restrict__ d_g, uint32_t* __restrict__ stats) {
   constexpr int LB = B / 8;                     // lanes per block
   constexpr int ESZ = F32 ? 4 : 2;
   const int64_t nft = (cols + QF - 1) / QF;
@@ -178,6 +181,7 @@ __global__ __launch_bounds__(NT) void k_quant_row_t(const void* __restrict__ x, 
     c[p].load(rx, (cok && r < rl) ? (uint32_t)r * ld_b + (uint32_t)(lc * 8 * ESZ) : OOB);
   }
   float obs = 0.0f;
+  Health h;
 #pragma unroll
   for (int p = 0; p < QPASSES; ++p) {
     const int r = p * QPP + lr;
@@ -186,20 +190,23 @@ __global__ __launch_bounds__(NT) void k_quant_row_t(const void* __restrict__ x, 
     c[p].to_float(v);
     float am = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(v[j]));
+    for (int j = 0; j < 8; ++j) am = mag_max(am, fabsf(v[j]));
     am = group_max<LB>(am);
     uint32_t code;
     float mult;
-    block_scale<FMT>(am, ts, code, mult);
+    Health hb;
+    block_scale<FMT>(am, ts, code, mult, hb);
+    h.add_if(ok && (lc & (LB - 1)) == 0, hb);     // one count per block (its first lane)
     uint32_t w;
     payload<8, SR>(v, mult, SR ? (uint64_t)((t0 + r) * cols + f0 + lc * 8) : 0, seed, offset, &w);
     __builtin_amdgcn_raw_buffer_store_b32(w, rq, ok ? (uint32_t)r * qcols + (uint32_t)(lc * 4) : OOB, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code, rs,
                                          (ok && (lc & (LB - 1)) == 0) ? (uint32_t)r * scols + (uint32_t)(lc / LB) : OOB,
                                          0, 0);
-    if (ok) obs = fmaxf(obs, am);
+    if (ok) obs = mag_max(obs, am);
   }
   if (d_amax_obs) wg_max_to(d_amax_obs, obs);
+  health_flush(stats, h);
 }
 
 // ---------------------------------------------------------------- COL view (wgrad operands)
@@ -242,12 +249,13 @@ __device__ __forceinline__ void stage_tile(const void* __restrict__ x, int64_t r
 
 // COL-view quantization of one staged CT x CF tile (tokens x features): each thread owns a
 // U-token run of one feature, the payload goes through the LDS output tile and is stored
-// row-contiguously (feature rows of q). Returns the thread's largest block amax.
+// row-contiguously (feature rows of q). Returns the thread's largest block amax; adds the
+// blocks of features inside the matrix to h.
 template <int FMT, int B, bool SR, int HN>
 __device__ __forceinline__ float col_tile(float (*tile)[CF + 1], uint32_t (*qout)[CT / 8 + 1], uint8_t (*sout)[CT / B],
                                           int64_t rows, int64_t cols, int64_t t0, int64_t f0, const TensorScales& ts,
                                           uint64_t seed, uint64_t offset, uint8_t* __restrict__ q,
-                                          uint8_t* __restrict__ s) {
+                                          uint8_t* __restrict__ s, Health& h) {
   constexpr int U = (HN > B) ? HN : B;          // tokens per thread unit
   constexpr int UNITS = CT / U;                 // units per feature in a tile
   const int f = threadIdx.x & 63;
@@ -266,11 +274,13 @@ __device__ __forceinline__ float col_tile(float (*tile)[CF + 1], uint32_t (*qout
     for (int bb = 0; bb < U / B; ++bb) {
       float amax_b = 0.0f;
 #pragma unroll
-      for (int i = 0; i < B; ++i) amax_b = fmaxf(amax_b, fabsf(v[bb * B + i]));
-      obs = fmaxf(obs, amax_b);
+      for (int i = 0; i < B; ++i) amax_b = mag_max(amax_b, fabsf(v[bb * B + i]));
+      obs = mag_max(obs, amax_b);
       uint32_t code;
       float mult;
-      block_scale<FMT>(amax_b, ts, code, mult);
+      Health hb;
+      block_scale<FMT>(amax_b, ts, code, mult, hb);
+      h.add_if(f0 + f < cols, hb);              // features past the matrix are zero padding
       uint32_t words[B / 8];
       const int tok = u * U + bb * B;           // token offset inside the tile
       payload<B, SR>(v + bb * B, mult, (uint64_t)((f0 + f) * rows + t0 + tok), seed, offset, words);
@@ -301,7 +311,8 @@ template <int FMT, int B, bool SR, bool F32, int HN>
 __global__ __launch_bounds__(NT) void k_quant_col(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
                                                   const float* __restrict__ d_amax, float T, uint64_t seed,
                                                   uint64_t offset, uint8_t* __restrict__ q, uint8_t* __restrict__ s,
-                                                  float* __restrict__ d_amax_obs, float* __restrict__ d_g) {
+                                                  float* __restrict__ d_amax_obs, float* __restrict__ d_g,
+                                                  uint32_t* __restrict__ stats) {
   __shared__ float tile[CT][CF + 1];
   __shared__ uint32_t qout[CF][CT / 8 + 1];     // 8 codes per dword
   __shared__ uint8_t sout[CF][CT / B];
@@ -312,8 +323,10 @@ __global__ __launch_bounds__(NT) void k_quant_col(const void* __restrict__ x, in
   TensorScales ts{1.0f, 1.0f, 1.0f};
   if constexpr (FMT != FMT_E8M0) ts = tensor_scales(d_amax, T);
   write_g<FMT>(d_g, ts);
-  const float obs = col_tile<FMT, B, SR, HN>(tile, qout, sout, rows, cols, t0, f0, ts, seed, offset, q, s);
+  Health h;
+  const float obs = col_tile<FMT, B, SR, HN>(tile, qout, sout, rows, cols, t0, f0, ts, seed, offset, q, s, h);
   if (d_amax_obs) wg_max_to(d_amax_obs, obs);
+  health_flush(stats, h);
 }
 
 // ---------------------------------------------------------------- ROW + COL views in one pass
@@ -366,7 +379,8 @@ __global__ __launch_bounds__(NT) void k_quant_rowcol(const void* __restrict__ x,
                                                      uint8_t* __restrict__ s, float* __restrict__ g_r,
                                                      float* __restrict__ obs_r, uint8_t* __restrict__ qt,
                                                      uint8_t* __restrict__ st, float* __restrict__ g_c,
-                                                     float* __restrict__ obs_c) {
+                                                     float* __restrict__ obs_c, uint32_t* __restrict__ stats_r,
+                                                     uint32_t* __restrict__ stats_c) {
   constexpr int RT = RcTile<SRR || SRC>::T, RF = RcTile<SRR || SRC>::F;
   constexpr int U = (HN > B) ? HN : B;          // COL tokens per thread unit
   constexpr int UNITS = RT / U;
@@ -426,6 +440,7 @@ __global__ __launch_bounds__(NT) void k_quant_rowcol(const void* __restrict__ x,
     }
   };
   float orow = 0.0f, ocol = 0.0f;
+  Health hrow, hcol;
   Chunk8<F32> cur[PASSES];
   load_tile(id, cur);
   // wait for the first tile here: inside the loop the current tile always comes from the
@@ -454,18 +469,20 @@ __global__ __launch_bounds__(NT) void k_quant_rowcol(const void* __restrict__ x,
       cur[p].to_float(v);
       float am = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(v[j]));
+      for (int j = 0; j < 8; ++j) am = mag_max(am, fabsf(v[j]));
       am = group_max<LB>(am);
       uint32_t code;
       float mult;
-      block_scale<FMT>(am, tr, code, mult);
+      Health hb;
+      block_scale<FMT>(am, tr, code, mult, hb);
+      hrow.add_if(ok && (lc & (LB - 1)) == 0, hb);
       uint32_t w;
       payload<8, SRR>(v, mult, SRR ? (uint64_t)((t0 + r) * cols + f0 + lc * 8) : 0, seed_r, offset_r, &w);
       __builtin_amdgcn_raw_buffer_store_b32(w, rq, ok ? (uint32_t)r * qcols + (uint32_t)(lc * 4) : OOB, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code, rs,
                                            (ok && (lc & (LB - 1)) == 0) ? (uint32_t)r * scols + (uint32_t)(lc / LB) : OOB,
                                            0, 0);
-      if (ok) orow = fmaxf(orow, am);
+      if (ok) orow = mag_max(orow, am);
     }
 
     // stage the tile in the input's own type for the COL view
@@ -494,11 +511,13 @@ __global__ __launch_bounds__(NT) void k_quant_rowcol(const void* __restrict__ x,
       for (int bb = 0; bb < U / B; ++bb) {
         float amax_b = 0.0f;
 #pragma unroll
-        for (int i = 0; i < B; ++i) amax_b = fmaxf(amax_b, fabsf(c[bb * B + i]));
-        if (f < cl) ocol = fmaxf(ocol, amax_b);
+        for (int i = 0; i < B; ++i) amax_b = mag_max(amax_b, fabsf(c[bb * B + i]));
+        if (f < cl) ocol = mag_max(ocol, amax_b);
         uint32_t code;
         float mult;
-        block_scale<FMT>(amax_b, tc, code, mult);
+        Health hb;
+        block_scale<FMT>(amax_b, tc, code, mult, hb);
+        hcol.add_if(f < cl, hb);
         uint32_t words[B / 8];
         const int tok = u * U + bb * B;
         payload<B, SRC>(c + bb * B, mult, SRC ? (uint64_t)((f0 + f) * rows + t0 + tok) : 0, seed_c, offset_c, words);
@@ -531,6 +550,9 @@ __global__ __launch_bounds__(NT) void k_quant_rowcol(const void* __restrict__ x,
   if (obs_r) wg_max_to(obs_r, orow);
   if (obs_r && obs_c) __syncthreads();   // wg_max_to's partials array is reused
   if (obs_c) wg_max_to(obs_c, ocol);
+  health_flush(stats_r, hrow);
+  if (stats_r && stats_c) __syncthreads();   // health_flush's partials array is reused
+  health_flush(stats_c, hcol);
 }
 
 // ---------------------------------------------------------------- ROW view, tile-local scales
@@ -565,14 +587,14 @@ __global__ __launch_bounds__(NT) void k_quant_row_local(const void* __restrict__
 #pragma unroll
     for (int u = 0; u < UL; ++u)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[u][j]));
+      for (int j = 0; j < 8; ++j) m = mag_max(m, fabsf(v[u][j]));
   }
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
   __syncthreads();
   float A = part[0];
 #pragma unroll
-  for (int i = 1; i < NT / 64; ++i) A = fmaxf(A, part[i]);
+  for (int i = 1; i < NT / 64; ++i) A = mag_max(A, part[i]);
   const TensorScales ts = tensor_scales_from(A, T);
   if (threadIdx.x == 0) {
     g_out[blockIdx.x] = ts.g;
@@ -592,7 +614,8 @@ __global__ __launch_bounds__(NT) void k_quant_row_local(const void* __restrict__
 #pragma unroll
     for (int u = 0; u < UB; ++u) {
       const int64_t i = i0 + u * NT;
-      if (i < nblk) quant_block_row<FMT, B, SR>(v[u], ts, r0 + i / nb, i % nb, cols, seed, offset, q, s);
+      Health unused;
+      if (i < nblk) quant_block_row<FMT, B, SR>(v[u], ts, r0 + i / nb, i % nb, cols, seed, offset, q, s, unused);
     }
   }
 }
@@ -666,7 +689,8 @@ __global__ __launch_bounds__(NTL) void k_quant_row_local_reg(const void* __restr
         v[8 * c + 0] = bf16_lo(w.x); v[8 * c + 1] = bf16_hi(w.x); v[8 * c + 2] = bf16_lo(w.y); v[8 * c + 3] = bf16_hi(w.y);
         v[8 * c + 4] = bf16_lo(w.z); v[8 * c + 5] = bf16_hi(w.z); v[8 * c + 6] = bf16_lo(w.w); v[8 * c + 7] = bf16_hi(w.w);
       }
-      quant_block_row<FMT, B, SR>(v, ts, r0 + rr, (int64_t)bb, cols, seed, offset, q, s);
+      Health unused;
+      quant_block_row<FMT, B, SR>(v, ts, r0 + rr, (int64_t)bb, cols, seed, offset, q, s, unused);
     }
   }
 }
@@ -706,7 +730,7 @@ __global__ __launch_bounds__(NT) void k_stripe_amax(const void* __restrict__ x, 
 #pragma unroll
     for (int u = 0; u < UL; ++u)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[u][j]));
+      for (int j = 0; j < 8; ++j) m = mag_max(m, fabsf(v[u][j]));
   }
   wg_max_to(amax + blockIdx.y, m);
 }
@@ -738,7 +762,8 @@ template <int FMT, bool F32>
 __global__ __launch_bounds__(NT) void k_quant_2d(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
                                                  const float* __restrict__ d_amax, float T, uint8_t* __restrict__ q,
                                                  uint8_t* __restrict__ qt, uint8_t* __restrict__ s,
-                                                 float* __restrict__ d_amax_obs, float* __restrict__ d_g) {
+                                                 float* __restrict__ d_amax_obs, float* __restrict__ d_g,
+                                                 uint32_t* __restrict__ stats) {
   __shared__ float tile[WT][WT + 1];
   __shared__ float mults[WT / 16][WT / 16];
   const int64_t r0 = (int64_t)blockIdx.y * WT, c0 = (int64_t)blockIdx.x * WT;
@@ -764,15 +789,17 @@ __global__ __launch_bounds__(NT) void k_quant_2d(const void* __restrict__ x, int
   for (int i = 0; i < 16; ++i) v[i] = tile[r][sg * 16 + i];
   float m = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
-  m = fmaxf(m, __shfl_xor(m, 4, 64));
-  m = fmaxf(m, __shfl_xor(m, 8, 64));
-  m = fmaxf(m, __shfl_xor(m, 16, 64));
-  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  for (int i = 0; i < 16; ++i) m = mag_max(m, fabsf(v[i]));
+  m = mag_max(m, __shfl_xor(m, 4, 64));
+  m = mag_max(m, __shfl_xor(m, 8, 64));
+  m = mag_max(m, __shfl_xor(m, 16, 64));
+  m = mag_max(m, __shfl_xor(m, 32, 64));
   uint32_t code;
   float mult;
-  block_scale<FMT>(m, ts, code, mult);
+  Health hb, h;
+  block_scale<FMT>(m, ts, code, mult, hb);
   const bool rvalid = (r0 + r) < rows && (c0 + sg * 16) < cols;
+  h.add_if(rvalid && (r & 15) == 0, hb);        // one count per 16x16 tile
   if ((r & 15) == 0) {
     mults[r >> 4][sg] = mult;
     if (rvalid) s[((r0 + r) >> 4) * (cols / 16) + ((c0 >> 4) + sg)] = (uint8_t)code;
@@ -789,6 +816,7 @@ __global__ __launch_bounds__(NT) void k_quant_2d(const void* __restrict__ x, int
   if ((c0 + cc) < cols && (r0 + rs * 16) < rows)
     *reinterpret_cast<uint2*>(qt + (c0 + cc) * (rows / 2) + (r0 + rs * 16) / 2) = make_uint2(words[0], words[1]);
   if (d_amax_obs) wg_max_to(d_amax_obs, m);
+  health_flush(stats, h);
 }
 
 // ---------------------------------------------------------------- amax
@@ -821,7 +849,7 @@ __global__ __launch_bounds__(NT) void k_amax_plain(const void* __restrict__ x, i
 #pragma unroll
         for (int p = 0; p < P; ++p)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[u][p][j]));
+          for (int j = 0; j < 8; ++j) m = mag_max(m, fabsf(v[u][p][j]));
     }
   }
   wg_max_to(out, m);
@@ -854,12 +882,17 @@ __global__ __launch_bounds__(NT) void k_amax_hadamard(const void* __restrict__ x
     for (int i = 0; i < HN; ++i) v[i] = tile[u * HN + i][f];
     fwht_inplace<HN>(v);
 #pragma unroll
-    for (int i = 0; i < HN; ++i) m = fmaxf(m, fabsf(v[i]));   // padded rows/cols are zero
+    for (int i = 0; i < HN; ++i) m = mag_max(m, fabsf(v[i]));   // padded rows/cols are zero
   }
   wg_max_to(out, m);
 }
 
 __global__ void k_fill_f32(float* p, float v) { *p = v; }
+
+// health counts of a call start at zero (a kernel, not a memset: safe under graph capture)
+__global__ void k_zero_stats(uint32_t* p) {
+  if (threadIdx.x < FP4_STATS_WORDS) p[threadIdx.x] = 0u;
+}
 
 __global__ void k_write_g(const float* __restrict__ d_amax, float T, int fmt, float* __restrict__ d_g) {
   *d_g = (fmt == FMT_E8M0) ? 1.0f : tensor_scales(d_amax, T).g;
@@ -896,7 +929,7 @@ static hipError_t launch_row(const QuantArgs& a) {
   if (FP4_ROW_TILED && a.ld * (F32 ? 4 : 2) <= (int64_t(1) << 24) && a.cols <= (int64_t(1) << 25) &&
       tiles < (int64_t(1) << 31)) {
     hipLaunchKernelGGL((k_quant_row_t<FMT, B, SR, F32>), dim3((unsigned)tiles), dim3(NT), 0, a.stream, a.x, a.rows,
-                       a.cols, a.ld, a.d_amax, a.T, a.seed, a.offset, a.q, a.s, a.d_amax_obs, a.d_g);
+                       a.cols, a.ld, a.d_amax, a.T, a.seed, a.offset, a.q, a.s, a.d_amax_obs, a.d_g, a.stats);
     return hipGetLastError();
   }
   const int64_t nbr = a.cols / B;
@@ -907,7 +940,7 @@ static hipError_t launch_row(const QuantArgs& a) {
   const unsigned gy = (unsigned)(groups < 65535 ? groups : 65535);     // the kernel strides over the rest
   dim3 grid((unsigned)((nbr + (1 << tpr_log2) - 1) >> tpr_log2), gy);
   hipLaunchKernelGGL((k_quant_row<FMT, B, SR, F32>), grid, dim3(NT), 0, a.stream, a.x, a.rows, a.cols, a.ld, tpr_log2,
-                     a.d_amax, a.T, a.seed, a.offset, a.q, a.s, a.d_amax_obs, a.d_g);
+                     a.d_amax, a.T, a.seed, a.offset, a.q, a.s, a.d_amax_obs, a.d_g, 0, a.stats);
   return hipGetLastError();
 }
 
@@ -915,7 +948,7 @@ template <int FMT, int B, bool SR, bool F32, int HN>
 static hipError_t launch_col(const QuantArgs& a) {
   dim3 grid((unsigned)((a.rows + CT - 1) / CT), (unsigned)((a.cols + CF - 1) / CF));
   hipLaunchKernelGGL((k_quant_col<FMT, B, SR, F32, HN>), grid, dim3(NT), 0, a.stream, a.x, a.rows, a.cols, a.ld,
-                     a.d_amax, a.T, a.seed, a.offset, a.q, a.s, a.d_amax_obs, a.d_g);
+                     a.d_amax, a.T, a.seed, a.offset, a.q, a.s, a.d_amax_obs, a.d_g, a.stats);
   return hipGetLastError();
 }
 
@@ -936,7 +969,7 @@ static hipError_t launch_rowcol(const RowColArgs& a) {
   if (grid >= 8) grid &= ~(int64_t)7;
   hipLaunchKernelGGL((k_quant_rowcol<FMT, B, SRR, SRC, F32, HN>), dim3((unsigned)grid), dim3(NT), 0, a.stream, a.x, a.rows, a.cols,
                      a.ld, a.amax_r, a.T_r, a.seed_r, a.offset_r, a.amax_c, a.T_c, a.seed_c, a.offset_c, a.q, a.s,
-                     a.g_r, a.obs_r, a.qt, a.st, a.g_c, a.obs_c);
+                     a.g_r, a.obs_r, a.qt, a.st, a.g_c, a.obs_c, a.stats_r, a.stats_c);
   return hipGetLastError();
 }
 
@@ -965,6 +998,11 @@ hipError_t run_quantize_rowcol(const RowColArgs& a) {
   for (float* o : {a.obs_r, a.obs_c}) {
     if (!o) continue;
     hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, a.stream, o, 0.0f);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  for (uint32_t* h : {a.stats_r, a.stats_c}) {
+    if (!h) continue;
+    hipLaunchKernelGGL(k_zero_stats, dim3(1), dim3(64), 0, a.stream, h);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.rows == 0 || a.cols == 0) {
@@ -1047,7 +1085,7 @@ template <int FMT, bool F32>
 static hipError_t launch_2d(const QuantArgs& a) {
   dim3 grid((unsigned)((a.cols + WT - 1) / WT), (unsigned)((a.rows + WT - 1) / WT));
   hipLaunchKernelGGL((k_quant_2d<FMT, F32>), grid, dim3(NT), 0, a.stream, a.x, a.rows, a.cols, a.ld, a.d_amax, a.T, a.q,
-                     a.qt, a.s, a.d_amax_obs, a.d_g);
+                     a.qt, a.s, a.d_amax_obs, a.d_g, a.stats);
   return hipGetLastError();
 }
 
@@ -1077,6 +1115,10 @@ hipError_t run_quantize(const QuantArgs& a) {
   hipError_t e;
   if (a.d_amax_obs) {
     hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, a.stream, a.d_amax_obs, 0.0f);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (a.stats) {
+    hipLaunchKernelGGL(k_zero_stats, dim3(1), dim3(64), 0, a.stream, a.stats);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.rows == 0 || a.cols == 0) {

@@ -9,9 +9,16 @@ namespace fp4k {
 
 constexpr int NT = 256;
 
+// Maximum of two magnitudes with NaN propagation (IEEE 754-2019 maximum, v_maximum3_f32 on
+// gfx950, abs folded into its operand modifiers): a NaN anywhere in a block or tensor makes
+// its maximum NaN, as the float maximum of the oracle does, so the tensor amax, the stripe
+// maxima and the block maxima of every kernel agree on NaN inputs (a maxNum-style max would
+// return the other operand and hide the NaN).
+__device__ __forceinline__ float mag_max(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  for (int o = 32; o > 0; o >>= 1) v = mag_max(v, __shfl_xor(v, o, 64));
   return v;
 }
 
@@ -40,7 +47,7 @@ __device__ __forceinline__ void wg_max_to(float* out, float v) {
   if (threadIdx.x == 0) {
     float m = part[0];
 #pragma unroll
-    for (int i = 1; i < NT / 64; ++i) m = fmaxf(m, part[i]);
+    for (int i = 1; i < NT / 64; ++i) m = mag_max(m, part[i]);
     atomic_max_nonneg(out, m);
   }
 }
@@ -66,16 +73,69 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, float* v) 
   }
 }
 
-// Scale code and payload multiplier of one block with maximum amax_b.
+// Quantizer health counts ("UE5M3 FP4 Block Scaling for Stable Language Model Pretraining",
+// key contributions: a stale cached amax is safe while the data grows by less than
+// 61440 / T; these counts make that headroom visible per call). Per block:
+//   sat     UE5M3/E4M3: the unrounded block scale amax_b * s_blk exceeds the format maximum
+//           (the scale saturates); E8M0 has no tensor scale and counts none
+//   zero    the block scale encodes to zero and the zero-scale rule replaces it by one
+//           (E8M0: a zero block, which takes exponent 0)
+//   nonfin  the block maximum is not finite (an Inf or NaN input)
+struct Health {
+  uint32_t sat = 0, zero = 0, nonfin = 0;
+  __device__ __forceinline__ void add_if(bool c, const Health& o) {
+    sat += c ? o.sat : 0u;
+    zero += c ? o.zero : 0u;
+    nonfin += c ? o.nonfin : 0u;
+  }
+};
+
+// Scale code and payload multiplier of one block with maximum amax_b; adds the block to h.
 template <int FMT>
-__device__ __forceinline__ void block_scale(float amax_b, const TensorScales& ts, uint32_t& code, float& mult) {
+__device__ __forceinline__ void block_scale(float amax_b, const TensorScales& ts, uint32_t& code, float& mult,
+                                            Health& h) {
+  h.nonfin += (amax_b <= 3.4028234663852886e38f) ? 0u : 1u;
   if constexpr (FMT == FMT_E8M0) {
     code = e8m0_code(amax_b);
     mult = e8m0_inv(code);
+    h.zero += (amax_b == 0.0f) ? 1u : 0u;
   } else {
-    code = enc_scale3<FMT>(amax_b * ts.s_blk);
+    const float v = amax_b * ts.s_blk;
+    code = enc_scale3<FMT>(v);
+    h.sat += (v > ScaleFmt<FMT>::MAXV) ? 1u : 0u;
+    h.zero += (code == 0) ? 1u : 0u;
     if (code == 0) code = ScaleFmt<FMT>::ONE;          // zero-scale rule
     mult = ts.s_enc / dec_scale3<FMT>(code);           // correctly rounded division
+  }
+}
+template <int FMT>
+__device__ __forceinline__ void block_scale(float amax_b, const TensorScales& ts, uint32_t& code, float& mult) {
+  Health unused;
+  block_scale<FMT>(amax_b, ts, code, mult, unused);
+}
+
+// Adds the workgroup's counts to stats[0..2] (sat, zero, nonfin): a wave sum, a workgroup sum
+// through LDS, then one atomic per non-zero count. Every thread of the workgroup calls it
+// with the same stats pointer; nothing happens when it is null.
+__device__ __forceinline__ void health_flush(uint32_t* stats, Health h) {
+  if (!stats) return;
+  __shared__ uint32_t part[3][NT / 64];
+  uint32_t c[3] = {h.sat, h.zero, h.nonfin};
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) c[k] += __shfl_xor(c[k], o, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) part[k][threadIdx.x >> 6] = c[k];
+  }
+  __syncthreads();
+  if (threadIdx.x < 3) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) t += part[threadIdx.x][i];
+    if (t) atomicAdd(stats + threadIdx.x, t);
   }
 }
 
@@ -106,9 +166,9 @@ __device__ __forceinline__ void payload(const float* v, float mult, uint64_t i0,
 template <int G>
 __device__ __forceinline__ float group_max(float v) {
   if constexpr (G >= 2)
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));  // lane ^ 1
+    v = mag_max(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));  // lane ^ 1
   if constexpr (G >= 4)
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));  // lane ^ 2
+    v = mag_max(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));  // lane ^ 2
   static_assert(G == 1 || G == 2 || G == 4, "ROW blocks span 1, 2 or 4 lanes");
   return v;
 }

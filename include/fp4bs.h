@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FP4BS_ABI_VERSION 1
+#define FP4BS_ABI_VERSION 2
 
 typedef enum {
   FP4_OK = 0,
@@ -127,7 +127,15 @@ typedef struct {
  *   q_t      TILE2D only: the transposed (dgrad) payload [cols x rows/2]; NULL otherwise
  *   d_g      device float receiving the tensor decode scale g = 1/s_enc (1 for E8M0); may be NULL
  *   d_amax_obs  optional device float receiving the observed max|x| of this tensor (after
- *            the Hadamard rotation when enabled); overwritten
+ *            the Hadamard rotation when enabled); overwritten. A NaN anywhere in x makes it NaN
+ *            (NaN propagates through every maximum the library takes, as in the float maximum)
+ *   d_stats  optional device uint32[3], overwritten with the call's health counts [UE5M3 key
+ *            contributions: a stale cached amax stays safe while the data grows by less than
+ *            61440/T; these counts show when it does not]: [0] blocks whose unrounded scale
+ *            amax_b*s_blk exceeds the format maximum (the scale saturates; always 0 for E8M0),
+ *            [1] blocks whose scale encodes to zero and becomes one (E8M0: all-zero blocks),
+ *            [2] blocks whose maximum is not finite (an Inf or NaN input; out of contract for
+ *            the payload). A TILE2D block is a 16x16 tile.
  * Arithmetic (float32, nearest-even): s_enc = 6T/A, s_blk = T/A, g = 1/s_enc (all 1 when A
  * is 0 or not finite or 6T/A overflows); block scale S = enc(amax_b*s_blk) saturating,
  * replaced by 1 if it encodes to 0; payload E2M1(x * (s_enc/S)). E8M0: exponent
@@ -140,7 +148,7 @@ typedef struct {
 fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld,
                         const fp4_quant_cfg* cfg, const float* d_amax,
                         uint8_t* q, uint8_t* s, uint8_t* q_t, float* d_g, float* d_amax_obs,
-                        void* stream);
+                        uint32_t* d_stats, void* stream);
 
 /*
  * fp4_quantize_rowcol - the ROW view and the COL view of one tensor from a single read of x
@@ -157,6 +165,8 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t co
  *            tensor, so the two usually differ.
  *   d_g, d_g_t, d_amax_obs_row, d_amax_obs_col  optional device float outputs, as in
  *            fp4_quantize
+ *   d_stats_row, d_stats_col  optional device uint32[3] health counts of each view, as in
+ *            fp4_quantize
  * Requires the shape conditions of both views: cols % B == 0, rows % B == 0 and
  * rows % hadamard_n == 0; also ld * elem_size <= 2^24 bytes, rows <= 2^24 and cols <= 2^25
  * (FP4_EUNSUPPORTED otherwise). Empty tensors are a no-op (g values are still written).
@@ -165,7 +175,8 @@ fp4_status fp4_quantize_rowcol(const void* x, int32_t x_dtype, int64_t rows, int
                                const fp4_quant_cfg* cfg_row, const fp4_quant_cfg* cfg_col,
                                const float* d_amax_row, const float* d_amax_col,
                                uint8_t* q, uint8_t* s, float* d_g, float* d_amax_obs_row,
-                               uint8_t* q_t, uint8_t* s_t, float* d_g_t, float* d_amax_obs_col, void* stream);
+                               uint8_t* q_t, uint8_t* s_t, float* d_g_t, float* d_amax_obs_col,
+                               uint32_t* d_stats_row, uint32_t* d_stats_col, void* stream);
 
 /*
  * fp4_fake_quant - inference fake quantization: y = the decoded value of x's FP4 ROW-view

@@ -35,7 +35,7 @@ Pins (tests/test_oracle_*.py) and their strength:
 """
 from . import formats, philox, hadamard, quantize, gemm, exact, fakequant, fp8convert, local
 from .formats import UE5M3, E4M3, E8M0
-from .quantize import (AmaxCache, QuantResult, quantize_1d, quantize_2d, quantize_col, tensor_amax,
+from .quantize import (AmaxCache, QuantResult, block_health, quantize_1d, quantize_2d, quantize_col, tensor_amax,
                        tensor_scales, pack_codes, unpack_codes, transposed_view)
 from .gemm import gemm_model, gemm_fp64, rtz_add_f32, operand_from_quant, output_scale, expand_2d_scales
 from .fakequant import dequantize, fake_quant, f32_to_bf16_bits, FakeQuantPolicy

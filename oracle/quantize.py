@@ -63,6 +63,42 @@ def e8m0_block(amax_b: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return (E + 127).astype(np.uint8), mult
 
 
+def block_health(x: np.ndarray, fmt: int, block: int = 16, amax=None, T: float = 448.0, view: str = "row",
+                 hadamard_n: int = 0) -> tuple[int, int, int]:
+    """Health counts of a quantization (saturated, zero-scale, non-finite blocks), from the
+    block maxima alone, so that inputs holding Inf or NaN (outside the payload's contract)
+    can be counted too.
+
+    view: 'row' (blocks along the columns of x), 'col' (the weight-gradient view: blocks along
+    the tokens of the optionally rotated x), '2d' (16x16 tiles). A block maximum is the float
+    maximum of |x| over the block, NaN if the block holds a NaN.
+    - saturated: the unrounded scale float32(amax_b * s_blk) exceeds the format maximum (so the
+      scale clips; the key-contributions headroom of 61440/T is the growth that stays below
+      it). E8M0 has no tensor scale and counts none.
+    - zero-scale: the scale encodes to zero and the zero rule replaces it by one (E8M0: an
+      all-zero block).
+    - non-finite: the block maximum is Inf or NaN."""
+    x = np.asarray(x, dtype=np.float32)
+    if view == "col":
+        x = transposed_view(x, hadamard_n)
+    if view == "2d":
+        R, K = x.shape
+        amax_b = np.max(np.abs(x.reshape(R // 16, 16, K // 16, 16)), axis=(1, 3))
+    else:
+        R, K = x.shape
+        amax_b = np.max(np.abs(x.reshape(R, K // block, block)), axis=2)
+    n_nonfin = int(np.sum(~np.isfinite(amax_b)))
+    if fmt == F.E8M0:
+        return 0, int(np.sum(amax_b == 0)), n_nonfin
+    _, s_blk, _ = tensor_scales(amax, T)
+    with np.errstate(over="ignore", invalid="ignore"):
+        v = (amax_b * s_blk).astype(np.float32)
+    fin = np.isfinite(v)
+    n_sat = int(np.sum(v[fin].astype(np.float64) > F.SCALE_MAX[fmt]) + np.sum(np.isposinf(v)))
+    n_zero = int(np.sum(F.decode_scale(F.encode_scale(v[fin], fmt), fmt) == 0.0))
+    return n_sat, n_zero, n_nonfin
+
+
 @dataclass
 class QuantResult:
     codes: np.ndarray        # uint8 E2M1 codes, [rows, K] (unpacked), sign in bit 3
@@ -72,6 +108,7 @@ class QuantResult:
     block: int
     n_sat: int = 0           # blocks whose unrounded scale exceeded the format maximum
     n_zero: int = 0          # blocks whose scale rounded to zero and was replaced by one
+                             # (E8M0: all-zero blocks, which take exponent 0)
 
     @property
     def packed(self) -> np.ndarray:
@@ -141,7 +178,7 @@ def quantize_1d(x: np.ndarray, fmt: int, block: int, amax=None, T: float = 448.0
     if fmt == F.E8M0:
         codes, mult = e8m0_block(amax_b)
         q = _payload(xb, mult, rounding, seed, offset, K, row0)
-        return QuantResult(q, codes, np.float32(1.0), fmt, block)
+        return QuantResult(q, codes, np.float32(1.0), fmt, block, 0, int(np.sum(amax_b == 0)))
     s_enc, s_blk, g = tensor_scales(amax, T)
     codes, mult, n_sat, n_zero = _block_scales(amax_b, s_enc, s_blk, fmt)
     q = _payload(xb, mult, rounding, seed, offset, K, row0)

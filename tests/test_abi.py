@@ -74,7 +74,7 @@ def test_quantize_sizes(lib):
 def test_quantize_rejects_bad_config(lib, kw, status):
     c = cfg(**kw)
     st = lib.fp4_quantize(ctypes.c_void_p(16), 0, 64, 64, 64, ctypes.byref(c), ctypes.c_void_p(16),
-                          ctypes.c_void_p(16), ctypes.c_void_p(16), None, None, None, None)
+                          ctypes.c_void_p(16), ctypes.c_void_p(16), None, None, None, None, None)
     assert st == status
     assert lib.fp4_last_error().decode()
 
@@ -82,19 +82,23 @@ def test_quantize_rejects_bad_config(lib, kw, status):
 def test_quantize_rejects_bad_shapes_and_pointers(lib):
     c = cfg()
     P = ctypes.c_void_p(4096)
-    assert lib.fp4_quantize(P, 0, 64, 40, 40, ctypes.byref(c), P, P, P, None, None, None, None) == _lib.FP4_EINVAL
-    assert lib.fp4_quantize(P, 0, 64, 64, 32, ctypes.byref(c), P, P, P, None, None, None, None) == _lib.FP4_EINVAL
-    assert lib.fp4_quantize(None, 0, 64, 64, 64, ctypes.byref(c), P, P, P, None, None, None, None) == _lib.FP4_EINVAL
+    assert lib.fp4_quantize(P, 0, 64, 40, 40, ctypes.byref(c), P, P, P, None, None, None, None, None) == _lib.FP4_EINVAL
+    assert lib.fp4_quantize(P, 0, 64, 64, 32, ctypes.byref(c), P, P, P, None, None, None, None, None) == _lib.FP4_EINVAL
+    assert lib.fp4_quantize(None, 0, 64, 64, 64, ctypes.byref(c), P, P, P, None, None, None, None, None) == _lib.FP4_EINVAL
     assert lib.fp4_quantize(ctypes.c_void_p(4098), 0, 64, 64, 64, ctypes.byref(c), P, P, P, None, None, None,
-                            None) == _lib.FP4_EALIGN
-    assert lib.fp4_quantize(P, 0, 64, 64, 68, ctypes.byref(c), P, P, P, None, None, None, None) == _lib.FP4_EALIGN
-    assert lib.fp4_quantize(P, 0, 64, 64, 64, ctypes.byref(c), None, P, P, None, None, None, None) == _lib.FP4_EINVAL
-    assert lib.fp4_quantize(P, 3, 64, 64, 64, ctypes.byref(c), P, P, P, None, None, None, None) == _lib.FP4_EINVAL
+                            None, None) == _lib.FP4_EALIGN
+    assert lib.fp4_quantize(P, 0, 64, 64, 68, ctypes.byref(c), P, P, P, None, None, None, None, None) == _lib.FP4_EALIGN
+    assert lib.fp4_quantize(P, 0, 64, 64, 64, ctypes.byref(c), None, P, P, None, None, None, None, None) == _lib.FP4_EINVAL
+    assert lib.fp4_quantize(P, 3, 64, 64, 64, ctypes.byref(c), P, P, P, None, None, None, None, None) == _lib.FP4_EINVAL
     c2 = cfg(view=1)
-    assert lib.fp4_quantize(P, 0, 40, 64, 64, ctypes.byref(c2), P, P, P, None, None, None, None) == _lib.FP4_EINVAL
+    assert lib.fp4_quantize(P, 0, 40, 64, 64, ctypes.byref(c2), P, P, P, None, None, None, None, None) == _lib.FP4_EINVAL
     c3 = cfg(view=2)
-    assert lib.fp4_quantize(P, 0, 64, 64, 64, ctypes.byref(c3), P, P, P, None, None, None, None) == _lib.FP4_EINVAL
+    assert lib.fp4_quantize(P, 0, 64, 64, 64, ctypes.byref(c3), P, P, P, None, None, None, None, None) == _lib.FP4_EINVAL
     assert "q_t" in lib.fp4_last_error().decode()
+    # the health-count output is 4-byte aligned
+    assert lib.fp4_quantize(P, 0, 64, 64, 64, ctypes.byref(c), P, P, P, None, None, None, ctypes.c_void_p(4098),
+                            None) == _lib.FP4_EALIGN
+    assert "stats" in lib.fp4_last_error().decode()
 
 
 def op(rows=64, k=128, fmt=0, block=16, layout=0, q=4096, s=4096):
@@ -142,11 +146,11 @@ def test_binding_fails_loudly_without_gpu_tensors():
                      amax=torch.ones(1))
 
 
-def rowcol(lib, cr, cc, rows=64, cols=64, ld=64, x=4096, q=4096, qt=4096, a_r=16, a_c=16):
+def rowcol(lib, cr, cc, rows=64, cols=64, ld=64, x=4096, q=4096, qt=4096, a_r=16, a_c=16, st_r=None, st_c=None):
     P = ctypes.c_void_p(4096)
     return lib.fp4_quantize_rowcol(ctypes.c_void_p(x), 0, rows, cols, ld, ctypes.byref(cr), ctypes.byref(cc),
                                    ctypes.c_void_p(a_r), ctypes.c_void_p(a_c), ctypes.c_void_p(q), P, None, None,
-                                   ctypes.c_void_p(qt), P, None, None, None)
+                                   ctypes.c_void_p(qt), P, None, None, st_r, st_c, None)
 
 
 def test_rowcol_rejects_bad_arguments(lib):
@@ -166,6 +170,7 @@ def test_rowcol_rejects_bad_arguments(lib):
     assert rowcol(lib, r, c, rows=(1 << 24) + 32) == _lib.FP4_EUNSUPPORTED  # 32-bit in-tile offsets
     mr, mc = cfg(fmt=2, block=32, view=0, T=0.0), cfg(fmt=2, block=32, view=1, T=0.0)
     assert rowcol(lib, mr, mc, rows=48) == _lib.FP4_EINVAL                  # 48 % 32
+    assert rowcol(lib, r, c, st_c=ctypes.c_void_p(4098)) == _lib.FP4_EALIGN  # health counts are words
     assert lib.fp4_last_error().decode()
 
 

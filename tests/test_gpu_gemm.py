@@ -140,8 +140,9 @@ def test_tiny_end_to_end():
 
 @pytest.mark.parametrize("fmt,block", [(OF.UE5M3, 16), (OF.E4M3, 16), (OF.E8M0, 32)])
 def test_format_sweep_2048(fmt, block):
-    """2048^3 bf16 N(0,1) with 0.1% outlier columns, each format, quantize + GEMM on the GPU;
-    128 output rows against the oracle, all rows against float64 within tolerance."""
+    """2048^3 bf16 N(0,1) with 0.1% outlier columns, each format, quantize + GEMM on the GPU:
+    every output bit-exact against the oracle's group model and within the tolerance of the
+    float64 product."""
     cfg = synth.make_config(2)
     X, W = cfg["X"], cfg["W"]
     Ax, Aw = oracle.tensor_amax(X.values), oracle.tensor_amax(W.values)
@@ -154,12 +155,11 @@ def test_format_sweep_2048(fmt, block):
     assert np.array_equal(y.view(np.uint32), y_again.cpu().numpy().view(np.uint32))   # run-to-run
     rx = oracle.quantize_1d(X.values, fmt, block, amax=Ax, T=448)
     rw = oracle.quantize_1d(W.values, fmt, block, amax=Aw, T=448)
-    rows = np.r_[0:64, 1000:1032, 2016:2048]
-    assert_f32_bits_equal(y[rows], _oracle_y(rx, rw, rows=rows), f"fmt {fmt}")
+    assert_f32_bits_equal(y, _oracle_y(rx, rw), f"fmt {fmt}")
     a, sa = oracle.operand_from_quant(rx)
     b, sb = oracle.operand_from_quant(rw)
-    y64, sabs = oracle.gemm_fp64(a[rows], sa[rows], b, sb, block, rx.g, rw.g)
-    assert np.all(np.abs(y[rows] - y64) <= 1e-6 * sabs)
+    y64, sabs = oracle.gemm_fp64(a, sa, b, sb, block, rx.g, rw.g)
+    assert np.all(np.abs(y - y64) <= 1e-6 * sabs)
 
 
 def test_backward_dgrad_wgrad():

@@ -204,12 +204,12 @@ def test_amax_cache_update_and_reset():
 
 @pytest.mark.parametrize("r", [1.3, 3.7, 0.2])
 def test_stochastic_rounding_unbiased_over_a_million_draws(r):
-    """The whole SR path of the library (Philox draws, the E2M1 decision, packing): 65536 rows
+    """The whole SR path of the library (Philox draws, the E2M1 decision, packing): 70000 rows
     of 16, each row a block with one element 6 (so that the block scale is 448 and the
-    payload multiplier is exactly 1) and 15 elements r. The mean of the 983040 decoded SR
+    payload multiplier is exactly 1) and 15 elements r. The mean of the 1,050,000 decoded SR
     values lies within 3 sigma (plus the 2^-16 resolution of the draws times the grid step)
     of r, and every value is one of r's two neighbouring codebook values."""
-    rows = 65536
+    rows = 70000
     x = np.full((rows, 16), np.float32(r), dtype=np.float32)
     x[:, 0] = 6.0
     amax = dev_scalar(np.float32(6.0))

@@ -95,6 +95,7 @@ def test_down_proj_backward_full_size_sampled(down_proj, fmt):
         assert_bytes_equal(qdy.s[r0:r1], rq.scales, f"dY ROW scales rows {r0}")
     for (f0, f1), rq in zip(feat_out, _col_slices(dY, fmt, B, feat_out, **sr_col)):
         assert_bytes_equal(qdyt.q[f0:f1], rq.packed, f"dY COL features {f0}")
+        assert_bytes_equal(qdyt.s[f0:f1], rq.scales, f"dY COL scales features {f0}")
     # dgrad blocks: rows = token slices, cols = input-feature slices (rows of the W^T view)
     a_parts = _row_slices(dY, fmt, B, tok, **sr_row)
     if E8:

@@ -193,3 +193,48 @@ def test_true_amax_maps_to_scale_T_and_payload_6(fmt, T, sign):
         assert code == want, (view, hex(code))
         decoded = 6.0 * T * float(q.g)
         assert abs(decoded - abs(v)) <= 4 * 2.0 ** -24 * abs(v), (view, decoded, v)
+
+
+def test_block_health_matches_quantizer_counts_and_headroom_edge():
+    """The health counts agree with the quantizer's own saturation and zero-scale counts (whose
+    saturation edge is pinned at gamma * T = 61440 above), in every view."""
+    rng = np.random.default_rng(41)
+    base = rng.uniform(-1, 1, (64, 256)).astype(np.float32)
+    base[3, 32:48] = 0.0                      # a zero block (ROW view)
+    base[0, 0] = 1.0
+    for gamma in (1.0, 137.0, 137.3, 300.0):
+        x = (base * np.float32(gamma)).astype(np.float32)
+        for fmt in (F.UE5M3, F.E4M3):
+            q = oracle.quantize_1d(x, fmt, 16, amax=1.0, T=448)
+            assert oracle.block_health(x, fmt, 16, amax=1.0, T=448) == (q.n_sat, q.n_zero, 0)
+            qc = oracle.quantize_col(x, fmt, 16, amax=1.0, T=448, hadamard_n=16)
+            assert oracle.block_health(x, fmt, 16, amax=1.0, T=448, view="col", hadamard_n=16) == \
+                (qc.n_sat, qc.n_zero, 0)
+            q2 = oracle.quantize_2d(x, fmt, amax=1.0, T=448)
+            assert oracle.block_health(x, fmt, 16, amax=1.0, T=448, view="2d") == (q2.n_sat, q2.n_zero, 0)
+        sat = oracle.block_health(x, F.UE5M3, 16, amax=1.0, T=448)[0]
+        assert (sat > 0) == (gamma * 448 > 61440), gamma
+    qm = oracle.quantize_1d(base, F.E8M0, 32)
+    assert oracle.block_health(base, F.E8M0, 32) == (0, qm.n_zero, 0) and qm.n_zero == 0
+    z = base.copy()
+    z[5, 64:96] = 0.0
+    assert oracle.block_health(z, F.E8M0, 32) == (0, 1, 0) == (0, oracle.quantize_1d(z, F.E8M0, 32).n_zero, 0)
+
+
+def test_block_health_counts_nonfinite_blocks():
+    """Hand-placed Inf and NaN inputs: each block holding one counts once as non-finite; an Inf
+    block's unrounded scale is infinite, so it also counts as saturated (a NaN block does not)."""
+    x = np.random.default_rng(42).uniform(-1, 1, (32, 128)).astype(np.float32)
+    x[2, 5] = np.inf           # ROW block (2, 0)
+    x[2, 7] = np.nan           # same block
+    x[9, 100] = -np.inf        # ROW block (9, 6)
+    x[17, 40] = np.nan         # ROW block (17, 2)
+    assert oracle.block_health(x, F.UE5M3, 16, amax=1.0, T=448) == (1, 0, 3)
+    assert oracle.block_health(x, F.E8M0, 32) == (0, 0, 3)
+    # COL view: blocks run along 16 tokens of one feature: (feature 5, tokens 0-15),
+    # (feature 7, tokens 0-15), (100, 0-15), (40, 16-31)
+    assert oracle.block_health(x, F.UE5M3, 16, amax=1.0, T=448, view="col") == (2, 0, 4)
+    # 2D tiles: (0, 0) holds the Inf and a NaN (its maximum is NaN: not saturated), (0, 6) the
+    # -inf, (1, 2) the NaN
+    assert oracle.block_health(x, F.E4M3, 16, amax=1.0, T=448, view="2d") == (1, 0, 3)
+    assert np.isnan(oracle.tensor_amax(x))
