@@ -22,7 +22,8 @@ ROW, COL, TILE2D = FP4_VIEW_ROW, FP4_VIEW_COL, FP4_VIEW_TILE2D
 __all__ = ["UE5M3", "E4M3", "E8M0", "ROW", "COL", "TILE2D", "QTensor", "AmaxCache", "quantize", "quantize_rowcol",
            "fake_quant", "dequantize", "FakeQuantPolicy", "mxfp4_to_fp8", "quantize_local",
            "tensor_amax",
-           "gemm_fprop", "gemm_dgrad", "gemm_wgrad", "debug_encode", "FP4Error", "library"]
+           "gemm_fprop", "gemm_dgrad", "gemm_wgrad", "scale_range", "check_range", "new_stats", "debug_encode",
+           "FP4Error", "library"]
 
 
 def library() -> ctypes.CDLL:
@@ -327,19 +328,47 @@ def _gemm(name: str, a: QTensor, b: QTensor, canon: bool, hadamard_n: int | None
     return out
 
 
-def gemm_fprop(x: QTensor, w: QTensor, canon: bool = False, out: torch.Tensor | None = None) -> torch.Tensor:
-    """Y = X . W^T (fp4_gemm_fprop)."""
+def scale_range(a: QTensor) -> torch.Tensor:
+    """fp4_scale_range: int32 device tensor [min code, max code] of the operand's scale codes."""
+    lib = _lib.load()
+    out = torch.empty(2, dtype=torch.int32, device=a.q.device)
+    op = a.operand()
+    _lib.check(lib.fp4_scale_range(ctypes.byref(op), _ptr(out), _stream()))
+    return out
+
+
+def check_range(a: QTensor, b: QTensor) -> None:
+    """Checked mode of a GEMM: raises FP4Error (FP4_ERANGE) when the two operands' scale codes
+    could take a block partial outside the GEMM's exact range. Synchronises (the ranges are
+    read back to the host)."""
+    lib = _lib.load()
+    ra, rb = scale_range(a).cpu().numpy(), scale_range(b).cpu().numpy()
+    A = (ctypes.c_int32 * 2)(int(ra[0]), int(ra[1]))
+    B = (ctypes.c_int32 * 2)(int(rb[0]), int(rb[1]))
+    _lib.check(lib.fp4_gemm_check_range(int(a.fmt), A, B))
+
+
+def gemm_fprop(x: QTensor, w: QTensor, canon: bool = False, out: torch.Tensor | None = None,
+               checked: bool = False) -> torch.Tensor:
+    """Y = X . W^T (fp4_gemm_fprop). checked: verify the exact range first (check_range)."""
+    if checked:
+        check_range(x, w)
     return _gemm("fp4_gemm_fprop", x, w, canon, None, out)
 
 
-def gemm_dgrad(dy: QTensor, wt: QTensor, canon: bool = False, out: torch.Tensor | None = None) -> torch.Tensor:
+def gemm_dgrad(dy: QTensor, wt: QTensor, canon: bool = False, out: torch.Tensor | None = None,
+               checked: bool = False) -> torch.Tensor:
     """dX = dY . W (fp4_gemm_dgrad); wt is the weight's transposed operand."""
+    if checked:
+        check_range(dy, wt)
     return _gemm("fp4_gemm_dgrad", dy, wt, canon, None, out)
 
 
 def gemm_wgrad(dyt: QTensor, xt: QTensor, hadamard_n: int = 0, canon: bool = False,
-               out: torch.Tensor | None = None) -> torch.Tensor:
+               out: torch.Tensor | None = None, checked: bool = False) -> torch.Tensor:
     """dW = dY^T . X (fp4_gemm_wgrad) from the two COL-view operands."""
+    if checked:
+        check_range(dyt, xt)
     return _gemm("fp4_gemm_wgrad", dyt, xt, canon, hadamard_n, out)
 
 

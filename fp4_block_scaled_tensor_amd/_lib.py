@@ -7,8 +7,8 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfp4bs.so")
 
-FP4_OK, FP4_EINVAL, FP4_EUNSUPPORTED, FP4_EALIGN, FP4_EHIP = range(5)
-STATUS_NAMES = {0: "FP4_OK", 1: "FP4_EINVAL", 2: "FP4_EUNSUPPORTED", 3: "FP4_EALIGN", 4: "FP4_EHIP"}
+FP4_OK, FP4_EINVAL, FP4_EUNSUPPORTED, FP4_EALIGN, FP4_EHIP, FP4_ERANGE = range(6)
+STATUS_NAMES = {0: "FP4_OK", 1: "FP4_EINVAL", 2: "FP4_EUNSUPPORTED", 3: "FP4_EALIGN", 4: "FP4_EHIP", 5: "FP4_ERANGE"}
 FP4_UE5M3, FP4_E4M3, FP4_E8M0 = 0, 1, 2
 FP4_VIEW_ROW, FP4_VIEW_COL, FP4_VIEW_TILE2D = 0, 1, 2
 FP4_IN_BF16, FP4_IN_FP32 = 0, 1
@@ -17,7 +17,8 @@ ABI_VERSION = 2
 
 EXPORTED = [
     "fp4_quantize", "fp4_quantize_rowcol", "fp4_fake_quant", "fp4_dequantize", "fp4_mxfp4_to_fp8", "fp4_quantize_local", "fp4_quantize_sizes", "fp4_tensor_amax", "amax_cache_update", "amax_cache_reset",
-    "fp4_gemm_fprop", "fp4_gemm_dgrad", "fp4_gemm_wgrad", "fp4_debug_encode", "fp4_last_error", "fp4_abi_version",
+    "fp4_gemm_fprop", "fp4_gemm_dgrad", "fp4_gemm_wgrad", "fp4_scale_range", "fp4_gemm_check_range",
+    "fp4_debug_encode", "fp4_last_error", "fp4_abi_version",
 ]
 
 
@@ -57,6 +58,8 @@ SIGNATURES = {
     "fp4_gemm_fprop": ([ctypes.POINTER(Operand), ctypes.POINTER(Operand), _P, _I32, _P], ctypes.c_int),
     "fp4_gemm_dgrad": ([ctypes.POINTER(Operand), ctypes.POINTER(Operand), _P, _I32, _P], ctypes.c_int),
     "fp4_gemm_wgrad": ([ctypes.POINTER(Operand), ctypes.POINTER(Operand), _P, _I32, _I32, _P], ctypes.c_int),
+    "fp4_scale_range": ([ctypes.POINTER(Operand), _P, _P], ctypes.c_int),
+    "fp4_gemm_check_range": ([_I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)], ctypes.c_int),
     "fp4_debug_encode": ([_P, _P, _I64, _I32, _P, _P], ctypes.c_int),
     "fp4_last_error": ([], ctypes.c_char_p),
     "fp4_abi_version": ([], ctypes.c_int32),

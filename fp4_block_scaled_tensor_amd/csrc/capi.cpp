@@ -445,6 +445,30 @@ fp4_status amax_cache_reset(const fp4_amax_cache* cache, void* stream) {
   return hip_status(fp4k::run_cache_reset(cache->valid, (hipStream_t)stream), "amax_cache_reset");
 }
 
+fp4_status fp4_scale_range(const fp4_operand* a, int32_t* d_range, void* stream) {
+  fp4_status st;
+  if ((st = check_operand(a, "operand")) != FP4_OK) return st;
+  if (!d_range || !aligned(d_range, 4)) return fail(FP4_EINVAL, "d_range must be a 4-byte aligned device pointer");
+  const int64_t n = a->scale_layout == FP4_SCALES_1D ? a->rows * (a->k / a->block) : (a->rows / 16) * (a->k / 16);
+  return hip_status(fp4k::run_scale_range(a->s, n, d_range, (hipStream_t)stream), "fp4_scale_range");
+}
+
+fp4_status fp4_gemm_check_range(int32_t fmt, const int32_t* range_a, const int32_t* range_b) {
+  if (!range_a || !range_b) return fail(FP4_EINVAL, "NULL range");
+  if (fmt != FP4_UE5M3 && fmt != FP4_E4M3 && fmt != FP4_E8M0) return fail(FP4_EINVAL, "unknown scale format %d", fmt);
+  for (const int32_t* r : {range_a, range_b})
+    if (r[0] < 0 || r[1] > 255 || (r[0] > r[1] && !(r[0] == 255 && r[1] == 0)))
+      return fail(FP4_EINVAL, "a range is [min code, max code] within [0, 255]");
+  if (fmt != FP4_E8M0) return ok();   // UE5M3 / E4M3 partials always lie inside the normal range
+  if ((range_a[0] == 255 && range_a[1] == 0) || (range_b[0] == 255 && range_b[1] == 0)) return ok();   // empty
+  // E = code - 127; every combined exponent Ea + Eb must lie in [-124, 116]
+  const int lo = range_a[0] + range_b[0] - 254, hi = range_a[1] + range_b[1] - 254;
+  if (lo < -124 || hi > 116)
+    return fail(FP4_ERANGE, "MXFP4 combined block exponents reach [%d, %d], outside the exact range [-124, 116]", lo,
+                hi);
+  return ok();
+}
+
 fp4_status fp4_gemm_fprop(const fp4_operand* x, const fp4_operand* w, float* y, int32_t canon, void* stream) {
   if (x && x->scale_layout != FP4_SCALES_1D) return fail(FP4_EUNSUPPORTED, "fprop: activation needs 1D scales");
   if (w && w->scale_layout == FP4_SCALES_2D_T)

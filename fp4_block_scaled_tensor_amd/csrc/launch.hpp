@@ -141,6 +141,7 @@ hipError_t run_amax(const void* x, bool f32, int64_t rows, int64_t cols, int64_t
                     hipStream_t stream);
 hipError_t run_cache_update(float* amax, int32_t* valid, int32_t D, int64_t step, const float* obs, hipStream_t stream);
 hipError_t run_cache_reset(int32_t* valid, hipStream_t stream);
+hipError_t run_scale_range(const uint8_t* s, int64_t n, int32_t* out, hipStream_t stream);   // out[0..1] = min, max
 hipError_t run_debug_encode(const float* x, const uint16_t* u16, int64_t n, int which, uint8_t* out,
                             hipStream_t stream);
 hipError_t run_gemm_mx(const GemmArgs& g);      // E8M0, block 32

@@ -907,6 +907,42 @@ __global__ void k_cache_update(float* amax, int32_t* valid, int32_t D, int64_t s
 
 __global__ void k_cache_reset(int32_t* valid) { *valid = 0; }
 
+// Smallest and largest scale code of an operand: out[0] = min, out[1] = max (the caller's fill
+// kernel sets them to 255 and 0 first); a workgroup reduction, then one atomic each.
+__global__ __launch_bounds__(NT) void k_scale_range(const uint8_t* __restrict__ s, int64_t n, int32_t* out) {
+  int lo = 255, hi = 0;
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) {
+    const int c = s[i];
+    lo = min(lo, c);
+    hi = max(hi, c);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, __shfl_xor(lo, o, 64));
+    hi = max(hi, __shfl_xor(hi, o, 64));
+  }
+  __shared__ int part[2][NT / 64];
+  if ((threadIdx.x & 63) == 0) {
+    part[0][threadIdx.x >> 6] = lo;
+    part[1][threadIdx.x >> 6] = hi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) {
+      lo = min(lo, part[0][i]);
+      hi = max(hi, part[1][i]);
+    }
+    atomicMin(out, lo);
+    atomicMax(out + 1, hi);
+  }
+}
+
+__global__ void k_range_init(int32_t* out) {
+  out[0] = 255;
+  out[1] = 0;
+}
+
 __global__ void k_debug_encode(const float* __restrict__ x, const uint16_t* __restrict__ u16, int64_t n, int which,
                                uint8_t* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
@@ -1164,6 +1200,15 @@ hipError_t run_amax(const void* x, bool f32, int64_t rows, int64_t cols, int64_t
 
 hipError_t run_cache_update(float* amax, int32_t* valid, int32_t D, int64_t step, const float* obs, hipStream_t stream) {
   hipLaunchKernelGGL(k_cache_update, dim3(1), dim3(1), 0, stream, amax, valid, D, step, obs);
+  return hipGetLastError();
+}
+
+hipError_t run_scale_range(const uint8_t* s, int64_t n, int32_t* out, hipStream_t stream) {
+  hipLaunchKernelGGL(k_range_init, dim3(1), dim3(1), 0, stream, out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n == 0) return e;
+  const int64_t want = (n + NT - 1) / NT, cap = 4 * (int64_t)device_cu_count();
+  hipLaunchKernelGGL(k_scale_range, dim3((unsigned)(want < cap ? want : cap)), dim3(NT), 0, stream, s, n, out);
   return hipGetLastError();
 }
 

@@ -49,7 +49,8 @@ typedef enum {
   FP4_EINVAL = 1,        /* null pointer, bad size, bad enum value */
   FP4_EUNSUPPORTED = 2,  /* valid but unsupported combination (e.g. E8M0 with block 16) */
   FP4_EALIGN = 3,        /* misaligned pointer or leading dimension */
-  FP4_EHIP = 4           /* a HIP runtime call or kernel launch failed */
+  FP4_EHIP = 4,          /* a HIP runtime call or kernel launch failed */
+  FP4_ERANGE = 5         /* fp4_gemm_check_range: operands outside the GEMM's exact range */
 } fp4_status;
 
 /* Block-scale formats [UE5M3 approach; HOPPER methodology]. */
@@ -273,8 +274,9 @@ fp4_status amax_cache_reset(const fp4_amax_cache* cache, void* stream);
  *   c = acc * float32(g_a * g_b) [* 1/hadamard_n for wgrad], rounded to nearest-even; with
  *   tile-local operands g_a = a->g[m / a->g_stripe], g_b = b->g[n / b->g_stripe].
  * Exact results require every block partial and group sum to stay inside the float32
- * normal range (always true for UE5M3/E4M3; for E8M0, combined block exponents within
- * about +-100). K = 0 writes +0 to every output (an empty sum).
+ * normal range (always true for UE5M3/E4M3; for E8M0, combined block exponents Ea + Eb in
+ * [-124, 116], which fp4_scale_range + fp4_gemm_check_range verify). K = 0 writes +0 to every
+ * output (an empty sum).
  *
  * fp4_gemm_fprop: Y = X . W^T. x: ROW-view activation (1D scales); w: weight forward view
  *                 (TILE2D q with FP4_SCALES_2D, or a ROW-view weight with 1D scales).
@@ -287,6 +289,24 @@ fp4_status fp4_gemm_fprop(const fp4_operand* x, const fp4_operand* w, float* y, 
 fp4_status fp4_gemm_dgrad(const fp4_operand* dy, const fp4_operand* wt, float* dx, int32_t canon, void* stream);
 fp4_status fp4_gemm_wgrad(const fp4_operand* dyt, const fp4_operand* xt, float* dw, int32_t hadamard_n,
                           int32_t canon, void* stream);
+
+/*
+ * fp4_scale_range - d_range[0] = smallest and d_range[1] = largest scale code of operand a
+ * (device int32[2], overwritten; 255 and 0 for an empty operand). Reads the scale codes only
+ * (1/64 of the payload bytes for MXFP4). Together with fp4_gemm_check_range it is the checked
+ * mode of the MXFP4 GEMMs.
+ *
+ * fp4_gemm_check_range - host-only check that a GEMM between operands of format fmt whose
+ * scale codes lie in range_a / range_b (host int32[2], e.g. copied from fp4_scale_range) stays
+ * exact under the GEMM model [UE5M3 approach, GEMM model; MXFP4 method]. MXFP4 block partials
+ * 2^(Ea+Eb) * sum(q_a q_b) have nonzero magnitudes in [0.25, 1152] * 2^(Ea+Eb) and group sums
+ * below 2304 * 2^(Ea+Eb); every one stays a normal float32 (the kernels' exactness condition)
+ * iff -124 <= Ea + Eb <= 116 for every block pair, i.e. min_a + min_b >= 130 and
+ * max_a + max_b <= 370 in codes. Returns FP4_OK inside, FP4_ERANGE outside (with the range
+ * in fp4_last_error). UE5M3 / E4M3 partials are always inside: FP4_OK. Launches nothing.
+ */
+fp4_status fp4_scale_range(const fp4_operand* a, int32_t* d_range, void* stream);
+fp4_status fp4_gemm_check_range(int32_t fmt, const int32_t* range_a, const int32_t* range_b);
 
 /*
  * fp4_debug_encode - runs the device encoders on n float32 inputs, for parity tests only.

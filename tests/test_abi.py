@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_and_binding_agree():
     decl = declared_functions()
     assert set(decl) == set(_lib.EXPORTED), decl
-    assert len(decl) == 16
+    assert len(decl) == 18
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -222,3 +222,44 @@ def test_quantize_local_and_stripe_operands_reject_bad_arguments(lib):
     assert lib.fp4_gemm_fprop(ctypes.byref(a), ctypes.byref(op(fmt=2, block=32)), y, 0, None) == _lib.FP4_EUNSUPPORTED
     a = _lib.Operand(4096, 4096, None, 1, 16, 0, 32, 64, 128)       # stripe g without the array
     assert lib.fp4_gemm_fprop(ctypes.byref(a), ctypes.byref(op(fmt=1)), y, 0, None) == _lib.FP4_EINVAL
+
+
+def test_gemm_check_range_bounds(lib):
+    """Host-only range check of the MXFP4 GEMM (no launch): combined exponents Ea + Eb in
+    [-124, 116] pass, one step outside either edge is FP4_ERANGE; UE5M3/E4M3 always pass."""
+    R = lambda lo, hi: (ctypes.c_int32 * 2)(lo, hi)
+    E8, UE = _lib.FP4_E8M0, _lib.FP4_UE5M3
+    assert lib.fp4_gemm_check_range(E8, R(120, 140), R(110, 130)) == _lib.FP4_OK
+    assert lib.fp4_gemm_check_range(E8, R(65, 185), R(65, 185)) == _lib.FP4_OK        # -124 .. +116 exactly
+    assert lib.fp4_gemm_check_range(E8, R(64, 185), R(65, 185)) == _lib.FP4_ERANGE    # -125
+    assert "-125" in lib.fp4_last_error().decode()
+    assert lib.fp4_gemm_check_range(E8, R(65, 186), R(65, 185)) == _lib.FP4_ERANGE    # +117
+    assert lib.fp4_gemm_check_range(E8, R(0, 254), R(127, 127)) == _lib.FP4_ERANGE
+    assert lib.fp4_gemm_check_range(E8, R(255, 0), R(0, 254)) == _lib.FP4_OK          # an empty operand
+    assert lib.fp4_gemm_check_range(UE, R(0, 247), R(0, 247)) == _lib.FP4_OK
+    assert lib.fp4_gemm_check_range(E8, R(10, 5), R(0, 1)) == _lib.FP4_EINVAL
+    assert lib.fp4_gemm_check_range(E8, None, R(0, 1)) == _lib.FP4_EINVAL
+    assert lib.fp4_scale_range(None, ctypes.c_void_p(16), None) == _lib.FP4_EINVAL
+
+
+def test_exact_range_edges_match_the_oracle_contract():
+    """The check's edges against the oracle model: at combined exponents -124 and +116 the
+    smallest and largest block partials and group sums are normal float32 numbers and the
+    oracle's result for worst-case operands is finite and exact; at +117 the largest group sum
+    (two block partials of 1152 * 2^117) overflows float32; at -125 the smallest partial is
+    subnormal."""
+    import numpy as np
+    import oracle
+    q6 = np.full((1, 64), 6.0)
+    qh = np.full((1, 64), 0.5)
+    for e, ok in ((116, True), (117, False)):
+        sa = np.full((1, 2), 2.0 ** (e // 2))
+        sb = np.full((1, 2), 2.0 ** (e - e // 2))
+        if ok:
+            y = oracle.gemm_model(q6, sa, q6, sb, 32)
+            assert np.isfinite(y).all() and y[0, 0] == np.float32(2304 * 2.0 ** e)
+        else:
+            with np.errstate(over="ignore"):
+                assert not np.isfinite(oracle.gemm_model(q6, sa, q6, sb, 32)).any()
+    tiny = lambda e: 0.25 * 2.0 ** e
+    assert tiny(-124) == 2.0 ** -126 and tiny(-125) < 2.0 ** -126

@@ -238,3 +238,35 @@ def test_up_projection_full_size_sampled(fmt, block):
         rw = oracle.quantize_1d(W.values, fmt, block)
         want = _oracle_y(rx, rw)
     assert_f32_bits_equal(y_rows, want, f"up-projection fmt {fmt}")
+
+
+def test_mxfp4_exact_range_edges_checked_mode():
+    """MXFP4 operands whose block exponents reach both edges of the exact range (codes 65 and
+    185 on both sides: combined exponents -124 and +116, the smallest nonzero partials 2^-126
+    and group sums up to 2304 * 2^116) with wide in-group gaps: fp4_scale_range reports the
+    code range, the checked mode accepts it and the GEMM is bit-exact against the oracle
+    (including round-toward-zero accumulations that saturate at the largest float32). One
+    code past the edge makes the checked mode raise FP4_ERANGE before anything runs."""
+    rng = np.random.default_rng(81)
+    M, N, K = 96, 64, 512
+    pick = np.array([65, 185, 127, 100, 150], dtype=np.uint8)
+
+    def operand(rows):
+        codes = rng.integers(0, 16, (rows, K)).astype(np.uint8)
+        sc = pick[rng.integers(0, len(pick), (rows, K // 32))]
+        sc[0, 0], sc[1, 1] = 65, 185
+        codes[2, :], sc[2, :] = 7, 185        # all +6 at the top exponent: output (2, 2) saturates
+        return oracle.QuantResult(codes, sc, np.float32(1.0), OF.E8M0, 32)
+
+    qa, qb = operand(M), operand(N)
+    A, B = qtensor_from_oracle(qa), qtensor_from_oracle(qb)
+    assert fp4.scale_range(A).cpu().tolist() == [65, 185]
+    y = fp4.gemm_fprop(A, B, checked=True)
+    torch.cuda.synchronize()
+    with np.errstate(over="ignore"):
+        want = _oracle_y(qa, qb)
+    assert_f32_bits_equal(y, want, "MXFP4 at the exact-range edges")
+    assert np.any(np.abs(want) == np.finfo(np.float32).max)      # some sums saturate under round-toward-zero
+    qb.scales[5, 3] = 186
+    with pytest.raises(fp4.FP4Error, match="FP4_ERANGE"):
+        fp4.gemm_fprop(A, qtensor_from_oracle(qb), checked=True)
