@@ -22,7 +22,7 @@ ROW, COL, TILE2D = FP4_VIEW_ROW, FP4_VIEW_COL, FP4_VIEW_TILE2D
 __all__ = ["UE5M3", "E4M3", "E8M0", "ROW", "COL", "TILE2D", "QTensor", "AmaxCache", "quantize", "quantize_rowcol",
            "fake_quant", "dequantize", "FakeQuantPolicy", "mxfp4_to_fp8", "quantize_local",
            "tensor_amax",
-           "gemm_fprop", "gemm_dgrad", "gemm_wgrad", "scale_range", "check_range", "new_stats", "debug_encode",
+           "gemm_fprop", "gemm_dgrad", "gemm_wgrad", "gemm_fprop_q", "gemm_dgrad_q", "scale_range", "check_range", "new_stats", "debug_encode",
            "FP4Error", "library"]
 
 
@@ -326,6 +326,40 @@ def _gemm(name: str, a: QTensor, b: QTensor, canon: bool, hadamard_n: int | None
         st = fn(ctypes.byref(oa), ctypes.byref(ob), _ptr(out), int(hadamard_n), int(bool(canon)), _stream())
     _lib.check(st)
     return out
+
+
+def _gemm_q(name: str, a: QTensor, b: QTensor, fmt: int, block: int, amax: torch.Tensor | None, T: float,
+            stochastic: bool, seed: int, offset: int, canon: bool, want_f32: bool, amax_obs, stats):
+    lib = _lib.load()
+    _dev_check(amax, amax_obs, stats)
+    _stats_check(stats)
+    M, N = a.rows, b.rows
+    dev = a.q.device
+    y = torch.empty((M, N), dtype=torch.float32, device=dev) if want_f32 else None
+    q = torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
+    s = torch.empty((M, N // block), dtype=torch.uint8, device=dev)
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    cfg = _cfg(fmt, block, ROW, stochastic, 0, T, seed, offset)
+    oa, ob = a.operand(), b.operand()
+    _lib.check(getattr(lib, name)(ctypes.byref(oa), ctypes.byref(ob), _ptr(y), int(bool(canon)), ctypes.byref(cfg),
+                                  _ptr(amax), _ptr(q), _ptr(s), _ptr(g), _ptr(amax_obs), _ptr(stats), _stream()))
+    return QTensor(q, s, g, fmt, block, FP4_SCALES_1D, M, N), y
+
+
+def gemm_fprop_q(x: QTensor, w: QTensor, fmt: int = UE5M3, block: int = 16, amax: torch.Tensor | None = None,
+                 T: float = 448.0, stochastic: bool = False, seed: int = 0, offset: int = 0, canon: bool = False,
+                 want_f32: bool = False, amax_obs: torch.Tensor | None = None, stats: torch.Tensor | None = None):
+    """fp4_gemm_fprop_q: (Y quantized as the next fprop's ROW-view operand, float32 Y or None)."""
+    return _gemm_q("fp4_gemm_fprop_q", x, w, fmt, block, amax, T, stochastic, seed, offset, canon, want_f32,
+                   amax_obs, stats)
+
+
+def gemm_dgrad_q(dy: QTensor, wt: QTensor, fmt: int = UE5M3, block: int = 16, amax: torch.Tensor | None = None,
+                 T: float = 448.0, stochastic: bool = True, seed: int = 0, offset: int = 0, canon: bool = False,
+                 want_f32: bool = False, amax_obs: torch.Tensor | None = None, stats: torch.Tensor | None = None):
+    """fp4_gemm_dgrad_q: (dX quantized as the previous dgrad's ROW-view dY operand, float32 dX or None)."""
+    return _gemm_q("fp4_gemm_dgrad_q", dy, wt, fmt, block, amax, T, stochastic, seed, offset, canon, want_f32,
+                   amax_obs, stats)
 
 
 def scale_range(a: QTensor) -> torch.Tensor:

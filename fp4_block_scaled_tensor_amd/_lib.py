@@ -17,7 +17,8 @@ ABI_VERSION = 2
 
 EXPORTED = [
     "fp4_quantize", "fp4_quantize_rowcol", "fp4_fake_quant", "fp4_dequantize", "fp4_mxfp4_to_fp8", "fp4_quantize_local", "fp4_quantize_sizes", "fp4_tensor_amax", "amax_cache_update", "amax_cache_reset",
-    "fp4_gemm_fprop", "fp4_gemm_dgrad", "fp4_gemm_wgrad", "fp4_scale_range", "fp4_gemm_check_range",
+    "fp4_gemm_fprop", "fp4_gemm_dgrad", "fp4_gemm_wgrad", "fp4_gemm_fprop_q", "fp4_gemm_dgrad_q",
+    "fp4_scale_range", "fp4_gemm_check_range",
     "fp4_debug_encode", "fp4_last_error", "fp4_abi_version",
 ]
 
@@ -58,6 +59,10 @@ SIGNATURES = {
     "fp4_gemm_fprop": ([ctypes.POINTER(Operand), ctypes.POINTER(Operand), _P, _I32, _P], ctypes.c_int),
     "fp4_gemm_dgrad": ([ctypes.POINTER(Operand), ctypes.POINTER(Operand), _P, _I32, _P], ctypes.c_int),
     "fp4_gemm_wgrad": ([ctypes.POINTER(Operand), ctypes.POINTER(Operand), _P, _I32, _I32, _P], ctypes.c_int),
+    "fp4_gemm_fprop_q": ([ctypes.POINTER(Operand), ctypes.POINTER(Operand), _P, _I32, ctypes.POINTER(QuantCfg), _P,
+                          _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "fp4_gemm_dgrad_q": ([ctypes.POINTER(Operand), ctypes.POINTER(Operand), _P, _I32, ctypes.POINTER(QuantCfg), _P,
+                          _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "fp4_scale_range": ([ctypes.POINTER(Operand), _P, _P], ctypes.c_int),
     "fp4_gemm_check_range": ([_I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)], ctypes.c_int),
     "fp4_debug_encode": ([_P, _P, _I64, _I32, _P, _P], ctypes.c_int),

@@ -125,8 +125,36 @@ int stripe_shift(int32_t stripe) {
   return k;
 }
 
+// The output operand of a *_q GEMM: a ROW view of C [M x N] (blocks along N).
+fp4_status check_qout(const fp4_quant_cfg* cfg, const float* d_amax, uint8_t* q, uint8_t* s, float* d_g,
+                      float* d_amax_obs, uint32_t* d_stats, fp4k::QuantOut& qo) {
+  fp4_status st;
+  if ((st = check_cfg(cfg)) != FP4_OK) return st;
+  if (cfg->view != FP4_VIEW_ROW || cfg->hadamard_n != 0)
+    return fail(FP4_EUNSUPPORTED, "the quantized GEMM output is a ROW view without rotation");
+  if (!q || !s) return fail(FP4_EINVAL, "NULL q or s of the quantized output");
+  if (!aligned(q, 16)) return fail(FP4_EALIGN, "output q must be 16-byte aligned");
+  if (cfg->fmt != FP4_E8M0 && !d_amax) return fail(FP4_EINVAL, "UE5M3/E4M3 output needs the cached amax d_amax");
+  if ((d_amax && !aligned(d_amax, 4)) || (d_g && !aligned(d_g, 4)) || (d_amax_obs && !aligned(d_amax_obs, 4)) ||
+      (d_stats && !aligned(d_stats, 4)))
+    return fail(FP4_EALIGN, "amax / g / stats pointers must be 4-byte aligned");
+  qo.fmt = cfg->fmt;
+  qo.block = cfg->block;
+  qo.sr = cfg->stochastic;
+  qo.T = cfg->T;
+  qo.seed = cfg->seed;
+  qo.offset = cfg->offset;
+  qo.amax = d_amax;
+  qo.q = q;
+  qo.s = s;
+  qo.g = d_g;
+  qo.amax_obs = d_amax_obs;
+  qo.stats = d_stats;
+  return FP4_OK;
+}
+
 fp4_status gemm_common(const fp4_operand* a, const fp4_operand* b, float* c, int32_t canon, int32_t hadamard_n,
-                       void* stream, const char* what) {
+                       void* stream, const char* what, const fp4k::QuantOut* qout = nullptr) {
   fp4_status st;
   if ((st = check_operand(a, "A")) != FP4_OK) return st;
   if ((st = check_operand(b, "B")) != FP4_OK) return st;
@@ -135,8 +163,12 @@ fp4_status gemm_common(const fp4_operand* a, const fp4_operand* b, float* c, int
   if (a->fmt != b->fmt || a->block != b->block) return fail(FP4_EUNSUPPORTED, "%s: operands differ in format/block", what);
   if (canon != 0 && canon != 1) return fail(FP4_EINVAL, "canon must be 0 or 1");
   if (a->rows > 0 && b->rows > 0) {
-    if (!c) return fail(FP4_EINVAL, "%s: output is NULL", what);
-    if (!aligned(c, 16)) return fail(FP4_EALIGN, "%s: output not 16-byte aligned", what);
+    if (!c && !qout) return fail(FP4_EINVAL, "%s: output is NULL", what);
+    if (c && !aligned(c, 16)) return fail(FP4_EALIGN, "%s: output not 16-byte aligned", what);
+  }
+  if (qout) {
+    if (b->rows % qout->block) return fail(FP4_EINVAL, "%s: N must be a multiple of the output block", what);
+    if (a->k == 0) return fail(FP4_EUNSUPPORTED, "%s: K = 0 with a quantized output", what);
   }
   fp4k::GemmArgs g;
   g.a = fp4k::GemmOperand{a->q, a->s, a->g, a->scale_layout, a->rows, a->g_stripe ? stripe_shift(a->g_stripe) : 0};
@@ -149,7 +181,14 @@ fp4_status gemm_common(const fp4_operand* a, const fp4_operand* b, float* c, int
   g.c = c;
   g.canon = canon;
   g.hadamard_n = hadamard_n;
+  g.qout = qout;
   g.stream = (hipStream_t)stream;
+  if (qout) {
+    hipError_t e = hipSuccess;
+    if (qout->amax_obs) e = fp4k::run_fill(qout->amax_obs, 0.0f, 1, g.stream);
+    if (e == hipSuccess && qout->stats) e = fp4k::run_zero_stats(qout->stats, g.stream);
+    if (e != hipSuccess) return hip_status(e, what);
+  }
   if (g.M == 0 || g.N == 0) return ok();
   // K = 0: every output is an empty sum, +0 after canonicalisation and the output scale
   const hipError_t e = g.K == 0 ? fp4k::run_fill(c, 0.0f, g.M * g.N, g.stream)
@@ -481,6 +520,30 @@ fp4_status fp4_gemm_dgrad(const fp4_operand* dy, const fp4_operand* wt, float* d
   if (wt && wt->scale_layout == FP4_SCALES_2D)
     return fail(FP4_EUNSUPPORTED, "dgrad: pass the weight's transposed payload with FP4_SCALES_2D_T");
   return gemm_common(dy, wt, dx, canon, 0, stream, "fp4_gemm_dgrad");
+}
+
+fp4_status fp4_gemm_fprop_q(const fp4_operand* x, const fp4_operand* w, float* y, int32_t canon,
+                            const fp4_quant_cfg* out_cfg, const float* d_amax_out, uint8_t* q, uint8_t* s, float* d_g,
+                            float* d_amax_obs, uint32_t* d_stats, void* stream) {
+  if (x && x->scale_layout != FP4_SCALES_1D) return fail(FP4_EUNSUPPORTED, "fprop: activation needs 1D scales");
+  if (w && w->scale_layout == FP4_SCALES_2D_T)
+    return fail(FP4_EUNSUPPORTED, "fprop: the weight's transposed (dgrad) view is not the forward operand");
+  fp4k::QuantOut qo;
+  fp4_status st = check_qout(out_cfg, d_amax_out, q, s, d_g, d_amax_obs, d_stats, qo);
+  if (st != FP4_OK) return st;
+  return gemm_common(x, w, y, canon, 0, stream, "fp4_gemm_fprop_q", &qo);
+}
+
+fp4_status fp4_gemm_dgrad_q(const fp4_operand* dy, const fp4_operand* wt, float* dx, int32_t canon,
+                            const fp4_quant_cfg* out_cfg, const float* d_amax_out, uint8_t* q, uint8_t* s, float* d_g,
+                            float* d_amax_obs, uint32_t* d_stats, void* stream) {
+  if (dy && dy->scale_layout != FP4_SCALES_1D) return fail(FP4_EUNSUPPORTED, "dgrad: dY needs 1D scales");
+  if (wt && wt->scale_layout == FP4_SCALES_2D)
+    return fail(FP4_EUNSUPPORTED, "dgrad: the weight's forward view is not the dgrad operand");
+  fp4k::QuantOut qo;
+  fp4_status st = check_qout(out_cfg, d_amax_out, q, s, d_g, d_amax_obs, d_stats, qo);
+  if (st != FP4_OK) return st;
+  return gemm_common(dy, wt, dx, canon, 0, stream, "fp4_gemm_dgrad_q", &qo);
 }
 
 fp4_status fp4_gemm_wgrad(const fp4_operand* dyt, const fp4_operand* xt, float* dw, int32_t hadamard_n, int32_t canon,

@@ -19,6 +19,7 @@
 #pragma once
 #include "fp4_device.hpp"
 #include "launch.hpp"
+#include "quant_common.hpp"
 
 namespace fp4k {
 
@@ -193,6 +194,21 @@ __device__ __forceinline__ v16f add_rne_from_rtz(v16f T0, v16f T1) {
 // Output row of register r of a 32x32 MFMA tile in lane l (column = l & 31).
 __device__ __forceinline__ int tile_row(int r, int l) { return (r >> 2) * 8 + (l >> 5) * 4 + (r & 3); }
 
+// Staging of a workgroup's 128 x 128 float32 output tile for the output quantizer, in the two
+// 32 KB stage buffers of the K loop (free once the loop is done): rows 0-63 in st0, 64-127 in
+// st1; element (r, c) sits at column c ^ ((r & 7) << 4) of its row, i.e. the row's 16-float
+// blocks are permuted by the row, so that threads reading neighbouring rows' blocks spread
+// over the LDS banks.
+constexpr int QO_T = 128;
+struct QoStage {
+  float* st0;
+  float* st1;
+  int r0, c0;   // the wave's first row and column inside the workgroup tile
+};
+__device__ __forceinline__ float* qo_slot(float* st0, float* st1, int r, int c) {
+  return (r < 64 ? st0 : st1) + (r & 63) * QO_T + (c ^ ((r & 7) << 4));
+}
+
 // Epilogue: nearest-even mode, optional canonicalisation, scale by alpha, store float32.
 // (m0, n0) is the wave's first output row and column; tile (i, j) covers rows m0 + 32i and
 // columns n0 + 32j. pre (a power of two) undoes a constant factor the K loop carried; it is
@@ -200,10 +216,12 @@ __device__ __forceinline__ int tile_row(int r, int l) { return (r >> 2) * 8 + (l
 // the log2 stripe height of A's / B's tile-local g (0: one g for the operand), in which case
 // alpha = float32(g_a[row >> sa] * g_b[col >> sb]) per output. The float32 outputs are stored
 // non-temporal: they stream past the L2, which keeps the operand tiles other workgroups reuse.
-template <int TM, int TN>
+// With QOUT the values are also staged for the output quantizer (stage), and c may be null
+// (no float32 output).
+template <int TM, int TN, bool QOUT = false>
 __device__ __forceinline__ void store_tiles(float* __restrict__ c, int64_t M, int64_t N, int64_t m0, int64_t n0,
                                             v16f (&acc)[TM][TN], const float* ga, const float* gb, int canon,
-                                            int epi, float pre = 1.0f) {
+                                            int epi, float pre = 1.0f, QoStage stage = QoStage{}) {
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -212,6 +230,11 @@ __device__ __forceinline__ void store_tiles(float* __restrict__ c, int64_t M, in
   const int hadamard_n = epi & 0xFF, sa = (epi >> 8) & 0xFF, sb = (epi >> 16) & 0xFF;
   const float hinv = hadamard_n ? 1.0f / (float)hadamard_n : 1.0f;
   const int l = threadIdx.x & 63;
+  const bool store = !QOUT || c != nullptr;
+  auto stage_value = [&](int rt, int ct, int r, float v) {
+    if constexpr (QOUT)
+      *qo_slot(stage.st0, stage.st1, stage.r0 + rt * 32 + tile_row(r, l), stage.c0 + ct * 32 + (l & 31)) = v;
+  };
   if (sa == 0 && sb == 0) {
     float a = ga ? *ga : 1.0f;
     float b = gb ? *gb : 1.0f;
@@ -226,7 +249,7 @@ __device__ __forceinline__ void store_tiles(float* __restrict__ c, int64_t M, in
     if (m0 + TM * 32 <= M && n0 + TN * 32 <= N) {
       // the wave's outputs all lie inside C: one per-lane base, and every register's row
       // offset is a compile-time multiple of N (a scalar product)
-      float* base = c + (m0 + (l >> 5) * 4) * N + n0 + (l & 31);
+      float* base = store ? c + (m0 + (l >> 5) * 4) * N + n0 + (l & 31) : nullptr;
 #pragma unroll
       for (int rt = 0; rt < TM; ++rt)
 #pragma unroll
@@ -234,7 +257,9 @@ __device__ __forceinline__ void store_tiles(float* __restrict__ c, int64_t M, in
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int64_t k = rt * 32 + (r >> 2) * 8 + (r & 3);   // tile_row(r, l) - 4 (l >> 5)
-            __builtin_nontemporal_store(value(rt, ct, r), base + k * N + ct * 32);
+            const float v = value(rt, ct, r);
+            if (store) __builtin_nontemporal_store(v, base + k * N + ct * 32);
+            stage_value(rt, ct, r, v);
           }
     } else {
 #pragma unroll
@@ -246,7 +271,8 @@ __device__ __forceinline__ void store_tiles(float* __restrict__ c, int64_t M, in
           for (int r = 0; r < 16; ++r) {
             const int64_t row = m0 + rt * 32 + tile_row(r, l);
             const float v = value(rt, ct, r);
-            if (row < M && col < N) __builtin_nontemporal_store(v, &c[row * N + col]);
+            if (store && row < M && col < N) __builtin_nontemporal_store(v, &c[row * N + col]);
+            stage_value(rt, ct, r, v);
           }
         }
     }
@@ -268,9 +294,112 @@ __device__ __forceinline__ void store_tiles(float* __restrict__ c, int64_t M, in
           float v = acc[rt][ct][r] * pre;
           if (canon) v = __builtin_rintf(v * 1024.0f) * (1.0f / 1024.0f);
           v = v * alpha;
-          if (row < M && col < N) __builtin_nontemporal_store(v, &c[row * N + col]);
+          if (store && row < M && col < N) __builtin_nontemporal_store(v, &c[row * N + col]);
+          stage_value(rt, ct, r, v);
         }
       }
+  }
+}
+
+// One block of the staged tile (row r, columns [c0, c0 + B)) quantized as the quantizer's ROW
+// view would quantize the same float32 values: payload and scale byte stored, block maximum
+// returned, health counted.
+template <int FMT, int B, bool SR>
+__device__ __forceinline__ float qo_block(const QoStage& st, int r, int c0, int64_t grow, int64_t gcol, int64_t N,
+                                          const TensorScales& ts, const QuantOut& qo, Health& h) {
+  float v[B];
+#pragma unroll
+  for (int k = 0; k < B / 16; ++k) {
+    const float4* p = reinterpret_cast<const float4*>(qo_slot(st.st0, st.st1, r, c0 + 16 * k));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 t = p[j];
+      v[16 * k + 4 * j] = t.x;
+      v[16 * k + 4 * j + 1] = t.y;
+      v[16 * k + 4 * j + 2] = t.z;
+      v[16 * k + 4 * j + 3] = t.w;
+    }
+  }
+  float amax_b = 0.0f;
+#pragma unroll
+  for (int j = 0; j < B; ++j) amax_b = mag_max(amax_b, fabsf(v[j]));
+  uint32_t code;
+  float mult;
+  block_scale<FMT>(amax_b, ts, code, mult, h);
+  uint32_t words[B / 8];
+  payload<B, SR>(v, mult, (uint64_t)(grow * N + gcol), qo.seed, qo.offset, words);
+  uint8_t* qp = qo.q + grow * (N / 2) + gcol / 2;
+  if constexpr (B == 16) *reinterpret_cast<uint2*>(qp) = make_uint2(words[0], words[1]);
+  else *reinterpret_cast<uint4*>(qp) = make_uint4(words[0], words[1], words[2], words[3]);
+  qo.s[grow * (N / B) + gcol / B] = (uint8_t)code;
+  return amax_b;
+}
+
+template <int FMT, int B>
+__device__ __forceinline__ float qo_block_sr(const QoStage& st, int r, int c0, int64_t grow, int64_t gcol, int64_t N,
+                                             const TensorScales& ts, const QuantOut& qo, Health& h) {
+  return qo.sr ? qo_block<FMT, B, true>(st, r, c0, grow, gcol, N, ts, qo, h)
+               : qo_block<FMT, B, false>(st, r, c0, grow, gcol, N, ts, qo, h);
+}
+
+// The output quantizer: all NTH threads of the workgroup, after every wave has staged its
+// values with store_tiles<..., true>. The workgroup tile starts at (m0, n0) of C [M x N]; N is
+// a multiple of the block. Writes q and s of the tile's blocks, g (workgroup 0), and folds the
+// block maxima into amax_obs and the health counts into stats (one atomic each per workgroup).
+template <int NTH>
+__device__ __forceinline__ void quantize_out_tile(const QoStage& st, int64_t m0, int64_t n0, int64_t M, int64_t N,
+                                                  const QuantOut& qo) {
+  __syncthreads();
+  TensorScales ts{1.0f, 1.0f, 1.0f};
+  if (qo.fmt != FMT_E8M0) ts = tensor_scales(qo.amax, qo.T);
+  if (qo.g && blockIdx.x == 0 && threadIdx.x == 0) *qo.g = qo.fmt == FMT_E8M0 ? 1.0f : ts.g;
+  float obs = 0.0f;
+  Health h;
+  const int bpr = QO_T / qo.block;
+  for (int id = threadIdx.x; id < QO_T * bpr; id += NTH) {
+    const int r = id / bpr, c0 = (id - r * bpr) * qo.block;
+    const int64_t grow = m0 + r, gcol = n0 + c0;
+    if (grow >= M || gcol >= N) continue;
+    float a;
+    if (qo.fmt == FMT_E8M0) a = qo_block_sr<FMT_E8M0, 32>(st, r, c0, grow, gcol, N, ts, qo, h);
+    else if (qo.fmt == FMT_UE5M3)
+      a = qo.block == 16 ? qo_block_sr<FMT_UE5M3, 16>(st, r, c0, grow, gcol, N, ts, qo, h)
+                         : qo_block_sr<FMT_UE5M3, 32>(st, r, c0, grow, gcol, N, ts, qo, h);
+    else
+      a = qo.block == 16 ? qo_block_sr<FMT_E4M3, 16>(st, r, c0, grow, gcol, N, ts, qo, h)
+                         : qo_block_sr<FMT_E4M3, 32>(st, r, c0, grow, gcol, N, ts, qo, h);
+    obs = mag_max(obs, a);
+  }
+  if (!qo.amax_obs && !qo.stats) return;
+  uint32_t hc[3] = {h.sat, h.zero, h.nonfin};
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    obs = mag_max(obs, __shfl_xor(obs, o, 64));
+#pragma unroll
+    for (int k = 0; k < 3; ++k) hc[k] += __shfl_xor(hc[k], o, 64);
+  }
+  __shared__ float pobs[NTH / 64];
+  __shared__ uint32_t ph[3][NTH / 64];
+  if ((threadIdx.x & 63) == 0) {
+    pobs[threadIdx.x >> 6] = obs;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) ph[k][threadIdx.x >> 6] = hc[k];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = pobs[0];
+    uint32_t t[3] = {ph[0][0], ph[1][0], ph[2][0]};
+#pragma unroll
+    for (int i = 1; i < NTH / 64; ++i) {
+      m = mag_max(m, pobs[i]);
+#pragma unroll
+      for (int k = 0; k < 3; ++k) t[k] += ph[k][i];
+    }
+    if (qo.amax_obs) atomic_max_nonneg(qo.amax_obs, m);
+    if (qo.stats)
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+        if (t[k]) atomicAdd(qo.stats + k, t[k]);
   }
 }
 

@@ -153,13 +153,14 @@ using DecTiling = Tiling<2, 2, 2, 2>;   // 128x128 workgroup tile, 4 waves of 64
 
 // INTERIOR: every tile lies inside the matrix and K is a multiple of 256 (no clamped loads;
 // every stage holds four groups).
-template <int FMT, int B, bool INTERIOR>
+// QOUT: the epilogue also quantizes C as the next GEMM's ROW-view operand (qo).
+template <int FMT, int B, bool INTERIOR, bool QOUT>
 __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
                                                        int la, const uint8_t* __restrict__ qb,
                                                        const uint8_t* __restrict__ sb, int lb,
                                                        const float* __restrict__ ga, const float* __restrict__ gb,
                                                        float* __restrict__ c, int64_t M, int64_t N, int64_t K,
-                                                       int canon, int epi, int align) {
+                                                       int canon, int epi, int align, const QuantOut qo) {
   using TL = DecTiling;
   constexpr int GT = TL::BM;        // == TL::BN
   __shared__ __attribute__((aligned(4096))) uint2 lDec[256];   // decode factors of every scale code (p2 bits, M pair)
@@ -316,7 +317,15 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
       __syncthreads();
     }
   }
-  store_tiles<2, 2>(c, M, N, m0 + wm * 64, n0 + wn * 64, acc, ga, gb, canon, epi, 64.0f);   // undo 2^-3 x 2^-3
+  if constexpr (QOUT) {
+    static_assert(TL::BM == QO_T && TL::BN == QO_T, "the output quantizer stages 128 x 128 tiles");
+    __syncthreads();   // every wave is done with the last stage's buffers
+    const QoStage stg{reinterpret_cast<float*>(&lA[0][0]), reinterpret_cast<float*>(&lB[0][0]), wm * 64, wn * 64};
+    store_tiles<2, 2, true>(c, M, N, m0 + wm * 64, n0 + wn * 64, acc, ga, gb, canon, epi, 64.0f, stg);
+    quantize_out_tile<TL::NT>(stg, m0, n0, M, N, qo);
+  } else {
+    store_tiles<2, 2>(c, M, N, m0 + wm * 64, n0 + wn * 64, acc, ga, gb, canon, epi, 64.0f);   // undo 2^-3 x 2^-3
+  }
 }
 
 template <int FMT, int B>
@@ -327,10 +336,11 @@ static hipError_t launch_dec16(const GemmArgs& g) {
   const int align = (((reinterpret_cast<uintptr_t>(g.a.s) & 15) == 0 && g.K % 256 == 0) ? 1 : 0) |
                     (((reinterpret_cast<uintptr_t>(g.b.s) & 15) == 0 && g.K % 256 == 0) ? 2 : 0);
   const bool interior = g.M % TL::BM == 0 && g.N % TL::BN == 0 && g.K > 0 && g.K % KS == 0;
-  auto kern = interior ? k_gemm_dec16<FMT, B, true> : k_gemm_dec16<FMT, B, false>;
+  auto kern = g.qout ? (interior ? k_gemm_dec16<FMT, B, true, true> : k_gemm_dec16<FMT, B, false, true>)
+                     : (interior ? k_gemm_dec16<FMT, B, true, false> : k_gemm_dec16<FMT, B, false, false>);
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(TL::NT), 0, g.stream, g.a.q, g.a.s, g.a.layout, g.b.q, g.b.s,
                      g.b.layout, g.a.g, g.b.g, g.c, g.M, g.N, g.K, g.canon,
-                     epilogue_word(g.hadamard_n, g.a.g_shift, g.b.g_shift), align);
+                     epilogue_word(g.hadamard_n, g.a.g_shift, g.b.g_shift), align, g.qout ? *g.qout : QuantOut{});
   return hipGetLastError();
 }
 

@@ -252,11 +252,12 @@ struct MxSmem {
 
 // INTERIOR: every tile lies inside the matrix, K is a multiple of 256 and the scale rows are
 // 8-byte aligned, so loads need no clamping.
-template <class TL, bool INTERIOR>
+// QOUT: the epilogue also quantizes C as the next GEMM's ROW-view operand (qo).
+template <class TL, bool INTERIOR, bool QOUT>
 __global__ __launch_bounds__(TL::NT, FP4_MX_MINB) void k_gemm_mx(
     const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa, const uint8_t* __restrict__ qb,
     const uint8_t* __restrict__ sb, const float* __restrict__ ga, const float* __restrict__ gb, float* __restrict__ c,
-    int64_t M, int64_t N, int64_t K, int canon, int epi) {
+    int64_t M, int64_t N, int64_t K, int canon, int epi, const QuantOut qo) {
   constexpr int TM = TL::TM, TN = TL::TN, BM = TL::BM, BN = TL::BN, NR = BM + BN;
   static_assert(TL::NT >= NR && BM % 64 == 0 && BN % 64 == 0, "one thread per staged scale row, whole waves");
   __shared__ __attribute__((aligned(1024))) MxSmem<TL> sm;
@@ -395,7 +396,16 @@ __global__ __launch_bounds__(TL::NT, FP4_MX_MINB) void k_gemm_mx(
     }
     ++st;
   }
-  store_tiles<TM, TN>(c, M, N, m0 + wm * (TM * 32), n0 + wn * (TN * 32), acc, ga, gb, canon, epi);
+  if constexpr (QOUT) {
+    static_assert(BM == QO_T && BN == QO_T, "the output quantizer stages 128 x 128 tiles");
+    __syncthreads();   // every wave is done with the last stage's buffers
+    const QoStage stg{reinterpret_cast<float*>(&sm.a[0][0]), reinterpret_cast<float*>(&sm.b[0][0]), wm * (TM * 32),
+                      wn * (TN * 32)};
+    store_tiles<TM, TN, true>(c, M, N, m0 + wm * (TM * 32), n0 + wn * (TN * 32), acc, ga, gb, canon, epi, 1.0f, stg);
+    quantize_out_tile<TL::NT>(stg, m0, n0, M, N, qo);
+  } else {
+    store_tiles<TM, TN>(c, M, N, m0 + wm * (TM * 32), n0 + wn * (TN * 32), acc, ga, gb, canon, epi);
+  }
 }
 
 #ifndef FP4_MX_TILING
@@ -409,9 +419,11 @@ hipError_t run_gemm_mx(const GemmArgs& g) {
   const int64_t tiles = ((g.M + TL::BM - 1) / TL::BM) * ((g.N + TL::BN - 1) / TL::BN);
   const bool interior = g.M % TL::BM == 0 && g.N % TL::BN == 0 && g.K > 0 && g.K % KS == 0 &&
                         reinterpret_cast<uintptr_t>(g.a.s) % 8 == 0 && reinterpret_cast<uintptr_t>(g.b.s) % 8 == 0;
-  auto kern = interior ? k_gemm_mx<TL, true> : k_gemm_mx<TL, false>;
+  auto kern = g.qout ? (interior ? k_gemm_mx<TL, true, true> : k_gemm_mx<TL, false, true>)
+                     : (interior ? k_gemm_mx<TL, true, false> : k_gemm_mx<TL, false, false>);
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(TL::NT), 0, g.stream, g.a.q, g.a.s, g.b.q, g.b.s, g.a.g,
-                     g.b.g, g.c, g.M, g.N, g.K, g.canon, epilogue_word(g.hadamard_n, g.a.g_shift, g.b.g_shift));
+                     g.b.g, g.c, g.M, g.N, g.K, g.canon, epilogue_word(g.hadamard_n, g.a.g_shift, g.b.g_shift),
+                     g.qout ? *g.qout : QuantOut{});
   return hipGetLastError();
 }
 

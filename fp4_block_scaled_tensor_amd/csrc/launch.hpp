@@ -54,13 +54,30 @@ inline int epilogue_word(int hadamard_n, int a_shift, int b_shift) {
   return hadamard_n | (a_shift << 8) | (b_shift << 16);
 }
 
+// Quantization of a GEMM's output as the next GEMM's ROW-view operand, in the epilogue
+// ("Format-Aware Fusion for Fast FP4 Pretraining", abstract: the producer writes the
+// consumer's layout): blocks of `block` along the output's columns, tensor scales from the
+// cached amax, nearest-even or stochastic payload with the logical-index counter.
+struct QuantOut {
+  int fmt = 0, block = 16, sr = 0;
+  float T = 448.0f;
+  uint64_t seed = 0, offset = 0;
+  const float* amax = nullptr;   // cached amax of the output operand (UE5M3 / E4M3)
+  uint8_t* q = nullptr;          // [M x N/2]
+  uint8_t* s = nullptr;          // [M x N/block]
+  float* g = nullptr;            // optional: the operand's g
+  float* amax_obs = nullptr;     // optional: max |C| (zeroed by the launcher)
+  uint32_t* stats = nullptr;     // optional: health counts (zeroed by the launcher)
+};
+
 struct GemmArgs {
   GemmOperand a, b;
   int fmt, block;
   int64_t M, N, K;
-  float* c;
+  float* c;          // may be null when qout is set (no float32 output)
   int canon;
   int hadamard_n;
+  const QuantOut* qout = nullptr;
   hipStream_t stream;
 };
 
@@ -141,6 +158,7 @@ hipError_t run_amax(const void* x, bool f32, int64_t rows, int64_t cols, int64_t
                     hipStream_t stream);
 hipError_t run_cache_update(float* amax, int32_t* valid, int32_t D, int64_t step, const float* obs, hipStream_t stream);
 hipError_t run_cache_reset(int32_t* valid, hipStream_t stream);
+hipError_t run_zero_stats(uint32_t* stats, hipStream_t stream);   // FP4_STATS_WORDS zeros (a kernel)
 hipError_t run_scale_range(const uint8_t* s, int64_t n, int32_t* out, hipStream_t stream);   // out[0..1] = min, max
 hipError_t run_debug_encode(const float* x, const uint16_t* u16, int64_t n, int which, uint8_t* out,
                             hipStream_t stream);

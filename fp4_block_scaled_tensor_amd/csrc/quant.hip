@@ -1203,6 +1203,11 @@ hipError_t run_cache_update(float* amax, int32_t* valid, int32_t D, int64_t step
   return hipGetLastError();
 }
 
+hipError_t run_zero_stats(uint32_t* stats, hipStream_t stream) {
+  hipLaunchKernelGGL(k_zero_stats, dim3(1), dim3(64), 0, stream, stats);
+  return hipGetLastError();
+}
+
 hipError_t run_scale_range(const uint8_t* s, int64_t n, int32_t* out, hipStream_t stream) {
   hipLaunchKernelGGL(k_range_init, dim3(1), dim3(1), 0, stream, out);
   hipError_t e = hipGetLastError();

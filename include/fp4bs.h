@@ -291,6 +291,32 @@ fp4_status fp4_gemm_wgrad(const fp4_operand* dyt, const fp4_operand* xt, float* 
                           int32_t canon, void* stream);
 
 /*
+ * fp4_gemm_fprop_q / fp4_gemm_dgrad_q - fprop / dgrad whose epilogue also writes C as the next
+ * GEMM's quantized ROW-view operand [FUSION abstract: the producer emits the FP4 payload,
+ * scales and layout its consumer reads, instead of a float32 round trip through HBM; HOPPER
+ * methodology: FP4 copies kept in the consumer's format]. Y = X . W^T feeds the next layer's
+ * fprop; dX = dY . W feeds the previous layer's dgrad (stochastic rounding, as for dY).
+ *   x, w / dy, wt, canon  as in fp4_gemm_fprop / fp4_gemm_dgrad
+ *   y / dx    float32 [M x N] output as before, or NULL to write only the quantized operand
+ *             (0.5 + 1/B bytes per output element instead of 4)
+ *   out_cfg   recipe of the output operand: view FP4_VIEW_ROW, hadamard_n 0, any fmt / block /
+ *             T / stochastic / seed / offset of fp4_quantize
+ *   d_amax_out  device float: the output operand's cached amax (delayed scaling: known before
+ *             the GEMM runs); may be NULL for E8M0
+ *   q, s      device [M x N/2] payload and [M x N/B] scale codes, as fp4_quantize ROW writes
+ *   d_g, d_amax_obs, d_stats  optional, as in fp4_quantize: g, the observed max|C| (for the
+ *             cache's next sample) and the health counts of the output operand
+ * q, s and g are byte-identical to fp4_quantize(ROW) applied to the float32 C that y holds
+ * (the SR counter is the element's index in C [M x N]). Requires N % B == 0 and K > 0.
+ */
+fp4_status fp4_gemm_fprop_q(const fp4_operand* x, const fp4_operand* w, float* y, int32_t canon,
+                            const fp4_quant_cfg* out_cfg, const float* d_amax_out, uint8_t* q, uint8_t* s, float* d_g,
+                            float* d_amax_obs, uint32_t* d_stats, void* stream);
+fp4_status fp4_gemm_dgrad_q(const fp4_operand* dy, const fp4_operand* wt, float* dx, int32_t canon,
+                            const fp4_quant_cfg* out_cfg, const float* d_amax_out, uint8_t* q, uint8_t* s, float* d_g,
+                            float* d_amax_obs, uint32_t* d_stats, void* stream);
+
+/*
  * fp4_scale_range - d_range[0] = smallest and d_range[1] = largest scale code of operand a
  * (device int32[2], overwritten; 255 and 0 for an empty operand). Reads the scale codes only
  * (1/64 of the payload bytes for MXFP4). Together with fp4_gemm_check_range it is the checked
