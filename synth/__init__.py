@@ -17,6 +17,7 @@ import numpy as np
 __all__ = [
     "rng", "f32_to_bf16_bits", "bf16_bits_to_f32", "normal", "student_t",
     "scale_channels", "Tensor", "make_config", "CONFIG_NAMES", "LINEARS_8B",
+    "C5_TOKENS", "C5_STEPS", "C5_CHECK_STEPS", "layer_base", "step_perm", "step_amp", "drift_np", "drift_torch",
 ]
 
 
@@ -129,3 +130,47 @@ def layer_step_inputs(layer: int, step: int, tokens: int, in_f: int, out_f: int,
     X, cx = scale_channels(X, 4, 100.0, 302 + layer)
     dY = normal((tokens, out_f), 1e-3, 100000 * (layer + 1) + 10 * step + 2)
     return {"X": _as("X", X * amp, "bf16", outlier_cols=cx), "dY": _as("dY", dY * amp, "bf16")}
+
+
+# ---------------------------------------------------------------- 8B layer set at seq 8192
+# Per-step inputs of the 8B layer set at its full size. Drawing 570M fresh random numbers per
+# step is too slow for a test, so each layer's activation X and upstream gradient dY are one
+# draw each (Student-t nu=3 with 4 outlier channels x100, and N(0, 1e-3)); the tensor of step s
+# is that draw with its token rows shuffled by a seeded permutation of step s, times the
+# amplitude drift**s, rounded to bf16. The shuffle changes which tokens share a weight-gradient
+# block and every element's stochastic-rounding index from step to step; the drift moves the
+# amax between the samples of a delayed amax cache. The same tensor comes from drift_np (host)
+# and drift_torch (device): a row gather, one float32 multiply and a nearest-even bf16 cast.
+C5_TOKENS = 8192
+C5_STEPS = 100
+C5_CHECK_STEPS = (0, 1, 49, 50, 51, 99)
+_TENSOR_ID = {"X": 1, "dY": 2}
+
+
+def layer_base(layer: int, tokens: int, in_f: int, out_f: int) -> dict:
+    """The layer's fixed float32 draws: X [tokens x in_f] and dY [tokens x out_f]."""
+    X = student_t((tokens, in_f), 3.0, 700000 + 10 * layer + 1)
+    X, cx = scale_channels(X, 4, 100.0, 302 + layer)
+    dY = normal((tokens, out_f), 1e-3, 700000 + 10 * layer + 2)
+    return {"X": X, "dY": dY, "outlier_cols": cx}
+
+
+def step_perm(layer: int, tensor: str, step: int, tokens: int) -> np.ndarray:
+    """Token order of ``tensor`` ('X' or 'dY') of ``layer`` at ``step`` (int64 [tokens])."""
+    return rng(800000 + 100000 * layer + 10 * step + _TENSOR_ID[tensor]).permutation(tokens).astype(np.int64)
+
+
+def step_amp(step: int, drift: float = 1.02) -> np.float32:
+    return np.float32(drift ** step)
+
+
+def drift_np(Z: np.ndarray, perm: np.ndarray, amp) -> Tensor:
+    """bf16(Z[perm] * amp) on the host, as a bf16 Tensor."""
+    return _as("x", (Z[perm] * np.float32(amp)).astype(np.float32), "bf16")
+
+
+def drift_torch(Zd, perm_d, amp):
+    """The same tensor on the device: Zd float32 [tokens x n] and perm_d int64 device tensors."""
+    import torch
+    a = torch.tensor(float(np.float32(amp)), dtype=torch.float32, device=Zd.device)
+    return (Zd.index_select(0, perm_d) * a).to(torch.bfloat16)
