@@ -77,3 +77,60 @@ def test_stochastic_e2m1():
                         np.array([0.25, 0.75, 1.75, 3.5, 5.0, -0.0], np.float32).repeat(64)]).astype(np.float32)
     u = rng.integers(0, 1 << 16, r.size).astype(np.uint16)
     assert np.array_equal(_run(r, 4, u), sr_e2m1(r, u))
+
+
+def _oracle_code(x: np.ndarray, which: int) -> np.ndarray:
+    x = np.asarray(x, np.float32)
+    if which == 3:
+        return e8m0_block(x)[0].astype(np.int64)
+    return OF.encode_scale(x, OF.UE5M3 if which == 1 else OF.E4M3).astype(np.int64)
+
+
+def _oracle_steps(which: int):
+    """(code at +0, [(bit pattern, new code)] of every float32 where the oracle's code differs
+    from the previous float's). The candidate points are where a nearest-even encoder can
+    change its code (every codebook midpoint and its float neighbours; for E8M0 every power of
+    two and the smallest subnormal); the oracle alone decides which of them are steps."""
+    if which == 3:
+        pts = np.ldexp(np.float64(1.0), np.arange(-149, 128)).astype(np.float32)
+    else:
+        v = OF.SCALE_VALUES[OF.UE5M3 if which == 1 else OF.E4M3]
+        mids = ((v[:-1] + v[1:]) / 2).astype(np.float32)
+        pts = np.concatenate([mids, np.nextafter(mids, np.float32(np.inf)), v[1:].astype(np.float32)])
+    pts = np.unique(pts[pts > 0])
+    prev = np.nextafter(pts, np.float32(0))
+    c, cp = _oracle_code(pts, which), _oracle_code(prev, which)
+    step = c != cp
+    return int(_oracle_code(np.zeros(1, np.float32), which)[0]), \
+        sorted(zip(pts[step].view(np.uint32).astype(np.int64).tolist(), c[step].tolist()))
+
+
+@pytest.mark.parametrize("which,name", [(1, "ue5m3"), (2, "e4m3"), (3, "e8m0")])
+def test_scale_encoder_every_nonnegative_float(which, name):
+    """Every non-negative float32 that is not a NaN (all 2^31 - 2^23 + 1 bit patterns from +0 to
+    +inf, subnormals included), in increasing order through the device scale encoder: its codes
+    start at the oracle's code of +0 and change exactly at the oracle's steps, to the oracle's
+    codes, and nowhere else. A piecewise-constant function is fixed by its first value and its
+    steps, so the device encoder equals the oracle's on every one of those inputs. (A block
+    maximum of +inf is outside the E8M0 exponent's contract: that sweep ends at the largest
+    finite float.)"""
+    start, want = _oracle_steps(which)
+    last = 0x7F7FFFFF if which == 3 else 0x7F800000   # +inf is outside the E8M0 exponent's contract
+    C = 1 << 27
+    steps, prev_code, first = [], None, None
+    for c0 in range(0, last + 1, C):
+        n = min(C, last + 1 - c0)
+        bits = torch.arange(c0, c0 + n, dtype=torch.int64, device="cuda").to(torch.int32)
+        codes = fp4.debug_encode(bits.view(torch.float32), which).to(torch.int32)
+        if first is None:
+            first = int(codes[0].item())
+        elif int(codes[0].item()) != prev_code:
+            steps.append((c0, int(codes[0].item())))
+        idx = torch.nonzero(codes[1:] != codes[:-1]).flatten() + 1
+        for i, cd in zip(idx.cpu().tolist(), codes[idx].cpu().tolist()):
+            steps.append((c0 + i, cd))
+        prev_code = int(codes[-1].item())
+        del bits, codes
+    assert first == start, (name, first, start)
+    assert steps == want, (name, len(steps), len(want),
+                           next(((a, b) for a, b in zip(steps, want) if a != b), None))
