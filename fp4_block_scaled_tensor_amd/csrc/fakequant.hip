@@ -97,12 +97,12 @@ __device__ __forceinline__ void store8(rsrc_t r, uint32_t off, const float* y) {
   if constexpr (BF16) {
     const v4u w = {bf16_rne(y[0]) | (bf16_rne(y[1]) << 16), bf16_rne(y[2]) | (bf16_rne(y[3]) << 16),
                    bf16_rne(y[4]) | (bf16_rne(y[5]) << 16), bf16_rne(y[6]) | (bf16_rne(y[7]) << 16)};
-    __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, ST_NT);
   } else {
     const v4u a = {__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])};
     const v4u b = {__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]), __float_as_uint(y[7])};
-    __builtin_amdgcn_raw_buffer_store_b128(a, r, off, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(b, r, off == OOB ? OOB : off + 16u, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(a, r, off, 0, ST_NT);
+    __builtin_amdgcn_raw_buffer_store_b128(b, r, off == OOB ? OOB : off + 16u, 0, ST_NT);
   }
 }
 
@@ -295,8 +295,8 @@ __global__ __launch_bounds__(NT) void k_mx_to_fp8(const uint8_t* __restrict__ q,
     if constexpr (!TRANSPOSE) {
       const uint32_t off = ok ? (uint32_t)r * (uint32_t)K + (uint32_t)(b * 32) : OOB;
       const v4u lo = {out[0], out[1], out[2], out[3]}, hi = {out[4], out[5], out[6], out[7]};
-      __builtin_amdgcn_raw_buffer_store_b128(lo, ry, off, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b128(hi, ry, off == OOB ? OOB : off + 16u, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(lo, ry, off, 0, ST_NT);
+      __builtin_amdgcn_raw_buffer_store_b128(hi, ry, off == OOB ? OOB : off + 16u, 0, ST_NT);
     } else {
 #pragma unroll
       for (int j = 0; j < 32; ++j) tile[b * 32 + j][r] = (uint8_t)(out[j >> 2] >> (8 * (j & 3)));
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(NT) void k_mx_to_fp8(const uint8_t* __restrict__ q,
       const uint4 w = *reinterpret_cast<const uint4*>(&tile[kk][c16 * 16]);
       const v4u wv = {w.x, w.y, w.z, w.w};
       __builtin_amdgcn_raw_buffer_store_b128(
-          wv, ry, (kk < kc && c16 * 16 < rl) ? (uint32_t)kk * (uint32_t)rows + (uint32_t)(c16 * 16) : OOB, 0, 0);
+          wv, ry, (kk < kc && c16 * 16 < rl) ? (uint32_t)kk * (uint32_t)rows + (uint32_t)(c16 * 16) : OOB, 0, ST_NT);
     }
   }
 }
