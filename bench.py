@@ -17,9 +17,15 @@ WRITE_SIZE counters, scaled by the counters' reading for a plain device copy of 
 size; it is read from the profile summary under ``profiles/`` and is null when the GEMM
 kernel sources changed since those counters were taken. ``quantizer`` is the row-view
 activation quantizer's algorithmic GB/s against HBM peak; ``quantizer_rowcol`` the fused
-ROW+COL quantizer's; ``next_rows`` the graph-timed fake-quant, decode, MXFP4->FP8 and
-tile-local quantizer kernels on the same activation. ``cpu_baseline`` times the CPU
-oracle on a bounded slice of the same workload. ``--calib-copy-mib N`` runs one plain
+ROW+COL quantizer's; ``step_quantizers`` the stochastic ROW+COL pass of dY and the weight
+quantizer (TILE2D for UE5M3/E4M3); ``producer_fusion`` the fprop whose epilogue writes the
+next layer's FP4 operand against fprop + a separate quantize; ``routes`` the same step in
+the other scale formats (UE5M3 block 16 with 2D weights and D = 50 caches, E4M3, MXFP4),
+each GEMM's fraction of the FP4 and the fp16/bf16 MFMA peaks; ``next_rows`` the
+graph-timed fake-quant, decode, MXFP4->FP8 and tile-local quantizer kernels on the same
+activation. ``cpu_baseline`` times the CPU oracle on bounded slices of the same workload
+(all BLAS threads and one thread) and its quantizer on the full activation of every
+workload (``--cpu-full``: every operand and view). ``--calib-copy-mib N`` runs one plain
 N-MiB device copy before warm-up, the known-size reference for the byte counters.
 """
 from __future__ import annotations
@@ -46,6 +52,11 @@ GEMM_SOURCES = {"mxfp4": ["gemm_mx.hip", "gemm_common.hpp", "fp4_device.hpp"],
 GEMM_KERNEL = {"mxfp4": "k_gemm_mx", "ue5m3": "k_gemm_dec16", "e4m3": "k_gemm_dec16"}
 
 
+def log(msg):
+    """Progress on stderr (stdout carries only the JSON line)."""
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -58,6 +69,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=384, help="output rows of the oracle GEMM sample")
     p.add_argument("--calib-copy-mib", type=int, default=0, help="one plain device copy of this size first")
+    p.add_argument("--no-routes", action="store_true", help="skip the other scale formats' steps")
+    p.add_argument("--cpu-full", action="store_true",
+                   help="also time the oracle quantizer on the full tensors of every workload (minutes)")
     return p.parse_args()
 
 
@@ -253,33 +267,175 @@ def next_rows(torch, fp4, Xrot, step_obj, args):
     return out
 
 
+def time_step(torch, step_obj, warmup, steps, first_step=0):
+    """(ms per step, average ms per GEMM launch) of `steps` timed steps after `warmup` untimed."""
+    for s in range(first_step, first_step + warmup):
+        step_obj.run(s)
+    torch.cuda.synchronize()
+    step_obj.ev.clear()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s in range(first_step + warmup, first_step + warmup + steps):
+        step_obj.run(s, timed=True)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps, float(np.mean([a.elapsed_time(b) for a, b in step_obj.ev]))
+
+
+def routes(torch, fp4, Xd, Wd, dYd, args, skip):
+    """The same training step in the other scale formats: UE5M3 block 16 with 2D weights and
+    D = 50 caches (the main recipe), E4M3 block 16 with D = 1 (current scaling), MXFP4.
+    Each: ms per step, the GEMM kernel's average launch, its TFLOP/s and fractions of the FP4
+    and the fp16/bf16 MFMA peaks (the decoded route's true ceiling)."""
+    out = {}
+    flop_gemm = 2.0 * M_TOK * N_OUT * K_IN
+    for name in ("ue5m3", "e4m3", "mxfp4"):
+        if name == skip:
+            continue
+        st = LinearStep(fp4, torch, Xd, Wd, dYd, name, args.hadamard)
+        ms_step, gemm_ms = time_step(torch, st, 3, 10)
+        tf = flop_gemm / (gemm_ms * 1e-3) / 1e12
+        out[name] = {"ms_per_step": round(ms_step, 4), "step_TFLOPs": round(3 * flop_gemm / (ms_step * 1e-3) / 1e12, 1),
+                     "gemm_kernel": GEMM_KERNEL[name], "gemm_avg_ms": round(gemm_ms, 4),
+                     "gemm_TFLOPs": round(tf, 1), "frac_of_fp4_peak": round(tf / FP4_PEAK_TFLOPS, 4),
+                     "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+                     "recipe": {"ue5m3": "UE5M3 block 16, W 2D 16x16, D=50 caches, SR dY, T=2048 wgrad dY",
+                                "e4m3": "E4M3 block 16 + fp32 tensor scale, W 2D, D=1 (current), SR dY",
+                                "mxfp4": "E8M0 block 32, no tensor scale, SR dY"}[name]}
+        del st
+        torch.cuda.empty_cache()
+    return out
+
+
+def step_kernels(torch, fp4, Xd, Wd, dYd, step_obj):
+    """Graph-timed quantizers of the step not covered above: the stochastic fused ROW+COL pass of
+    dY (8192 x 14336, both views SR, T = 2048 for the COL view) and the weight quantizer
+    (TILE2D for UE5M3/E4M3: 14336 x 4096 -> forward and transposed payload plus the shared
+    16x16 grid; the fused ROW+COL pass for MXFP4)."""
+    fmt, B = step_obj.fmt, step_obj.block
+    E8 = fmt == fp4.E8M0
+    out = {}
+    dyrot = [dYd] + [dYd.clone() for _ in range(2)]          # 3 x 235 MB: past the last-level cache
+    ady = None if E8 else step_obj.c_dy.amax
+    fn = lambda i: fp4.quantize_rowcol(dyrot[i % 3], fmt, B, amax_row=ady, amax_col=ady, T_row=448, T_col=2048,
+                                       stochastic_row=True, stochastic_col=True, seed_row=42, offset_row=8,
+                                       seed_col=42, offset_col=9)
+    ref = fn(0)
+    torch.cuda.synchronize()
+    ms, ok = graph_time_ms(torch, fn, lambda o: all(torch.equal(a.q, b.q) and torch.equal(a.s, b.s)
+                                                   for a, b in zip(o, ref)))
+    n = M_TOK * N_OUT
+    bpe = 2 + 2 * (0.5 + 1.0 / B)
+    gbs = n * bpe / (ms * 1e-3) / 1e9
+    out["sr_rowcol_dY"] = {"kernel": "k_quant_rowcol (dY 8192x14336 bf16, SR both views)", "bytes_per_elem": bpe,
+                           "avg_ms": round(ms, 4), "achieved": round(gbs, 1), "unit": "GB/s",
+                           "frac": round(gbs / HBM_PEAK_GBS, 4), "replay_matches_eager": ok,
+                           "bound": "VALU (Philox-4x32-10 draws and the stochastic E2M1 decision)"}
+    del dyrot
+    wrot = [Wd] + [Wd.clone() for _ in range(3)]              # 4 x 117 MB
+    if E8:
+        fn = lambda i: fp4.quantize_rowcol(wrot[i % 4], fmt, B)
+        kern, wbpe = "k_quant_rowcol (W 14336x4096, ROW + COL)", 2 + 2 * (0.5 + 1.0 / 32)
+    else:
+        aw = step_obj.c_w.amax
+        fn = lambda i: fp4.quantize(wrot[i % 4], fmt, 16, fp4.TILE2D, amax=aw, T=448)
+        kern, wbpe = "k_quant_2d (W 14336x4096, TILE2D)", 2 + 0.5 + 0.5 + 1.0 / 256
+    ref = fn(0)
+    torch.cuda.synchronize()
+    ms, ok = graph_time_ms(torch, fn, lambda o: all(torch.equal(a.q, b.q) and torch.equal(a.s, b.s)
+                                                   for a, b in zip(o, ref)))
+    n = N_OUT * K_IN
+    gbs = n * wbpe / (ms * 1e-3) / 1e9
+    out["weight"] = {"kernel": kern, "bytes_per_elem": round(wbpe, 6), "avg_ms": round(ms, 4),
+                     "achieved": round(gbs, 1), "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "replay_matches_eager": ok}
+    del wrot
+    # the COL view alone (the unfused form of the wgrad operand): X^T of the activation
+    xrot = [Xd] + [Xd.clone() for _ in range(NROT - 1)]
+    ax = None if E8 else step_obj.c_x.amax
+    fn = lambda i: fp4.quantize(xrot[i], fmt, B, fp4.COL, amax=ax, T=448)
+    ref = fn(0)
+    torch.cuda.synchronize()
+    ms, ok = graph_time_ms(torch, fn, lambda o: torch.equal(o.q, ref.q) and torch.equal(o.s, ref.s))
+    cbpe = 2 + 0.5 + 1.0 / B
+    gbs = M_TOK * K_IN * cbpe / (ms * 1e-3) / 1e9
+    out["col_view_X"] = {"kernel": "k_quant_col (X 8192x4096 -> X^T operand)", "bytes_per_elem": round(cbpe, 6),
+                         "avg_ms": round(ms, 4), "achieved": round(gbs, 1), "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "replay_matches_eager": ok}
+    return out
+
+
+def producer_fusion(torch, fp4, step_obj):
+    """The fprop whose epilogue writes Y as the next layer's FP4 operand (fp4_gemm_fprop_q, no
+    float32 Y) against the float32 fprop followed by a separate ROW quantization of Y: bytes
+    written per output element and the time of each route (events, 10 launches each)."""
+    fmt, B = step_obj.fmt, step_obj.block
+    E8 = fmt == fp4.E8M0
+    amx = None if E8 else step_obj.c_x.amax
+    qx = fp4.quantize(step_obj.X, fmt, B, fp4.ROW, amax=amx, T=448)
+    if E8:
+        qw = fp4.quantize(step_obj.W, fmt, B, fp4.ROW)
+    else:
+        qw, _ = fp4.quantize(step_obj.W, fmt, 16, fp4.TILE2D, amax=step_obj.c_w.amax, T=448)
+    a_out = torch.tensor([4.0], dtype=torch.float32, device="cuda")
+    Y = torch.empty((M_TOK, N_OUT), dtype=torch.float32, device="cuda")
+
+    def fused():
+        return fp4.gemm_fprop_q(qx, qw, fmt, B, amax=None if E8 else a_out, T=448)
+
+    def separate():
+        fp4.gemm_fprop(qx, qw, out=Y)
+        return fp4.quantize(Y, fmt, B, fp4.ROW, amax=None if E8 else a_out, T=448)
+
+    res = {}
+    for name, fn in (("fused", fused), ("separate", separate)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / 10
+    fq = fused()[0]
+    sq = separate()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(fq.q, sq.q) and torch.equal(fq.s, sq.s))
+    return {"kernel": GEMM_KERNEL[{fp4.E8M0: "mxfp4", fp4.UE5M3: "ue5m3", fp4.E4M3: "e4m3"}[fmt]] + " with the "
+                      "output quantized in its epilogue (fp4_gemm_fprop_q)",
+            "bytes_written_per_output": round(0.5 + 1.0 / B, 6), "bytes_written_per_output_f32": 4.0,
+            "separate_bytes_per_output": round(4.0 + 4.0 + 0.5 + 1.0 / B, 6),
+            "fused_ms": round(res["fused"], 4), "fprop_then_quantize_ms": round(res["separate"], 4),
+            "identical_to_separate": same}
+
+
 def bf16_device(torch, synth, x):
     bits = synth.f32_to_bf16_bits(x)
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def cpu_baseline(args, fmt_name, synth):
-    """The oracle as it stands, on the host, on a bounded slice of the same workload:
-    the group-model GEMM for args.cpu_rows output rows across all 14336 columns (W quantized
-    in full, untimed), and the row-view quantizer on 1024 rows of the activation."""
-    import oracle
-    from oracle import formats as OF
+def cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
     except Exception:
-        threads = os.cpu_count() or 1
-    fmt = {"mxfp4": OF.E8M0, "ue5m3": OF.UE5M3, "e4m3": OF.E4M3}[fmt_name]
-    block = 32 if fmt == OF.E8M0 else 16
-    rows = args.cpu_rows
-    qrows = 1024
-    Xs = synth.student_t((qrows, K_IN), 3.0, 301)
-    Xs, _ = synth.scale_channels(Xs, 4, 100.0, 302)
-    W = synth.normal((N_OUT, K_IN), 0.02, 303)
-    amax_x = float(np.max(np.abs(Xs)))
-    t0 = time.perf_counter()
-    oracle.quantize_1d(Xs, fmt, block, amax=amax_x, T=448)
-    tq = time.perf_counter() - t0
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_gemm_seconds(oracle, OF, fmt, block, Xs, W, rows, amax_x):
     qx = oracle.quantize_1d(Xs[:rows], fmt, block, amax=amax_x, T=448)
     if fmt == OF.E8M0:
         qw = oracle.quantize_1d(W, fmt, block)
@@ -290,13 +446,132 @@ def cpu_baseline(args, fmt_name, synth):
     a, sa = oracle.operand_from_quant(qx)
     t1 = time.perf_counter()
     oracle.gemm_model(a, sa, b, sb, block, alpha=oracle.output_scale(qx.g, qw.g))
-    tg = time.perf_counter() - t1
-    flops = 2.0 * rows * N_OUT * K_IN
-    qbytes = qrows * K_IN * (2 + 0.5 + 1.0 / block)
-    return {"value": round(flops / tg / 1e12, 8), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"group-model GEMM of {rows} output rows x {N_OUT} cols, K={K_IN} ({fmt_name}): {tg:.1f} s; "
-                      f"row-view quantizer on {qrows}x{K_IN} bf16-valued activations: {tq:.2f} s",
-            "quantizer_GBps": round(qbytes / tq / 1e9, 6)}
+    return time.perf_counter() - t1
+
+
+def oracle_full_tensors(oracle, OF, synth, every_view):
+    """The oracle quantizer on full tensors of each workload: the tiny 256x256 pair, the 2048^3
+    format sweep (all three formats), the up-projection, the down-projection backward and one
+    step of the 8B layer set. By default the activation (or dY) of each, ROW view; with
+    every_view every operand in each view its GEMMs read (ROW, COL with T = 2048 and SR for dY,
+    2D for UE5M3/E4M3 weights). Returns {workload: {elements, seconds, GBps}}."""
+    U, E4, E8 = OF.UE5M3, OF.E4M3, OF.E8M0
+    res = {}
+
+    def q(name, x, fmt, view="row", sr=False, T=448.0, src_bytes=2):
+        B = 32 if fmt == E8 else 16
+        A = None if fmt == E8 else float(np.max(np.abs(x)))
+        t0 = time.perf_counter()
+        if view == "2d":
+            oracle.quantize_2d(x, fmt, amax=A, T=T)
+            out_b = 2 * 0.5 + 1.0 / 256
+        else:
+            xv = np.ascontiguousarray(x.T) if view == "col" else x
+            oracle.quantize_1d(xv, fmt, B, amax=A, T=T, rounding="sr" if sr else "rne", seed=42, offset=0)
+            out_b = 0.5 + 1.0 / B
+        dt = time.perf_counter() - t0
+        log(f"oracle quantizer, {name}: {x.shape[0]}x{x.shape[1]} {view} {dt:.2f} s")
+        r = res.setdefault(name, {"elements": 0, "seconds": 0.0, "bytes": 0.0})
+        r["elements"] += x.size
+        r["seconds"] += dt
+        r["bytes"] += x.size * (src_bytes + out_b)
+
+    c1 = synth.make_config(1)
+    q("tiny 256x256 fp32 (UE5M3)", c1["X"].values, U, src_bytes=4)
+    if every_view:
+        q("tiny 256x256 fp32 (UE5M3)", c1["W"].values, U, src_bytes=4)
+    c2 = synth.make_config(2)
+    for f in (U, E4, E8):
+        q("format sweep 2048^3 bf16 (3 formats)", c2["X"].values, f)
+        if every_view:
+            q("format sweep 2048^3 bf16 (3 formats)", c2["W"].values, f)
+    del c2
+    bf16 = lambda x: synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(x))
+    key = "up-projection 8192x4096 -> 14336"
+    if every_view:
+        c3 = synth.make_config(3)
+        q(key, c3["X"].values, U)
+        q(key, c3["W"].values, U, "2d")
+        del c3
+    else:                               # the same seeded activation, without drawing W
+        X, _ = synth.scale_channels(synth.student_t((M_TOK, K_IN), 3.0, 301), 4, 100.0, 302)
+        q(key, bf16(X), U)
+        del X
+    key = "down-projection backward 8192 tok, 4096 x 21504"
+    if every_view:
+        c4 = synth.make_config(4)
+        q(key, c4["dY"].values, U, sr=True)
+        q(key, c4["dY"].values, U, "col", sr=True, T=2048.0)
+        q(key, c4["W"].values, U, "2d")
+        q(key, c4["X"].values, U, "col")
+        del c4
+    else:
+        q(key, bf16(synth.normal((M_TOK, 4096), 1e-3, 401)), U, sr=True)
+    for layer, (lname, in_f, out_f) in enumerate(synth.LINEARS_8B):
+        if not every_view and layer > 0:
+            break
+        base = synth.layer_base(layer, synth.C5_TOKENS, in_f, out_f)
+        key = "8B layer set, step 0 at 8192 tokens" + ("" if every_view else " (qkv X)")
+        toks = synth.C5_TOKENS
+        X = synth.drift_np(base["X"], synth.step_perm(layer, "X", 0, toks), synth.step_amp(0)).values
+        q(key, X, U)
+        if every_view:
+            dY = synth.drift_np(base["dY"], synth.step_perm(layer, "dY", 0, toks), synth.step_amp(0)).values
+            q(key, X, U, "col")
+            q(key, dY, U, sr=True)
+            q(key, dY, U, "col", sr=True, T=2048.0 if lname == "down" else 448.0)
+            q(key, synth.layer_weight(layer, out_f, in_f).values, U, "2d")
+            del dY
+        del base, X
+    for r in res.values():
+        r["GBps"] = round(r["bytes"] / r["seconds"] / 1e9, 6)
+        r["seconds"] = round(r["seconds"], 3)
+        del r["bytes"]
+    return res
+
+
+def cpu_baseline(args, fmt_name, synth):
+    """The oracle as it stands, on the host, on bounded slices of the same workload:
+    the group-model GEMM for args.cpu_rows output rows across all 14336 columns (W quantized
+    in full, untimed) with every BLAS thread, the same GEMM for 32 rows on one thread, and the
+    oracle quantizer on the full activation tensor of every workload."""
+    import oracle
+    from oracle import formats as OF
+    from threadpoolctl import threadpool_info, threadpool_limits
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    fmt = {"mxfp4": OF.E8M0, "ue5m3": OF.UE5M3, "e4m3": OF.E4M3}[fmt_name]
+    block = 32 if fmt == OF.E8M0 else 16
+    rows, rows1 = args.cpu_rows, 32
+    Xs = synth.student_t((max(rows, 1024), K_IN), 3.0, 301)
+    Xs, _ = synth.scale_channels(Xs, 4, 100.0, 302)
+    W = synth.normal((N_OUT, K_IN), 0.02, 303)
+    amax_x = float(np.max(np.abs(Xs)))
+    tg = oracle_gemm_seconds(oracle, OF, fmt, block, Xs, W, rows, amax_x)
+    with threadpool_limits(1):
+        tg1 = oracle_gemm_seconds(oracle, OF, fmt, block, Xs, W, rows1, amax_x)
+        t0 = time.perf_counter()
+        oracle.quantize_1d(Xs[:1024], fmt, block, amax=amax_x, T=448)
+        tq1 = time.perf_counter() - t0
+    del Xs, W
+    full = oracle_full_tensors(oracle, OF, synth, args.cpu_full)
+    flops_row = 2.0 * N_OUT * K_IN
+    qbytes1 = 1024 * K_IN * (2 + 0.5 + 1.0 / block)
+    up = full["up-projection 8192x4096 -> 14336"]
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
+    return {"value": round(rows * flops_row / tg / 1e12, 8), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"group-model GEMM of {rows} output rows x {N_OUT} cols, K={K_IN} ({fmt_name}): {tg:.1f} s "
+                      f"on {threads} BLAS threads",
+            "one_thread": {"value": round(rows1 * flops_row / tg1 / 1e12, 8), "unit": "TFLOP/s",
+                           "sample": f"the same GEMM for {rows1} rows: {tg1:.1f} s; row-view quantizer on "
+                                     f"1024x{K_IN}: {tq1:.2f} s",
+                           "quantizer_GBps": round(qbytes1 / tq1 / 1e9, 6)},
+            "quantizer_GBps": up["GBps"],
+            "quantizer_full_tensors": full,
+            "os_cpu_count": os.cpu_count(), "affinity_cpus": affinity, "cpu_model": cpu_model(),
+            "note": "the oracle quantizer is numpy elementwise code: one thread whatever the BLAS pool"}
 
 
 def main():
@@ -361,7 +636,10 @@ def main():
     rc_ms, rc_ok = graph_time_ms(torch, rcfn, same_rc)
     rc_bpe = 2 + 2 * (0.5 + 1.0 / step_obj.block)
     rc_gbs = M_TOK * K_IN * rc_bpe / (rc_ms * 1e-3) / 1e9
+    log(f"step {ms_step:.3f} ms, GEMM {gemm_ms:.4f} ms; graph-timed quantizers")
     extra = next_rows(torch, fp4, Xrot, step_obj, args)
+    log("producer fusion")
+    fusion = producer_fusion(torch, fp4, step_obj)
     # measured HBM reference on the same rotated inputs: a plain device copy of the activation
     # (2 B/elem read + 2 written)
     cp_ms, _ = graph_time_ms(torch, lambda i: Xrot[i].clone(), lambda o: True)
@@ -369,6 +647,11 @@ def main():
                "kernel": "device copy of the 8192x4096 bf16 activation (torch clone)",
                "timing": f"graph replay of 20 calls, inputs rotated over {NROT} copies"}
     del Xrot
+    torch.cuda.empty_cache()
+    log("step quantizers")
+    kernels = step_kernels(torch, fp4, Xd, Wd, dYd, step_obj)
+    log("other scale formats")
+    other = {} if args.no_routes else routes(torch, fp4, Xd, Wd, dYd, args, args.fmt)
     flop_gemm = 2.0 * M_TOK * N_OUT * K_IN
     step_flops = 3 * flop_gemm
     value = step_flops / (ms_step * 1e-3) / 1e12
@@ -408,11 +691,15 @@ def main():
                              "frac": round(rc_gbs / HBM_PEAK_GBS, 4), "bytes_per_elem": rc_bpe,
                              "avg_ms": round(rc_ms, 4), "replay_matches_eager": rc_ok,
                              "in_step_avg_ms": None if args.separate else round(quant_ms_step, 4)},
+        "step_quantizers": kernels,
+        "producer_fusion": fusion,
+        "routes": other,
         "next_rows": extra,
         "hbm_reference": hbm_ref,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:
+        log("oracle on the host")
         out["cpu_baseline"] = cpu_baseline(args, args.fmt, synth)
     print(json.dumps(out), flush=True)
 
