@@ -20,6 +20,17 @@
 //             outer one nearest-even.
 // Then acc = acc + G with round-toward-zero. Chaining the MFMA accumulator instead is not
 // used: its C + sum rounding does not match nearest-even.
+//
+// Work per group: the model's additions (4 per output: three nearest-even slice adds and the
+// toward-zero group add, 16 per MFMA) are fixed; the decode (8 vector instructions per 8
+// values) is done once per workgroup. A workgroup owns a 128 x 128 output tile, 4 waves of
+// 64 x 64. Each of its 256 threads owns one operand row (A rows 0-127, then B rows) and, one
+// group ahead of the MFMAs, loads that row's 32 payload bytes and 4 slice scales of the next
+// group from global memory into registers, decodes them (interleaved with the current
+// group's MFMAs) and writes the 64 fp16 values to a double-buffered LDS tile (128 bytes per row; 16-byte chunk c of row r at position
+// c ^ ((r >> 1) & 7): two rows share a 256-byte bank line, so sixteen consecutive rows cover
+// all 64 banks for both the row-wise writes and the fragment reads). The waves read their MFMA fragments from that tile; one barrier per
+// group hands the buffers over.
 #include "gemm_common.hpp"
 
 namespace fp4k {
@@ -67,70 +78,6 @@ __device__ __forceinline__ v8h decode8(uint32_t codes, const DecScale& d) {
   return v8h{h[0].x, h[0].y, h[1].x, h[1].y, h[2].x, h[2].y, h[3].x, h[3].y};
 }
 
-// The 16 scale codes (one per 16-wide K slice; block 32 repeats each code twice) of one
-// operand row for stage st, in the operand's scale layout. Rows past the matrix and slices
-// past K get the code of 1.0. With al (scale array 16-byte aligned, K % 256 == 0) a whole
-// stage of a 1D or forward-2D row is one 16-byte load (block 32: one 8-byte load, each code
-// doubled with v_perm); the transposed 2D layout, whose codes are strided, and a partial last
-// stage read byte by byte.
-template <int FMT, int B>
-__device__ __forceinline__ uint4 scale_row16(const uint8_t* __restrict__ s, int layout, int64_t row, int64_t rows,
-                                             int64_t K, int64_t st, bool al) {
-  const uint32_t one = ScaleFmt<FMT>::ONE;
-  if (row >= rows) {
-    const uint32_t w = one * 0x01010101u;
-    return make_uint4(w, w, w, w);
-  }
-  const int64_t k16 = K / 16;        // 16-wide slices per row
-  if (al && layout != 2 && (st + 1) * 16 <= k16) {
-    if (layout == 1 || B == 16) {
-      const int64_t base = layout == 1 ? (row >> 4) * k16 : row * k16;
-      return *reinterpret_cast<const uint4*>(s + base + st * 16);
-    }
-    const uint2 v = *reinterpret_cast<const uint2*>(s + row * (K / 32) + st * 8);
-    return make_uint4(__builtin_amdgcn_perm(v.x, v.x, 0x01010000u), __builtin_amdgcn_perm(v.x, v.x, 0x03030202u),
-                      __builtin_amdgcn_perm(v.y, v.y, 0x01010000u), __builtin_amdgcn_perm(v.y, v.y, 0x03030202u));
-  }
-  uint32_t w[4] = {0, 0, 0, 0};
-  if (layout == 2) {
-    // the transposed grid: slice i of the row's 16-row band is at i * (rows / 16) + row / 16
-    // (32-bit offsets: the grid holds k16 * rows / 16 < 2^32 codes)
-    const uint8_t* p = s + (row >> 4);
-    const uint32_t stride = (uint32_t)(rows >> 4);
-    uint32_t off = (uint32_t)(st * 16) * stride;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t b = st * 16 + i < k16 ? (uint32_t)p[off] : one;
-      w[i >> 2] |= b << (8 * (i & 3));
-      off += stride;
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t slice = st * 16 + i;
-    uint32_t b = one;
-    if (slice < k16) {
-      if (layout == 0) b = s[row * (K / B) + slice * 16 / B];
-      else b = s[(row >> 4) * k16 + slice];
-    }
-    w[i >> 2] |= b << (8 * (i & 3));
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-// One code of a transposed-2D operand's stage, for a cooperative load: thread j of the
-// operand's 128 staging threads takes slice j / 8 of the stage and 16-row band j % 8 of the
-// tile (rows r0 .. r0 + 127; rows % 16 == 0 in this layout). Bands past the matrix and
-// slices past K get the code of 1.0.
-template <int FMT>
-__device__ __forceinline__ uint32_t band_code(const uint8_t* __restrict__ s, int64_t rows, int64_t r0, int64_t K,
-                                              int64_t st, int j) {
-  const int64_t slice = st * 16 + (j >> 3), band = (r0 >> 4) + (j & 7);
-  if (slice >= K / 16 || band >= (rows >> 4)) return ScaleFmt<FMT>::ONE;
-  return s[(uint32_t)slice * (uint32_t)(rows >> 4) + (uint32_t)band];
-}
-
 // The decode-table entry of the scale code in byte `sub` of a word of codes:
 // one 8-byte LDS read. The byte offset is made opaque so that the table's base address is
 // added in the read's immediate offset rather than OR-ed into the address register, which
@@ -145,16 +92,50 @@ __device__ __forceinline__ DecScale dec_entry(const uint2* table, uint32_t word,
   return d;
 }
 
-#ifndef FP4_DEC_UNROLL
-#define FP4_DEC_UNROLL 1   // the group loop unrolled (interior stages always hold four groups)
-#endif
+// The 4 slice-scale codes of one operand row for group gi (byte i = 16-wide slice i; block 32
+// repeats each code twice), in the operand's scale layout: 1D (row * K/B + block), forward
+// 2D (16-row band * K/16 + slice) or transposed 2D (slice * rows/16 + band). With al (scale
+// array 4-byte aligned) a 1D or forward-2D group is one 4-byte load (block 32: one 2-byte
+// load, each code doubled with v_perm); the transposed layout, whose codes are strided,
+// and unaligned arrays read byte by byte. row is clamped into the matrix.
+template <int B>
+__device__ __forceinline__ uint32_t group_codes(const uint8_t* __restrict__ s, int layout, int64_t row, int64_t rows,
+                                                int64_t K, int64_t gi, bool al) {
+  const int64_t k16 = K / 16;
+  if (layout == 2) {
+    // (32-bit offsets: the grid holds k16 * rows / 16 < 2^32 codes)
+    const uint8_t* p = s + (row >> 4);
+    const uint32_t stride = (uint32_t)(rows >> 4);
+    uint32_t off = (uint32_t)(gi * 4) * stride, w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w |= (uint32_t)p[off] << (8 * i);
+      off += stride;
+    }
+    return w;
+  }
+  if (layout == 0 && B == 32) {
+    const int64_t off = row * (K / 32) + gi * 2;
+    const uint32_t v = al ? (uint32_t)*reinterpret_cast<const uint16_t*>(s + off)
+                          : ((uint32_t)s[off] | ((uint32_t)s[off + 1] << 8));
+    return __builtin_amdgcn_perm(v, v, 0x01010000u);
+  }
+  const int64_t off = (layout == 1 ? (row >> 4) * k16 : row * k16) + gi * 4;
+  if (al) return *reinterpret_cast<const uint32_t*>(s + off);
+  return (uint32_t)s[off] | ((uint32_t)s[off + 1] << 8) | ((uint32_t)s[off + 2] << 16) | ((uint32_t)s[off + 3] << 24);
+}
+
+// One operand row's next group, in flight in registers: 32 payload bytes (8 words of 8 E2M1
+// codes, K order) and the 4 slice-scale codes.
+struct GroupRegs {
+  uint4 p0, p1;
+  uint32_t codes;
+};
 
 using DecTiling = Tiling<2, 2, 2, 2>;   // 128x128 workgroup tile, 4 waves of 64x64
 
-// INTERIOR: every tile lies inside the matrix and K is a multiple of 256 (no clamped loads;
-// every stage holds four groups).
 // QOUT: the epilogue also quantizes C as the next GEMM's ROW-view operand (qo).
-template <int FMT, int B, bool INTERIOR, bool QOUT>
+template <int FMT, int B, bool QOUT>
 __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* __restrict__ qa, const uint8_t* __restrict__ sa,
                                                        int la, const uint8_t* __restrict__ qb,
                                                        const uint8_t* __restrict__ sb, int lb,
@@ -162,20 +143,62 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
                                                        float* __restrict__ c, int64_t M, int64_t N, int64_t K,
                                                        int canon, int epi, int align, const QuantOut qo) {
   using TL = DecTiling;
-  constexpr int GT = TL::BM;        // == TL::BN
+  constexpr int GT = TL::BM;                 // == TL::BN
+  constexpr int DROW = 64 * 2;               // decoded bytes per operand row and group
+  constexpr int DBUF = 2 * GT * DROW;        // one buffer: A rows then B rows (32 KB)
   __shared__ __attribute__((aligned(4096))) uint2 lDec[256];   // decode factors of every scale code (p2 bits, M pair)
-  __shared__ __attribute__((aligned(1024))) uint8_t lA[2][TL::BM * ROWB];
-  __shared__ __attribute__((aligned(1024))) uint8_t lB[2][TL::BN * ROWB];
-  __shared__ uint4 lS[2][TL::BM + TL::BN];   // 16 slice-scale codes per row: A rows then B rows
-  __shared__ uint4 lT[2][2][TL::BM / 16];     // transposed-2D operands: 16 codes per 16-row band
+  __shared__ __attribute__((aligned(1024))) uint8_t lD[2 * DBUF];
+  static_assert(TL::NT == 2 * GT, "one operand row per thread");
   static_assert(TL::NT == 256, "one decode-table entry per thread");
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
   int64_t m0, n0;
   tile_coords(M, N, TL::BM, TL::BN, m0, n0);
   const int64_t ngroups = K / 64;
-  const int64_t nstages = (K + KS - 1) / KS;
   const int half = l >> 5;
+
+  // the row this thread decodes (clamped into the matrix: rows past it feed only outputs
+  // that are not stored)
+  const bool is_a = threadIdx.x < GT;
+  const int drow = threadIdx.x;              // row of the decoded tile (A rows, then B rows)
+  const int64_t rows = is_a ? M : N;
+  const int64_t grow0 = (is_a ? m0 : n0) + (drow & (GT - 1));
+  const int64_t grow = grow0 < rows ? grow0 : rows - 1;
+  const uint8_t* const qrow = (is_a ? qa : qb) + grow * (K / 2);
+  const uint8_t* const srow = is_a ? sa : sb;
+  const int lay = is_a ? la : lb;
+  const bool al = is_a ? (align & 1) : (align & 2);
+  auto load_group = [&](int64_t gi) {
+    GroupRegs r;
+    const uint4* p = reinterpret_cast<const uint4*>(qrow + gi * 32);
+    r.p0 = p[0];
+    r.p1 = p[1];
+    r.codes = group_codes<B>(srow, lay, grow, rows, K, gi, al);
+    return r;
+  };
+  const uint32_t wbase = (uint32_t)(drow * DROW);
+  const uint32_t wkey = (uint32_t)((drow >> 1) & 7);
+  // decoded chunk c of this thread's row goes to position c ^ ((drow >> 1) & 7); one call
+  // decodes slice `sub` of a group (two words of codes)
+  auto decode_sub = [&](const GroupRegs& r, int sub, int buf) {
+    const uint32_t words[8] = {r.p0.x, r.p0.y, r.p0.z, r.p0.w, r.p1.x, r.p1.y, r.p1.z, r.p1.w};
+    const DecScale d = dec_entry(lDec, r.codes, sub);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int ch = 2 * sub + h;
+      const v8h v = decode8(words[ch], d);
+      *reinterpret_cast<v8h*>(lD + buf * DBUF + wbase + ((ch ^ wkey) << 4)) = v;
+    }
+  };
+  // fragment reads: lane l reads row r0 + (l & 31) (r0 a multiple of 32, so r & 15 = l & 15),
+  // logical chunk 2 sub + half at position (2 sub + half) ^ ((l >> 1) & 7)
+  uint32_t ra[4], rb[4];
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub) {
+    const uint32_t pos = (uint32_t)((2 * sub + half) ^ ((l >> 1) & 7)) << 4;
+    ra[sub] = (uint32_t)((wm * 64 + (l & 31)) * DROW) + pos;
+    rb[sub] = (uint32_t)((GT + wn * 64 + (l & 31)) * DROW) + pos;
+  }
 
   v16f acc[2][2];
 #pragma unroll
@@ -185,142 +208,79 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const bool srow_is_a = threadIdx.x < GT;
-  const int srow = threadIdx.x & (GT - 1);
-  const bool al_a = align & 1, al_b = align & 2;
-  // scale staging: one row's 16 codes per thread, or for a transposed-2D operand one code per
-  // thread (the operand's 128 threads cover its 8 bands x 16 slices)
-  const int lay = srow_is_a ? la : lb;
-  auto load_stage_scales = [&](int64_t st) -> uint4 {
-    if (lay == 2)
-      return make_uint4(srow_is_a ? band_code<FMT>(sa, M, m0, K, st, srow) : band_code<FMT>(sb, N, n0, K, st, srow), 0,
-                        0, 0);
-    return srow_is_a ? scale_row16<FMT, B>(sa, la, m0 + srow, M, K, st, al_a)
-                     : scale_row16<FMT, B>(sb, lb, n0 + srow, N, K, st, al_b);
-  };
-  auto store_stage_scales = [&](int buf, const uint4& v) {
-    if (lay == 2) reinterpret_cast<uint8_t*>(&lT[buf][srow_is_a ? 0 : 1][srow & 7])[srow >> 3] = (uint8_t)v.x;
-    else lS[buf][threadIdx.x] = v;
-  };
   {
     const DecScale d = dec_factors_code<FMT>(threadIdx.x);
     lDec[threadIdx.x] = make_uint2(__float_as_uint(d.p2), __builtin_bit_cast(uint32_t, d.m2));
   }
-  uint4 sreg = load_stage_scales(0);
-  StageLoader<TL::BM, TL::NW> LA;
-  StageLoader<TL::BN, TL::NW> LB;
-  LA.init(qa, M, K, m0);
-  LB.init(qb, N, K, n0);
-  if (nstages > 0) {
-    if (INTERIOR) {
-      LA.issue_interior(0, lA[0]);
-      LB.issue_interior(0, lB[0]);
-    } else {
-      LA.issue(0, lA[0]);
-      LB.issue(0, lB[0]);
-    }
+  GroupRegs nxt{};
+  if (ngroups > 0) nxt = load_group(0);
+  __syncthreads();   // decode table
+  if (ngroups > 0) {
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) decode_sub(nxt, sub, 0);
+    if (ngroups > 1) nxt = load_group(1);
   }
-  store_stage_scales(0, sreg);
-  wait_vm();
   __syncthreads();
 
-  for (int64_t st = 0; st < nstages; ++st) {
-    const int buf = (int)(st & 1);
-    if (st + 1 < nstages) {
-      if (INTERIOR) {
-        LA.issue_interior(st + 1, lA[buf ^ 1]);
-        LB.issue_interior(st + 1, lB[buf ^ 1]);
-      } else {
-        LA.issue(st + 1, lA[buf ^ 1]);
-        LB.issue(st + 1, lB[buf ^ 1]);
-      }
-      sreg = load_stage_scales(st + 1);
-    }
-    // the stage's scale codes of this lane's rows: word g holds the codes of group g's four slices
-    const uint32_t* scA[2];
-    const uint32_t* scB[2];
+  // group partial G of tile (i, j) from its four slice sums, nearest-even (the loop's mode;
+  // T is pinned after the previous switch back), then acc += G toward zero (pinned between
+  // the mode switches)
+  auto finish = [&](int i, int j, v16f (&T)[4]) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int ra = wm * 64 + t * 32 + (l & 31), rb = wn * 64 + t * 32 + (l & 31);
-      scA[t] = reinterpret_cast<const uint32_t*>(la == 2 ? &lT[buf][0][ra >> 4] : &lS[buf][ra]);
-      scB[t] = reinterpret_cast<const uint32_t*>(lb == 2 ? &lT[buf][1][rb >> 4] : &lS[buf][GT + rb]);
-    }
-    const int g_end = INTERIOR ? SGR : (int)((ngroups - st * SGR) < SGR ? (ngroups - st * SGR) : SGR);
-    uint32_t nwa[2], nwb[2];
+    for (int sub = 0; sub < 4; ++sub) pin(T[sub]);
+    v16f G;
+    if constexpr (B == 16) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      nwa[t] = scA[t][0];
-      nwb[t] = scB[t][0];
-    }
-#if FP4_DEC_UNROLL
+      for (int r = 0; r < 16; ++r) G[r] = ((T[0][r] + T[1][r]) + T[2][r]) + T[3][r];
+    } else {
 #pragma unroll
-#endif
-    for (int g = 0; g < g_end; ++g) {
-      uint32_t wa[2], wb[2];
+      for (int r = 0; r < 16; ++r) G[r] = (T[0][r] + T[1][r]) + (T[2][r] + T[3][r]);   // inner adds exact
+    }
+    pin(G);
+    mode_f32_rtz();
+    pin(G);
+    pin(acc[i][j]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][j][r] = acc[i][j][r] + G[r];
+    pin(acc[i][j]);
+    mode_f32_rne();
+    pin(acc[i][j]);
+  };
+  // one group: this group's MFMAs and additions from buffer gi & 1, with the next group's
+  // decode into the other buffer (free since the last barrier) spread over the four tiles,
+  // between each tile's MFMAs and its additions. Decoding again, in the last iteration, a
+  // group already decoded only writes the buffer that no later read uses. The group after
+  // the next is then loaded (clamped: the last iterations reload the final group).
+  for (int64_t gi = 0; gi < ngroups; ++gi) {
+    const int buf = (int)(gi & 1);
+    const GroupRegs cur = nxt;
+    const uint8_t* D = lD + buf * DBUF;
+    v8h fa[4][2], fb[4][2];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        wa[t] = nwa[t];
-        wb[t] = nwb[t];
-        nwa[t] = scA[t][(g + 1) & 3];
-        nwb[t] = scB[t][(g + 1) & 3];
-      }
-      // decoded fp16 fragments (times 2^-3) of the group's four 16-wide slices
-      v8h fa[4][2], fb[4][2];
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        const int off = g * 32 + sub * 8 + half * 4;   // payload byte inside the stage row
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int rowa = wm * 64 + t * 32 + (l & 31);
-          const int rowb = wn * 64 + t * 32 + (l & 31);
-          const uint32_t ca = *reinterpret_cast<const uint32_t*>(lA[buf] + swz(rowa, off >> 4) + (off & 15));
-          const uint32_t cb = *reinterpret_cast<const uint32_t*>(lB[buf] + swz(rowb, off >> 4) + (off & 15));
-          fa[sub][t] = decode8(ca, dec_entry(lDec, wa[t], sub));
-          fb[sub][t] = decode8(cb, dec_entry(lDec, wb[t], sub));
-        }
+        fa[sub][t] = *reinterpret_cast<const v8h*>(D + ra[sub] + t * 32 * DROW);
+        fb[sub][t] = *reinterpret_cast<const v8h*>(D + rb[sub] + t * 32 * DROW);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          // group partial of this tile, nearest-even (the loop's mode); the MFMA results
-          // are pinned after the previous switch back to nearest-even
-          v16f T[4];
+      for (int j = 0; j < 2; ++j) {
+        v16f T[4];
 #pragma unroll
-          for (int sub = 0; sub < 4; ++sub)
-            T[sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[sub][i], fb[sub][j], v16f{}, 0, 0, 0);
-#pragma unroll
-          for (int sub = 0; sub < 4; ++sub) pin(T[sub]);
-          v16f G;
-          if constexpr (B == 16) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) G[r] = ((T[0][r] + T[1][r]) + T[2][r]) + T[3][r];
-          } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) G[r] = (T[0][r] + T[1][r]) + (T[2][r] + T[3][r]);   // inner adds exact
-          }
-          // cross-group accumulation, toward zero (pinned between the mode switches)
-          pin(G);
-          mode_f32_rtz();
-          pin(G);
-          pin(acc[i][j]);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = acc[i][j][r] + G[r];
-          pin(acc[i][j]);
-          mode_f32_rne();
-          pin(acc[i][j]);
-        }
-    }
-    if (st + 1 < nstages) {
-      store_stage_scales(buf ^ 1, sreg);
-      wait_vm();
-      __syncthreads();
-    }
+        for (int sub = 0; sub < 4; ++sub)
+          T[sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[sub][i], fb[sub][j], v16f{}, 0, 0, 0);
+        decode_sub(cur, 2 * i + j, buf ^ 1);
+        finish(i, j, T);
+      }
+    nxt = load_group(gi + 2 < ngroups ? gi + 2 : ngroups - 1);
+    __syncthreads();
   }
   if constexpr (QOUT) {
     static_assert(TL::BM == QO_T && TL::BN == QO_T, "the output quantizer stages 128 x 128 tiles");
-    __syncthreads();   // every wave is done with the last stage's buffers
-    const QoStage stg{reinterpret_cast<float*>(&lA[0][0]), reinterpret_cast<float*>(&lB[0][0]), wm * 64, wn * 64};
+    static_assert(DBUF >= 64 * QO_T * 4, "two 64-row float32 halves of the output tile");
+    const QoStage stg{reinterpret_cast<float*>(lD), reinterpret_cast<float*>(lD + DBUF), wm * 64, wn * 64};
     store_tiles<2, 2, true>(c, M, N, m0 + wm * 64, n0 + wn * 64, acc, ga, gb, canon, epi, 64.0f, stg);
     quantize_out_tile<TL::NT>(stg, m0, n0, M, N, qo);
   } else {
@@ -332,12 +292,11 @@ template <int FMT, int B>
 static hipError_t launch_dec16(const GemmArgs& g) {
   using TL = DecTiling;
   const int64_t tiles = ((g.M + TL::BM - 1) / TL::BM) * ((g.N + TL::BN - 1) / TL::BN);
-  // per operand: scale array 16-byte aligned and K % 256 == 0 (whole-stage vector loads)
-  const int align = (((reinterpret_cast<uintptr_t>(g.a.s) & 15) == 0 && g.K % 256 == 0) ? 1 : 0) |
-                    (((reinterpret_cast<uintptr_t>(g.b.s) & 15) == 0 && g.K % 256 == 0) ? 2 : 0);
-  const bool interior = g.M % TL::BM == 0 && g.N % TL::BN == 0 && g.K > 0 && g.K % KS == 0;
-  auto kern = g.qout ? (interior ? k_gemm_dec16<FMT, B, true, true> : k_gemm_dec16<FMT, B, false, true>)
-                     : (interior ? k_gemm_dec16<FMT, B, true, false> : k_gemm_dec16<FMT, B, false, false>);
+  // per operand: scale array aligned for the group's one-word load (4 bytes; block 32, 2 bytes)
+  const uintptr_t am = B == 32 ? 1 : 3;
+  const int align = ((reinterpret_cast<uintptr_t>(g.a.s) & am) == 0 ? 1 : 0) |
+                    ((reinterpret_cast<uintptr_t>(g.b.s) & am) == 0 ? 2 : 0);
+  auto kern = g.qout ? k_gemm_dec16<FMT, B, true> : k_gemm_dec16<FMT, B, false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(TL::NT), 0, g.stream, g.a.q, g.a.s, g.a.layout, g.b.q, g.b.s,
                      g.b.layout, g.a.g, g.b.g, g.c, g.M, g.N, g.K, g.canon,
                      epilogue_word(g.hadamard_n, g.a.g_shift, g.b.g_shift), align, g.qout ? *g.qout : QuantOut{});

@@ -159,43 +159,19 @@ __device__ __forceinline__ int group_gap_sum(const uint32_t* sw, int nr, int ra0
 }
 
 // A full stage (4 groups) for a tile whose every group passed the gap test: one MFMA per
-// group partial, software-pipelined (the MFMA of unit u+1 is issued before the 16
-// additions of unit u; two partial buffers). All tile indices are compile-time constants.
-#ifndef FP4_MX_PIPE
-#define FP4_MX_PIPE 0
-#endif
+// group partial. All tile indices are compile-time constants.
 template <int TM, int TN>
 __device__ __forceinline__ void fast_stage(const uint8_t* la, const uint8_t* lb, uint32_t La, uint32_t Lb,
                                            const uint32_t (&sa)[TM], const uint32_t (&sb)[TN],
                                            v16f (&acc)[TM][TN]) {
-  if (FP4_MX_PIPE) {
-    v16f Gb[2];
 #pragma unroll
-    for (int g = 0; g < SGR; ++g) {
-      v8i fa[TM], fb[TN];
-      load_frags<TM, TN>(la, lb, La, Lb, g, fa, fb);
+  for (int g = 0; g < SGR; ++g) {
+    v8i fa[TM], fb[TN];
+    load_frags<TM, TN>(la, lb, La, Lb, g, fa, fb);
 #pragma unroll
-      for (int t = 0; t < TM * TN; ++t) {
-        const int u = g * TM * TN + t;
-        Gb[u & 1] = mfma_sel(g, fa[t / TN], fb[t % TN], sa[t / TN], sb[t % TN]);
-        if (u > 0) {
-          const int p = (u - 1) % (TM * TN);
-          add_tile(acc[p / TN][p % TN], Gb[(u - 1) & 1]);
-        }
-      }
-    }
-    constexpr int last = SGR * TM * TN - 1;
-    add_tile(acc[(last % (TM * TN)) / TN][(last % (TM * TN)) % TN], Gb[last & 1]);
-  } else {
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int g = 0; g < SGR; ++g) {
-      v8i fa[TM], fb[TN];
-      load_frags<TM, TN>(la, lb, La, Lb, g, fa, fb);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) add_tile(acc[i][j], mfma_sel(g, fa[i], fb[j], sa[i], sb[j]));
-    }
+      for (int j = 0; j < TN; ++j) add_tile(acc[i][j], mfma_sel(g, fa[i], fb[j], sa[i], sb[j]));
   }
 }
 
