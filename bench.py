@@ -530,11 +530,44 @@ def oracle_full_tensors(oracle, OF, synth, every_view):
     return res
 
 
+def oracle_gemm_full(oracle, OF, synth, every_format):
+    """The oracle's group-model GEMM over whole workloads small enough to run in full: the tiny
+    256x256x256 pair (UE5M3, 1D) and the 2048^3 format sweep (UE5M3; with every_format also
+    E4M3 and MXFP4). Quantization untimed. Returns {workload: {seconds, GFLOPs}}."""
+    res = {}
+
+    def one(name, X, W, fmt):
+        B = 32 if fmt == OF.E8M0 else 16
+        ax = None if fmt == OF.E8M0 else float(np.max(np.abs(X)))
+        aw = None if fmt == OF.E8M0 else float(np.max(np.abs(W)))
+        qx = oracle.quantize_1d(X, fmt, B, amax=ax, T=448)
+        qw = oracle.quantize_1d(W, fmt, B, amax=aw, T=448)
+        a, sa = oracle.operand_from_quant(qx)
+        b, sb = oracle.operand_from_quant(qw)
+        t0 = time.perf_counter()
+        oracle.gemm_model(a, sa, b, sb, B, alpha=oracle.output_scale(qx.g, qw.g))
+        dt = time.perf_counter() - t0
+        fl = 2.0 * X.shape[0] * W.shape[0] * X.shape[1]
+        res[name] = {"seconds": round(dt, 3), "GFLOPs": round(fl / dt / 1e9, 4)}
+        log(f"oracle GEMM, {name}: {dt:.2f} s")
+
+    c1 = synth.make_config(1)
+    one("tiny 256x256x256 (UE5M3)", c1["X"].values, c1["W"].values, OF.UE5M3)
+    c2 = synth.make_config(2)
+    for fmt, nm in ((OF.UE5M3, "UE5M3"), (OF.E4M3, "E4M3"), (OF.E8M0, "MXFP4")):
+        if fmt != OF.UE5M3 and not every_format:
+            continue
+        one(f"format sweep 2048^3 ({nm})", c2["X"].values, c2["W"].values, fmt)
+    return res
+
+
 def cpu_baseline(args, fmt_name, synth):
     """The oracle as it stands, on the host, on bounded slices of the same workload:
     the group-model GEMM for args.cpu_rows output rows across all 14336 columns (W quantized
-    in full, untimed) with every BLAS thread, the same GEMM for 32 rows on one thread, and the
-    oracle quantizer on the full activation tensor of every workload."""
+    in full, untimed) with every BLAS thread (and the full up-projection's time extrapolated
+    linearly in M from it), the same GEMM for 32 rows on one thread, the GEMM over the tiny and
+    format-sweep workloads in full, and the oracle quantizer on the full activation tensor of
+    every workload; the speed-up of the GPU kernels over the oracle."""
     import oracle
     from oracle import formats as OF
     from threadpoolctl import threadpool_info, threadpool_limits
@@ -554,6 +587,7 @@ def cpu_baseline(args, fmt_name, synth):
         tq1 = time.perf_counter() - t0
     del Xs, W
     full = oracle_full_tensors(oracle, OF, synth, args.cpu_full)
+    gemm_full = oracle_gemm_full(oracle, OF, synth, args.cpu_full)
     flops_row = 2.0 * N_OUT * K_IN
     qbytes1 = 1024 * K_IN * (2 + 0.5 + 1.0 / block)
     up = full["up-projection 8192x4096 -> 14336"]
@@ -569,6 +603,8 @@ def cpu_baseline(args, fmt_name, synth):
                                      f"1024x{K_IN}: {tq1:.2f} s",
                            "quantizer_GBps": round(qbytes1 / tq1 / 1e9, 6)},
             "quantizer_GBps": up["GBps"],
+            "gemm_full_workloads": gemm_full,
+            "up_projection_gemm_estimate_s": round(tg * M_TOK / rows, 1),
             "quantizer_full_tensors": full,
             "os_cpu_count": os.cpu_count(), "affinity_cpus": affinity, "cpu_model": cpu_model(),
             "note": "the oracle quantizer is numpy elementwise code: one thread whatever the BLAS pool"}
@@ -701,6 +737,9 @@ def main():
     if not args.no_cpu_baseline:
         log("oracle on the host")
         out["cpu_baseline"] = cpu_baseline(args, args.fmt, synth)
+        cb = out["cpu_baseline"]
+        cb["speedup"] = {"gemm": round(achieved / cb["value"], 1),
+                         "quantizer": round(q_gbs / cb["quantizer_GBps"], 1)}
     print(json.dumps(out), flush=True)
 
 

@@ -388,19 +388,23 @@ __global__ __launch_bounds__(TL::NT, FP4_MX_MINB) void k_gemm_mx(
 #define FP4_MX_TILING 4, 2, 1, 2
 #endif
 using MxTiling = Tiling<FP4_MX_TILING>;
+using MxTilingQ = Tiling<4, 2, 1, 2>;   // the epilogue quantizer stages 128 x 128 tiles
 
-hipError_t run_gemm_mx(const GemmArgs& g) {
-  if (g.M == 0 || g.N == 0) return hipSuccess;
-  using TL = MxTiling;
+template <class TL, bool QOUT>
+static hipError_t launch_mx(const GemmArgs& g) {
   const int64_t tiles = ((g.M + TL::BM - 1) / TL::BM) * ((g.N + TL::BN - 1) / TL::BN);
   const bool interior = g.M % TL::BM == 0 && g.N % TL::BN == 0 && g.K > 0 && g.K % KS == 0 &&
                         reinterpret_cast<uintptr_t>(g.a.s) % 8 == 0 && reinterpret_cast<uintptr_t>(g.b.s) % 8 == 0;
-  auto kern = g.qout ? (interior ? k_gemm_mx<TL, true, true> : k_gemm_mx<TL, false, true>)
-                     : (interior ? k_gemm_mx<TL, true, false> : k_gemm_mx<TL, false, false>);
+  auto kern = interior ? k_gemm_mx<TL, true, QOUT> : k_gemm_mx<TL, false, QOUT>;
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(TL::NT), 0, g.stream, g.a.q, g.a.s, g.b.q, g.b.s, g.a.g,
                      g.b.g, g.c, g.M, g.N, g.K, g.canon, epilogue_word(g.hadamard_n, g.a.g_shift, g.b.g_shift),
                      g.qout ? *g.qout : QuantOut{});
   return hipGetLastError();
+}
+
+hipError_t run_gemm_mx(const GemmArgs& g) {
+  if (g.M == 0 || g.N == 0) return hipSuccess;
+  return g.qout ? launch_mx<MxTilingQ, true>(g) : launch_mx<MxTiling, false>(g);
 }
 
 }  // namespace fp4k
