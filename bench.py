@@ -50,6 +50,7 @@ GEMM_SOURCES = {"mxfp4": ["gemm_mx.hip", "gemm_common.hpp", "fp4_device.hpp"],
                 "ue5m3": ["gemm_dec16.hip", "gemm_common.hpp", "fp4_device.hpp"],
                 "e4m3": ["gemm_dec16.hip", "gemm_common.hpp", "fp4_device.hpp"]}
 GEMM_KERNEL = {"mxfp4": "k_gemm_mx", "ue5m3": "k_gemm_dec16", "e4m3": "k_gemm_dec16"}
+GEMM_KERNEL_PRE = "k_gemm_f16"   # --predecode (UE5M3/E4M3)
 
 
 def log(msg):
@@ -70,6 +71,8 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=384, help="output rows of the oracle GEMM sample")
     p.add_argument("--calib-copy-mib", type=int, default=0, help="one plain device copy of this size first")
     p.add_argument("--no-routes", action="store_true", help="skip the other scale formats' steps")
+    p.add_argument("--predecode", action="store_true",
+                   help="UE5M3/E4M3: decode each GEMM's operands once to fp16 and run the decode-once GEMM")
     p.add_argument("--cpu-full", action="store_true",
                    help="also time the oracle quantizer on the full tensors of every workload (minutes)")
     return p.parse_args()
@@ -83,9 +86,10 @@ def gemm_source_hash(fmt_name):
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(fmt_name):
+def traffic_from_profile(fmt_name, kernel=None):
     """HBM bytes per GEMM launch recorded in profiles/, if taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"{GEMM_KERNEL[fmt_name]}_{fmt_name}_8192x4096x14336_traffic.txt")
+    kernel = kernel or GEMM_KERNEL[fmt_name]
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{fmt_name}_8192x4096x14336_traffic.txt")
     if not os.path.exists(path):
         return None
     rec = {}
@@ -105,9 +109,12 @@ def traffic_from_profile(fmt_name):
 class LinearStep:
     """Buffers and per-operand amax caches of one FP4 linear layer (fprop + dgrad + wgrad)."""
 
-    def __init__(self, fp4, torch, X, W, dY, fmt_name, hadamard, fused=True):
+    def __init__(self, fp4, torch, X, W, dY, fmt_name, hadamard, fused=True, predecode=False):
         self.fp4, self.torch = fp4, torch
         self.fused = fused
+        self.predecode = predecode and fmt_name != "mxfp4"
+        self.buf16 = {}       # persistent fp16 decode buffers of the decode-once route
+        self.evd = []         # around each pair of operand decodes
         self.X, self.W, self.dY = X, W, dY
         self.hn = hadamard
         self.fmt = {"mxfp4": fp4.E8M0, "ue5m3": fp4.UE5M3, "e4m3": fp4.E4M3}[fmt_name]
@@ -133,6 +140,30 @@ class LinearStep:
         e1.record()
         self.ev.append((e0, e1))
         return r
+
+    def _gemm(self, timed, name, a, b, out, hadamard_n=0):
+        """One GEMM of the step; with predecode, both operands are first decoded once into fp16
+        (fp4_decode_f16, timed apart) and the decode-once kernel (fp4_gemm_f16) runs."""
+        fp4, torch = self.fp4, self.torch
+        if not self.predecode:
+            if name == "wgrad":
+                return self._timed(timed, fp4.gemm_wgrad, a, b, hadamard_n=hadamard_n, out=out)
+            return self._timed(timed, getattr(fp4, "gemm_" + name), a, b, out=out)
+        bufs = []
+        for tag, op in (("a", a), ("b", b)):
+            key = (name, tag)
+            if key not in self.buf16:
+                self.buf16[key] = torch.empty((op.rows, op.k), dtype=torch.float16, device="cuda")
+            bufs.append(self.buf16[key])
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        fp4.decode_f16(a, out=bufs[0])
+        fp4.decode_f16(b, out=bufs[1])
+        if timed:
+            e1.record()
+            self.evd.append((e0, e1))
+        return self._timed(timed, fp4.gemm_f16, a, b, a16=bufs[0], b16=bufs[1], hadamard_n=hadamard_n, out=out)
 
     def _sample(self, cache, x, step, hn=0):
         if self.fmt == self.fp4.E8M0:
@@ -169,7 +200,7 @@ class LinearStep:
                 qwt = fp4.quantize(self.W, self.fmt, B, fp4.COL)
         else:
             qw, qwt = fp4.quantize(self.W, self.fmt, 16, fp4.TILE2D, amax=self.c_w.amax, T=448)
-        self._timed(timed, fp4.gemm_fprop, qx, qw, out=self.Y)
+        self._gemm(timed, "fprop", qx, qw, self.Y)
         # backward: dY for dgrad (ROW, T = 448) and wgrad (COL, T = 2048, optional Hadamard),
         # both with stochastic rounding
         self._sample(self.c_dy, self.dY, step)
@@ -184,10 +215,10 @@ class LinearStep:
                                offset=step * 8 + 0)
             qdyt = fp4.quantize(self.dY, self.fmt, B, fp4.COL, amax=self.c_dyh.amax, T=2048, stochastic=True,
                                 seed=42, offset=step * 8 + 1, hadamard_n=self.hn)
-        self._timed(timed, fp4.gemm_dgrad, qdy, qwt, out=self.dX)
+        self._gemm(timed, "dgrad", qdy, qwt, self.dX)
         if not self.fused:
             qxt = fp4.quantize(self.X, self.fmt, B, fp4.COL, amax=self.c_xh.amax, T=448, hadamard_n=self.hn)
-        self._timed(timed, fp4.gemm_wgrad, qdyt, qxt, hadamard_n=self.hn, out=self.dW)
+        self._gemm(timed, "wgrad", qdyt, qxt, self.dW, hadamard_n=self.hn)
 
 
 # Graph-timed kernels read their input from one of NROT identical copies in turn, so the
@@ -284,24 +315,31 @@ def time_step(torch, step_obj, warmup, steps, first_step=0):
 
 def routes(torch, fp4, Xd, Wd, dYd, args, skip):
     """The same training step in the other scale formats: UE5M3 block 16 with 2D weights and
-    D = 50 caches (the main recipe), E4M3 block 16 with D = 1 (current scaling), MXFP4.
-    Each: ms per step, the GEMM kernel's average launch, its TFLOP/s and fractions of the FP4
-    and the fp16/bf16 MFMA peaks (the decoded route's true ceiling)."""
+    D = 50 caches (the main recipe), E4M3 block 16 with D = 1 (current scaling), each with the
+    per-workgroup decode and with each GEMM's operands decoded once to fp16 (the decode passes
+    inside the step and timed apart), and MXFP4. Each: ms per step, the GEMM kernel's average
+    launch, its TFLOP/s and fractions of the FP4 and the fp16/bf16 MFMA peaks (the decoded
+    routes' true ceiling)."""
     out = {}
     flop_gemm = 2.0 * M_TOK * N_OUT * K_IN
-    for name in ("ue5m3", "e4m3", "mxfp4"):
-        if name == skip:
+    for route in ("ue5m3", "ue5m3_decode_once", "e4m3", "e4m3_decode_once", "mxfp4"):
+        name = route.split("_")[0]
+        pre = route.endswith("decode_once")
+        if name == skip and pre == args.predecode:     # the headline step itself
             continue
-        st = LinearStep(fp4, torch, Xd, Wd, dYd, name, args.hadamard)
+        st = LinearStep(fp4, torch, Xd, Wd, dYd, name, args.hadamard, predecode=pre)
         ms_step, gemm_ms = time_step(torch, st, 3, 10)
         tf = flop_gemm / (gemm_ms * 1e-3) / 1e12
-        out[name] = {"ms_per_step": round(ms_step, 4), "step_TFLOPs": round(3 * flop_gemm / (ms_step * 1e-3) / 1e12, 1),
-                     "gemm_kernel": GEMM_KERNEL[name], "gemm_avg_ms": round(gemm_ms, 4),
+        out[route] = {"ms_per_step": round(ms_step, 4), "step_TFLOPs": round(3 * flop_gemm / (ms_step * 1e-3) / 1e12, 1),
+                     "gemm_kernel": "k_gemm_f16" if pre else GEMM_KERNEL[name], "gemm_avg_ms": round(gemm_ms, 4),
+                     "decode_pair_avg_ms": round(float(np.mean([a.elapsed_time(b) for a, b in st.evd])), 4) if pre
+                     else None,
                      "gemm_TFLOPs": round(tf, 1), "frac_of_fp4_peak": round(tf / FP4_PEAK_TFLOPS, 4),
                      "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
                      "recipe": {"ue5m3": "UE5M3 block 16, W 2D 16x16, D=50 caches, SR dY, T=2048 wgrad dY",
                                 "e4m3": "E4M3 block 16 + fp32 tensor scale, W 2D, D=1 (current), SR dY",
-                                "mxfp4": "E8M0 block 32, no tensor scale, SR dY"}[name]}
+                                "mxfp4": "E8M0 block 32, no tensor scale, SR dY"}[name]
+                               + ("; each GEMM's operands decoded once to fp16 (inside the step)" if pre else "")}
         del st
         torch.cuda.empty_cache()
     return out
@@ -629,7 +667,8 @@ def main():
     Wd = bf16_device(torch, synth, synth.normal((N_OUT, K_IN), 0.02, 303))
     dYd = bf16_device(torch, synth, synth.normal((M_TOK, N_OUT), 1e-3, 304))
     del X
-    step_obj = LinearStep(fp4, torch, Xd, Wd, dYd, args.fmt, args.hadamard, fused=not args.separate)
+    step_obj = LinearStep(fp4, torch, Xd, Wd, dYd, args.fmt, args.hadamard, fused=not args.separate,
+                          predecode=args.predecode)
     if args.calib_copy_mib > 0:
         # known-size reference for the HBM byte counters: one plain copy of N MiB
         src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
@@ -690,6 +729,7 @@ def main():
     other = {} if args.no_routes else routes(torch, fp4, Xd, Wd, dYd, args, args.fmt)
     flop_gemm = 2.0 * M_TOK * N_OUT * K_IN
     step_flops = 3 * flop_gemm
+    gemm_kernel = GEMM_KERNEL_PRE if step_obj.predecode else GEMM_KERNEL[args.fmt]
     value = step_flops / (ms_step * 1e-3) / 1e12
     achieved = flop_gemm / (gemm_ms * 1e-3) / 1e12
     bpe = 2 + 0.5 + 1.0 / step_obj.block
@@ -712,8 +752,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP4_PEAK_TFLOPS, 4),
-                     "traffic": traffic_from_profile(args.fmt),
-                     "kernel": GEMM_KERNEL[args.fmt] + " (fprop, dgrad and wgrad launches, 2*8192*4096*14336 FLOP each)",
+                     "traffic": traffic_from_profile(args.fmt, gemm_kernel),
+                     "kernel": gemm_kernel + " (fprop, dgrad and wgrad launches, 2*8192*4096*14336 FLOP each)",
                      "avg_ms": round(gemm_ms, 4), "source_sha256_16": gemm_source_hash(args.fmt),
                      "frac_of_bf16_peak": None if args.fmt == "mxfp4" else round(achieved / BF16_PEAK_TFLOPS, 4)},
         "quantizer": {"kernel": "k_quant_row (activation 8192x4096 bf16)", "achieved": round(q_gbs, 1),

@@ -22,7 +22,7 @@ ROW, COL, TILE2D = FP4_VIEW_ROW, FP4_VIEW_COL, FP4_VIEW_TILE2D
 __all__ = ["UE5M3", "E4M3", "E8M0", "ROW", "COL", "TILE2D", "QTensor", "AmaxCache", "quantize", "quantize_rowcol",
            "fake_quant", "dequantize", "FakeQuantPolicy", "mxfp4_to_fp8", "quantize_local",
            "tensor_amax",
-           "gemm_fprop", "gemm_dgrad", "gemm_wgrad", "gemm_fprop_q", "gemm_dgrad_q", "scale_range", "check_range", "new_stats", "debug_encode",
+           "gemm_fprop", "gemm_dgrad", "gemm_wgrad", "gemm_fprop_q", "gemm_dgrad_q", "decode_f16", "gemm_f16", "scale_range", "check_range", "new_stats", "debug_encode",
            "FP4Error", "library"]
 
 
@@ -360,6 +360,37 @@ def gemm_dgrad_q(dy: QTensor, wt: QTensor, fmt: int = UE5M3, block: int = 16, am
     """fp4_gemm_dgrad_q: (dX quantized as the previous dgrad's ROW-view dY operand, float32 dX or None)."""
     return _gemm_q("fp4_gemm_dgrad_q", dy, wt, fmt, block, amax, T, stochastic, seed, offset, canon, want_f32,
                    amax_obs, stats)
+
+
+def decode_f16(a: QTensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp4_decode_f16: the UE5M3/E4M3 operand decoded to float16 [rows, K] (E2M1 x block scale
+    x 2^-3, exact; no tensor scale)."""
+    lib = _lib.load()
+    if out is None:
+        out = torch.empty((a.rows, a.k), dtype=torch.float16, device=a.q.device)
+    if out.shape != (a.rows, a.k) or out.dtype != torch.float16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float16 [rows, K] tensor")
+    op = a.operand()
+    _lib.check(lib.fp4_decode_f16(ctypes.byref(op), _ptr(out), _stream()))
+    return out
+
+
+def gemm_f16(a: QTensor, b: QTensor, a16: torch.Tensor | None = None, b16: torch.Tensor | None = None,
+             hadamard_n: int = 0, canon: bool = False, out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp4_gemm_f16: C = A . B^T from the operands' fp16 decodes (decoded here when not given),
+    bit-identical to gemm_fprop / gemm_dgrad / gemm_wgrad on the same operands."""
+    lib = _lib.load()
+    a16 = decode_f16(a) if a16 is None else a16
+    b16 = decode_f16(b) if b16 is None else b16
+    _dev_check(a16, b16)
+    if out is None:
+        out = torch.empty((a.rows, b.rows), dtype=torch.float32, device=a.q.device)
+    if out.shape != (a.rows, b.rows) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [M, N] tensor")
+    oa, ob = a.operand(), b.operand()
+    _lib.check(lib.fp4_gemm_f16(ctypes.byref(oa), _ptr(a16), ctypes.byref(ob), _ptr(b16), _ptr(out), int(hadamard_n),
+                                int(bool(canon)), _stream()))
+    return out
 
 
 def scale_range(a: QTensor) -> torch.Tensor:

@@ -13,12 +13,12 @@ FP4_UE5M3, FP4_E4M3, FP4_E8M0 = 0, 1, 2
 FP4_VIEW_ROW, FP4_VIEW_COL, FP4_VIEW_TILE2D = 0, 1, 2
 FP4_IN_BF16, FP4_IN_FP32 = 0, 1
 FP4_SCALES_1D, FP4_SCALES_2D, FP4_SCALES_2D_T = 0, 1, 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 EXPORTED = [
     "fp4_quantize", "fp4_quantize_rowcol", "fp4_fake_quant", "fp4_dequantize", "fp4_mxfp4_to_fp8", "fp4_quantize_local", "fp4_quantize_sizes", "fp4_tensor_amax", "amax_cache_update", "amax_cache_reset",
     "fp4_gemm_fprop", "fp4_gemm_dgrad", "fp4_gemm_wgrad", "fp4_gemm_fprop_q", "fp4_gemm_dgrad_q",
-    "fp4_scale_range", "fp4_gemm_check_range",
+    "fp4_scale_range", "fp4_gemm_check_range", "fp4_decode_f16", "fp4_gemm_f16",
     "fp4_debug_encode", "fp4_last_error", "fp4_abi_version",
 ]
 
@@ -65,6 +65,8 @@ SIGNATURES = {
                           _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "fp4_scale_range": ([ctypes.POINTER(Operand), _P, _P], ctypes.c_int),
     "fp4_gemm_check_range": ([_I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)], ctypes.c_int),
+    "fp4_decode_f16": ([ctypes.POINTER(Operand), _P, _P], ctypes.c_int),
+    "fp4_gemm_f16": ([ctypes.POINTER(Operand), _P, ctypes.POINTER(Operand), _P, _P, _I32, _I32, _P], ctypes.c_int),
     "fp4_debug_encode": ([_P, _P, _I64, _I32, _P, _P], ctypes.c_int),
     "fp4_last_error": ([], ctypes.c_char_p),
     "fp4_abi_version": ([], ctypes.c_int32),

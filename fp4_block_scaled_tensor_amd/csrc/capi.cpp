@@ -154,7 +154,8 @@ fp4_status check_qout(const fp4_quant_cfg* cfg, const float* d_amax, uint8_t* q,
 }
 
 fp4_status gemm_common(const fp4_operand* a, const fp4_operand* b, float* c, int32_t canon, int32_t hadamard_n,
-                       void* stream, const char* what, const fp4k::QuantOut* qout = nullptr) {
+                       void* stream, const char* what, const fp4k::QuantOut* qout = nullptr,
+                       const void* a16 = nullptr, const void* b16 = nullptr) {
   fp4_status st;
   if ((st = check_operand(a, "A")) != FP4_OK) return st;
   if ((st = check_operand(b, "B")) != FP4_OK) return st;
@@ -182,6 +183,8 @@ fp4_status gemm_common(const fp4_operand* a, const fp4_operand* b, float* c, int
   g.canon = canon;
   g.hadamard_n = hadamard_n;
   g.qout = qout;
+  g.a16 = a16;
+  g.b16 = b16;
   g.stream = (hipStream_t)stream;
   if (qout) {
     hipError_t e = hipSuccess;
@@ -552,6 +555,30 @@ fp4_status fp4_gemm_wgrad(const fp4_operand* dyt, const fp4_operand* xt, float* 
   if ((dyt && dyt->scale_layout != FP4_SCALES_1D) || (xt && xt->scale_layout != FP4_SCALES_1D))
     return fail(FP4_EUNSUPPORTED, "wgrad: both operands need 1D scales along tokens");
   return gemm_common(dyt, xt, dw, canon, hadamard_n, stream, "fp4_gemm_wgrad");
+}
+
+fp4_status fp4_decode_f16(const fp4_operand* a, void* out, void* stream) {
+  fp4_status st;
+  if ((st = check_operand(a, "operand")) != FP4_OK) return st;
+  if (a->fmt == FP4_E8M0) return fail(FP4_EUNSUPPORTED, "decode_f16: UE5M3 / E4M3 operands only (MXFP4 runs natively)");
+  if (a->rows > 0 && a->k > 0) {
+    if (!out) return fail(FP4_EINVAL, "NULL out");
+    if (!aligned(out, 16)) return fail(FP4_EALIGN, "out must be 16-byte aligned");
+  }
+  fp4k::GemmOperand o{a->q, a->s, a->g, a->scale_layout, a->rows, 0};
+  return hip_status(fp4k::run_decode_f16(o, a->fmt, a->block, a->k, out, (hipStream_t)stream), "fp4_decode_f16");
+}
+
+fp4_status fp4_gemm_f16(const fp4_operand* a, const void* a16, const fp4_operand* b, const void* b16, float* c,
+                        int32_t hadamard_n, int32_t canon, void* stream) {
+  if (hadamard_n != 0 && hadamard_n != 16 && hadamard_n != 32) return fail(FP4_EINVAL, "hadamard_n must be 0, 16, 32");
+  if ((a && a->fmt == FP4_E8M0) || (b && b->fmt == FP4_E8M0))
+    return fail(FP4_EUNSUPPORTED, "gemm_f16: UE5M3 / E4M3 operands only (MXFP4 runs natively)");
+  if (a && b && a->rows > 0 && b->rows > 0 && a->k > 0) {
+    if (!a16 || !b16) return fail(FP4_EINVAL, "gemm_f16: NULL decoded operand");
+    if (!aligned(a16, 16) || !aligned(b16, 16)) return fail(FP4_EALIGN, "gemm_f16: decoded operands must be 16-byte aligned");
+  }
+  return gemm_common(a, b, c, canon, hadamard_n, stream, "fp4_gemm_f16", nullptr, a16, b16);
 }
 
 fp4_status fp4_debug_encode(const float* x, const uint16_t* u16, int64_t n, int32_t which, uint8_t* out, void* stream) {

@@ -288,6 +288,164 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
   }
 }
 
+// ---------------------------------------------------------------- decode once per operand
+// The operand decoded once into fp16 [rows x K], K-contiguous: the same exact values
+// q S 2^-3 the per-tile decode above produces. A GEMM whose two operands come with this copy
+// reads it instead of decoding per workgroup (the per-tile decode costs more than a third
+// of that kernel's time; the copy costs 2 bytes per element written once and read by the
+// GEMM through L2). One thread per 64-element group of a row: 32 payload bytes, 4 slice
+// scales, 128 bytes out.
+template <int FMT, int B>
+__global__ __launch_bounds__(256) void k_decode_f16(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
+                                                    int layout, int64_t rows, int64_t K, bool al,
+                                                    _Float16* __restrict__ out) {
+  const int64_t ng = K / 64;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= rows * ng) return;
+  const int64_t row = id / ng, gi = id - row * ng;
+  const uint4* p = reinterpret_cast<const uint4*>(q + row * (K / 2) + gi * 32);
+  const uint4 p0 = p[0], p1 = p[1];
+  const uint32_t codes = group_codes<B>(s, layout, row, rows, K, gi, al);
+  const uint32_t words[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+  v8h* o = reinterpret_cast<v8h*>(out + row * K + gi * 64);
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub) {
+    const DecScale d = dec_factors_code<FMT>((codes >> (8 * sub)) & 0xFFu);
+    o[2 * sub] = decode8(words[2 * sub], d);
+    o[2 * sub + 1] = decode8(words[2 * sub + 1], d);
+  }
+}
+
+template <int FMT, int B>
+static hipError_t launch_decode_f16(const GemmOperand& a, int64_t K, void* out, hipStream_t stream) {
+  const int64_t n = a.rows * (K / 64);
+  const uintptr_t am = B == 32 ? 1 : 3;
+  hipLaunchKernelGGL((k_decode_f16<FMT, B>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a.q, a.s,
+                     a.layout, a.rows, K, (reinterpret_cast<uintptr_t>(a.s) & am) == 0,
+                     reinterpret_cast<_Float16*>(out));
+  return hipGetLastError();
+}
+
+hipError_t run_decode_f16(const GemmOperand& a, int fmt, int block, int64_t K, void* out, hipStream_t stream) {
+  if (a.rows == 0 || K == 0) return hipSuccess;
+  if (fmt == FMT_UE5M3)
+    return block == 16 ? launch_decode_f16<FMT_UE5M3, 16>(a, K, out, stream)
+                       : launch_decode_f16<FMT_UE5M3, 32>(a, K, out, stream);
+  return block == 16 ? launch_decode_f16<FMT_E4M3, 16>(a, K, out, stream)
+                     : launch_decode_f16<FMT_E4M3, 32>(a, K, out, stream);
+}
+
+// The GEMM over decoded fp16 operands: the group loop of k_gemm_dec16 without the decode.
+// Each group's 128 fp16 rows of A and of B (128 bytes per row, one stage) go straight from
+// global memory into a double-buffered LDS tile with global_load_lds (the same chunk swizzle:
+// chunk c of row r at c ^ ((r >> 1) & 7)); the next group's copy is in flight during the
+// current group's MFMAs and additions. Same MFMAs, additions, rounding modes and epilogue.
+template <int B, bool INTERIOR>
+__global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_f16(const uint8_t* __restrict__ a16,
+                                                     const uint8_t* __restrict__ b16,
+                                                     const float* __restrict__ ga, const float* __restrict__ gb,
+                                                     float* __restrict__ c, int64_t M, int64_t N, int64_t K,
+                                                     int canon, int epi) {
+  using TL = DecTiling;
+  constexpr int GT = TL::BM;
+  constexpr int DROW = 64 * 2;               // fp16 bytes per row and group (one stage)
+  constexpr int DBUF = 2 * GT * DROW;        // one buffer: A rows then B rows (32 KB)
+  static_assert(DROW == ROWB, "one group of fp16 is one 128-byte stage row");
+  __shared__ __attribute__((aligned(1024))) uint8_t lD[2 * DBUF];
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  int64_t m0, n0;
+  tile_coords(M, N, TL::BM, TL::BN, m0, n0);
+  const int64_t ngroups = K / 64;
+  const int half = l >> 5;
+  // the loaders see rows of 2K bytes: 4K "FP4 elements"
+  StageLoader<GT, TL::NW> LA, LB;
+  LA.init(a16, M, 4 * K, m0);
+  LB.init(b16, N, 4 * K, n0);
+  auto issue = [&](int64_t gi, int buf) {
+    if (INTERIOR) {
+      LA.issue_interior(gi, lD + buf * DBUF);
+      LB.issue_interior(gi, lD + buf * DBUF + GT * DROW);
+    } else {
+      LA.issue(gi, lD + buf * DBUF);
+      LB.issue(gi, lD + buf * DBUF + GT * DROW);
+    }
+  };
+  uint32_t ra[4], rb[4];
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub) {
+    const uint32_t pos = (uint32_t)((2 * sub + half) ^ ((l >> 1) & 7)) << 4;
+    ra[sub] = (uint32_t)((wm * 64 + (l & 31)) * DROW) + pos;
+    rb[sub] = (uint32_t)((GT + wn * 64 + (l & 31)) * DROW) + pos;
+  }
+  v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  if (ngroups > 0) issue(0, 0);
+  wait_vm();
+  __syncthreads();
+  for (int64_t gi = 0; gi < ngroups; ++gi) {
+    const int buf = (int)(gi & 1);
+    if (gi + 1 < ngroups) issue(gi + 1, buf ^ 1);
+    const uint8_t* D = lD + buf * DBUF;
+    v8h fa[4][2], fb[4][2];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        fa[sub][t] = *reinterpret_cast<const v8h*>(D + ra[sub] + t * 32 * DROW);
+        fb[sub][t] = *reinterpret_cast<const v8h*>(D + rb[sub] + t * 32 * DROW);
+      }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        v16f T[4];
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub)
+          T[sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[sub][i], fb[sub][j], v16f{}, 0, 0, 0);
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) pin(T[sub]);
+        v16f G;
+        if constexpr (B == 16) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) G[r] = ((T[0][r] + T[1][r]) + T[2][r]) + T[3][r];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) G[r] = (T[0][r] + T[1][r]) + (T[2][r] + T[3][r]);   // inner adds exact
+        }
+        pin(G);
+        mode_f32_rtz();
+        pin(G);
+        pin(acc[i][j]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = acc[i][j][r] + G[r];
+        pin(acc[i][j]);
+        mode_f32_rne();
+        pin(acc[i][j]);
+      }
+    wait_vm();
+    __syncthreads();
+  }
+  store_tiles<2, 2>(c, M, N, m0 + wm * 64, n0 + wn * 64, acc, ga, gb, canon, epi, 64.0f);   // undo 2^-3 x 2^-3
+}
+
+template <int B>
+static hipError_t launch_f16(const GemmArgs& g) {
+  using TL = DecTiling;
+  const int64_t tiles = ((g.M + TL::BM - 1) / TL::BM) * ((g.N + TL::BN - 1) / TL::BN);
+  const bool interior = g.M % TL::BM == 0 && g.N % TL::BN == 0;
+  auto kern = interior ? k_gemm_f16<B, true> : k_gemm_f16<B, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(TL::NT), 0, g.stream,
+                     reinterpret_cast<const uint8_t*>(g.a16), reinterpret_cast<const uint8_t*>(g.b16), g.a.g, g.b.g,
+                     g.c, g.M, g.N, g.K, g.canon, epilogue_word(g.hadamard_n, g.a.g_shift, g.b.g_shift));
+  return hipGetLastError();
+}
+
 template <int FMT, int B>
 static hipError_t launch_dec16(const GemmArgs& g) {
   using TL = DecTiling;
@@ -305,6 +463,7 @@ static hipError_t launch_dec16(const GemmArgs& g) {
 
 hipError_t run_gemm_dec16(const GemmArgs& g) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
+  if (g.a16 && g.b16 && !g.qout) return g.block == 16 ? launch_f16<16>(g) : launch_f16<32>(g);
   if (g.fmt == FMT_UE5M3) return g.block == 16 ? launch_dec16<FMT_UE5M3, 16>(g) : launch_dec16<FMT_UE5M3, 32>(g);
   return g.block == 16 ? launch_dec16<FMT_E4M3, 16>(g) : launch_dec16<FMT_E4M3, 32>(g);
 }

@@ -78,10 +78,14 @@ struct GemmArgs {
   int canon;
   int hadamard_n;
   const QuantOut* qout = nullptr;
+  const void* a16 = nullptr;   // UE5M3/E4M3: both operands decoded to fp16 [rows x K] (run_decode_f16)
+  const void* b16 = nullptr;
   hipStream_t stream;
 };
 
 hipError_t run_quantize(const QuantArgs& a);
+// A UE5M3/E4M3 operand [rows x K] decoded to fp16 q S 2^-3 (exact), K-contiguous.
+hipError_t run_decode_f16(const GemmOperand& a, int fmt, int block, int64_t K, void* out, hipStream_t stream);
 
 // ROW and COL views of one tensor in one pass (same format and block; per-view amax, T,
 // stochastic flag and counter offset; Hadamard on the COL view only).

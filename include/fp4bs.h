@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FP4BS_ABI_VERSION 2
+#define FP4BS_ABI_VERSION 3
 
 typedef enum {
   FP4_OK = 0,
@@ -315,6 +315,26 @@ fp4_status fp4_gemm_fprop_q(const fp4_operand* x, const fp4_operand* w, float* y
 fp4_status fp4_gemm_dgrad_q(const fp4_operand* dy, const fp4_operand* wt, float* dx, int32_t canon,
                             const fp4_quant_cfg* out_cfg, const float* d_amax_out, uint8_t* q, uint8_t* s, float* d_g,
                             float* d_amax_obs, uint32_t* d_stats, void* stream);
+
+/*
+ * fp4_decode_f16 - the operand a (UE5M3 or E4M3, any scale layout) decoded to fp16 [rows x K],
+ * K-contiguous: out[r][k] = E2M1(q[r][k]) * S(r, k) * 2^-3, exactly (S is the block scale
+ * value, without the tensor factor g; every such value has at most 6 significant bits and lies
+ * in [2^-21, 46080], so fp16, subnormals included, holds it exactly) [UE5M3 approach: the
+ * software GEMM model; UE5M3 limits: no native UE5M3 hardware, hence an exact software route].
+ *   out  device, 16-byte aligned, 2 * rows * K bytes, caller-owned.
+ * Returns FP4_EUNSUPPORTED for E8M0 operands (the MXFP4 GEMM reads FP4 natively).
+ *
+ * fp4_gemm_f16 - C = A . B^T for UE5M3/E4M3 operands a [M x K] and b [N x K] whose fp16
+ * decodes (fp4_decode_f16) are a16 and b16: the same group model, rounding and epilogue as
+ * fp4_gemm_fprop / _dgrad / _wgrad on the same operands (hadamard_n as in fp4_gemm_wgrad, 0
+ * otherwise), bit for bit, from a kernel that reads the decoded values instead of decoding
+ * each operand tile in every workgroup that uses it. a and b supply format, block, sizes and g
+ * (their q and s are not read). c as in the other GEMMs.
+ */
+fp4_status fp4_decode_f16(const fp4_operand* a, void* out, void* stream);
+fp4_status fp4_gemm_f16(const fp4_operand* a, const void* a16, const fp4_operand* b, const void* b16, float* c,
+                        int32_t hadamard_n, int32_t canon, void* stream);
 
 /*
  * fp4_scale_range - d_range[0] = smallest and d_range[1] = largest scale code of operand a
