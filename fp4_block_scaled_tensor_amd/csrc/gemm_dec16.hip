@@ -340,35 +340,41 @@ hipError_t run_decode_f16(const GemmOperand& a, int fmt, int block, int64_t K, v
 // global memory into a double-buffered LDS tile with global_load_lds (the same chunk swizzle:
 // chunk c of row r at c ^ ((r >> 1) & 7)); the next group's copy is in flight during the
 // current group's MFMAs and additions. Same MFMAs, additions, rounding modes and epilogue.
+#ifndef FP4_F16_TILING
+#define FP4_F16_TILING 2, 2, 2, 2
+#endif
+using F16Tiling = Tiling<FP4_F16_TILING>;   // waves of 64 x 64 (TM = TN = 2)
+
 template <int B, bool INTERIOR>
-__global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_f16(const uint8_t* __restrict__ a16,
+__global__ __launch_bounds__(F16Tiling::NT, 512 / F16Tiling::NT) void k_gemm_f16(const uint8_t* __restrict__ a16,
                                                      const uint8_t* __restrict__ b16,
                                                      const float* __restrict__ ga, const float* __restrict__ gb,
                                                      float* __restrict__ c, int64_t M, int64_t N, int64_t K,
                                                      int canon, int epi) {
-  using TL = DecTiling;
-  constexpr int GT = TL::BM;
+  using TL = F16Tiling;
+  static_assert(TL::TM == 2 && TL::TN == 2, "waves of 64 x 64");
   constexpr int DROW = 64 * 2;               // fp16 bytes per row and group (one stage)
-  constexpr int DBUF = 2 * GT * DROW;        // one buffer: A rows then B rows (32 KB)
+  constexpr int DBUF = (TL::BM + TL::BN) * DROW;   // one buffer: A rows then B rows
   static_assert(DROW == ROWB, "one group of fp16 is one 128-byte stage row");
   __shared__ __attribute__((aligned(1024))) uint8_t lD[2 * DBUF];
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / TL::WN, wn = w % TL::WN;
   int64_t m0, n0;
   tile_coords(M, N, TL::BM, TL::BN, m0, n0);
   const int64_t ngroups = K / 64;
   const int half = l >> 5;
   // the loaders see rows of 2K bytes: 4K "FP4 elements"
-  StageLoader<GT, TL::NW> LA, LB;
+  StageLoader<TL::BM, TL::NW> LA;
+  StageLoader<TL::BN, TL::NW> LB;
   LA.init(a16, M, 4 * K, m0);
   LB.init(b16, N, 4 * K, n0);
   auto issue = [&](int64_t gi, int buf) {
     if (INTERIOR) {
       LA.issue_interior(gi, lD + buf * DBUF);
-      LB.issue_interior(gi, lD + buf * DBUF + GT * DROW);
+      LB.issue_interior(gi, lD + buf * DBUF + TL::BM * DROW);
     } else {
       LA.issue(gi, lD + buf * DBUF);
-      LB.issue(gi, lD + buf * DBUF + GT * DROW);
+      LB.issue(gi, lD + buf * DBUF + TL::BM * DROW);
     }
   };
   uint32_t ra[4], rb[4];
@@ -376,7 +382,7 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_f16(const uint8_t* __
   for (int sub = 0; sub < 4; ++sub) {
     const uint32_t pos = (uint32_t)((2 * sub + half) ^ ((l >> 1) & 7)) << 4;
     ra[sub] = (uint32_t)((wm * 64 + (l & 31)) * DROW) + pos;
-    rb[sub] = (uint32_t)((GT + wn * 64 + (l & 31)) * DROW) + pos;
+    rb[sub] = (uint32_t)((TL::BM + wn * 64 + (l & 31)) * DROW) + pos;
   }
   v16f acc[2][2];
 #pragma unroll
@@ -436,7 +442,7 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_f16(const uint8_t* __
 
 template <int B>
 static hipError_t launch_f16(const GemmArgs& g) {
-  using TL = DecTiling;
+  using TL = F16Tiling;
   const int64_t tiles = ((g.M + TL::BM - 1) / TL::BM) * ((g.N + TL::BN - 1) / TL::BN);
   const bool interior = g.M % TL::BM == 0 && g.N % TL::BN == 0;
   auto kern = interior ? k_gemm_f16<B, true> : k_gemm_f16<B, false>;
