@@ -31,6 +31,8 @@
 // c ^ ((r >> 1) & 7): two rows share a 256-byte bank line, so sixteen consecutive rows cover
 // all 64 banks for both the row-wise writes and the fragment reads). The waves read their MFMA fragments from that tile; one barrier per
 // group hands the buffers over.
+#include <algorithm>
+
 #include "gemm_common.hpp"
 
 namespace fp4k {
@@ -293,35 +295,46 @@ __global__ __launch_bounds__(DecTiling::NT, 2) void k_gemm_dec16(const uint8_t* 
 // q S 2^-3 the per-tile decode above produces. A GEMM whose two operands come with this copy
 // reads it instead of decoding per workgroup (the per-tile decode costs more than a third
 // of that kernel's time; the copy costs 2 bytes per element written once and read by the
-// GEMM through L2). One thread per 64-element group of a row: 32 payload bytes, 4 slice
-// scales, 128 bytes out.
+// GEMM through L2). One thread per 8-element chunk of a row (a 4-byte payload word, its
+// slice's scale code, 16 bytes out), so that a wave reads 256 and writes 1024 consecutive
+// bytes of a row; workgroups of 256 chunks, rows strided over the grid's y.
+template <int FMT>
+__device__ __forceinline__ DecScale dec_factors_nb(uint32_t c) {
+  // dec_factors_code without branches (lanes of one wave hold different codes)
+  constexpr int SUB_EXP = FMT == FMT_UE5M3 ? 17 : 9;
+  const uint32_t e = c >> 3, m = c & 7u;
+  DecScale d;
+  d.p2 = __uint_as_float(e != 0 ? (e + (uint32_t)(127 - ScaleFmt<FMT>::BIAS - 3)) << 23
+                                : (uint32_t)(127 - SUB_EXP - 3) << 23);
+  const uint32_t hs = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(float)m);   // exact
+  const uint32_t h = e != 0 ? (0x3C00u | (m << 7)) : hs;
+  d.m2 = __builtin_bit_cast(v2h, h | (h << 16));
+  return d;
+}
+
 template <int FMT, int B>
 __global__ __launch_bounds__(256) void k_decode_f16(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
                                                     int layout, int64_t rows, int64_t K, bool al,
                                                     _Float16* __restrict__ out) {
-  const int64_t ng = K / 64;
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (id >= rows * ng) return;
-  const int64_t row = id / ng, gi = id - row * ng;
-  const uint4* p = reinterpret_cast<const uint4*>(q + row * (K / 2) + gi * 32);
-  const uint4 p0 = p[0], p1 = p[1];
-  const uint32_t codes = group_codes<B>(s, layout, row, rows, K, gi, al);
-  const uint32_t words[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-  v8h* o = reinterpret_cast<v8h*>(out + row * K + gi * 64);
-#pragma unroll
-  for (int sub = 0; sub < 4; ++sub) {
-    const DecScale d = dec_factors_code<FMT>((codes >> (8 * sub)) & 0xFFu);
-    o[2 * sub] = decode8(words[2 * sub], d);
-    o[2 * sub + 1] = decode8(words[2 * sub + 1], d);
+  (void)al;
+  const int64_t nc = K / 8;
+  const int64_t kc = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (kc >= nc) return;
+  const int64_t k16 = K / 16, slice = kc >> 1;
+  for (int64_t row = blockIdx.y; row < rows; row += gridDim.y) {
+    const uint32_t word = *reinterpret_cast<const uint32_t*>(q + row * (K / 2) + kc * 4);
+    uint32_t code;
+    if (layout == 2) code = s[slice * (rows >> 4) + (row >> 4)];
+    else if (layout == 1) code = s[(row >> 4) * k16 + slice];
+    else code = s[row * (K / B) + (B == 16 ? slice : slice >> 1)];
+    *reinterpret_cast<v8h*>(out + row * K + kc * 8) = decode8(word, dec_factors_nb<FMT>(code));
   }
 }
 
 template <int FMT, int B>
 static hipError_t launch_decode_f16(const GemmOperand& a, int64_t K, void* out, hipStream_t stream) {
-  const int64_t n = a.rows * (K / 64);
-  const uintptr_t am = B == 32 ? 1 : 3;
-  hipLaunchKernelGGL((k_decode_f16<FMT, B>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a.q, a.s,
-                     a.layout, a.rows, K, (reinterpret_cast<uintptr_t>(a.s) & am) == 0,
+  const dim3 grid((unsigned)((K / 8 + 255) / 256), (unsigned)std::min<int64_t>(a.rows, 65535));
+  hipLaunchKernelGGL((k_decode_f16<FMT, B>), grid, dim3(256), 0, stream, a.q, a.s, a.layout, a.rows, K, true,
                      reinterpret_cast<_Float16*>(out));
   return hipGetLastError();
 }
