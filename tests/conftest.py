@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    """GPU tests skip (not fail) where no GPU is visible; on a GPU machine a missing library
+    """GPU tests skip (not fail) where no GPU is visible; on a machine with a GPU a missing library
     makes them fail, because the FP4 path has no fallback."""
     try:
         import torch
