@@ -30,6 +30,8 @@
 // the two overlap only in part. The stage loop is therefore kept free of other vector
 // work: fragment addresses are one per-lane base XOR a group constant plus immediate
 // offsets, and the direct-to-LDS loads use a scalar base plus a per-lane offset.
+#include <type_traits>
+
 #include "gemm_common.hpp"
 
 namespace fp4k {
@@ -242,9 +244,12 @@ __global__ __launch_bounds__(TL::NT, FP4_MX_MINB) void k_gemm_mx(
   int64_t m0, n0;
   tile_coords(M, N, BM, BN, m0, n0);
   const int64_t nblk = K / 32;   // E8M0 scales per row
-  const int64_t ngroups = K / 64;
-  const int64_t nstages = (K + KS - 1) / KS;
-  const int64_t nfull = ngroups / SGR;   // stages with 4 groups
+  // Stage and group counters (SI): 32-bit in the interior kernel, whose stage loop is
+  // unrolled by two (their compares then stay on the scalar unit); 64-bit in the others.
+  using SI = typename std::conditional<INTERIOR && !QOUT, int, int64_t>::type;
+  const SI ngroups = (SI)(K / 64);
+  const SI nstages = (SI)((K + KS - 1) / KS);
+  const SI nfull = ngroups / SGR;   // stages with 4 groups
   const int half = l >> 5;
   const int ra0 = wm * (TM * 32) + (l & 31), rb0 = wn * (TN * 32) + (l & 31);
   const uint32_t La = frag_lane_base(wm * (TM * 32), l), Lb = frag_lane_base(wn * (TN * 32), l);
@@ -259,10 +264,10 @@ __global__ __launch_bounds__(TL::NT, FP4_MX_MINB) void k_gemm_mx(
   if (t < BM) SS.init(sa, m0 + t, M, nblk);
   else SS.init(sb, n0 + t - BM, N, nblk);
   uint4 sraw = make_uint4(0, 0, 0, 0);   // the next stage's scale bytes, in flight during a stage
-  auto load_scales = [&](int64_t st) {
+  auto load_scales = [&](SI st) {
     if (stager) sraw = INTERIOR ? SS.load8(st) : SS.load(st);
   };
-  auto issue_stage = [&](int64_t st, int buf) {
+  auto issue_stage = [&](SI st, int buf) {
     if (INTERIOR) {
       LA.issue_interior(st, sm.a[buf]);
       LB.issue_interior(st, sm.b[buf]);
@@ -325,9 +330,11 @@ __global__ __launch_bounds__(TL::NT, FP4_MX_MINB) void k_gemm_mx(
     for (int j = 0; j < TN; ++j) pin(acc[i][j]);   // additions after the switch
 
   // A full stage whose every group passes: one MFMA per group partial. Returns false, having
-  // done nothing, when the stage fails the test.
-  auto fast_step = [&](int64_t st) -> bool {
-    const int buf = (int)(st & 1);
+  // done nothing, when the stage fails the test. The stage's buffer (st & 1) is passed either
+  // as a compile-time constant (an std::integral_constant), which turns every LDS address of
+  // the stage into a per-lane base plus an immediate offset, or as a run-time int.
+  auto fast_step = [&](auto bufc, SI st) -> bool {
+    const int buf = (int)bufc;
     if (!stage_passes(buf)) return false;
     const bool more = st + 1 < nstages;
     if (more) issue_stage(st + 1, buf ^ 1);
@@ -345,11 +352,28 @@ __global__ __launch_bounds__(TL::NT, FP4_MX_MINB) void k_gemm_mx(
     return true;
   };
 
-  int64_t st = 0;
+  SI st = 0;
   for (;;) {
     // full stages that pass
-    for (; st < nfull; ++st) {
-      if (!fast_step(st)) break;
+    if constexpr (INTERIOR && !QOUT) {
+      // in pairs (even, odd) after re-aligning on an even stage, both buffers compile-time.
+      // The edge and output-quantizing kernels keep one stage per iteration: the longer loop
+      // body costs them more in register spills than it saves.
+      constexpr std::integral_constant<int, 0> B0{};
+      constexpr std::integral_constant<int, 1> B1{};
+      if ((st & 1) && st < nfull && fast_step(B1, st)) ++st;
+      if (!(st & 1)) {
+        while (st < nfull) {
+          if (!fast_step(B0, st)) break;
+          ++st;
+          if (st >= nfull || !fast_step(B1, st)) break;
+          ++st;
+        }
+      }
+    } else {
+      for (; st < nfull; ++st) {
+        if (!fast_step((int)(st & 1), st)) break;
+      }
     }
     if (st >= nstages) break;
     // one stage that failed the test (or the partial last stage): each group tested on its
@@ -362,7 +386,7 @@ __global__ __launch_bounds__(TL::NT, FP4_MX_MINB) void k_gemm_mx(
     for (int i = 0; i < TM; ++i) s4a[i] = sm.sw[buf][half][ra0 + i * 32];
 #pragma unroll
     for (int j = 0; j < TN; ++j) s4b[j] = sm.sw[buf][half][BM + rb0 + j * 32];
-    const int g_end = (int)((ngroups - st * SGR) < SGR ? (ngroups - st * SGR) : SGR);
+    const int g_end = (int)((ngroups - st * SGR) < SGR ? (ngroups - st * SGR) : (SI)SGR);
     plain_stage<TM, TN>(sm.a[buf], sm.b[buf], La, Lb, s4a, s4b, true, g_end, &sm.sw[buf][0][0], NR, ra0, rb0, BM,
                         half, acc);
     if (more) {
