@@ -263,3 +263,53 @@ def test_exact_range_edges_match_the_oracle_contract():
                 assert not np.isfinite(oracle.gemm_model(q6, sa, q6, sb, 32)).any()
     tiny = lambda e: 0.25 * 2.0 ** e
     assert tiny(-124) == 2.0 ** -126 and tiny(-125) < 2.0 ** -126
+
+
+def test_quantized_output_gemms_reject_bad_arguments(lib):
+    """fp4_gemm_fprop_q / fp4_gemm_dgrad_q: every argument error returns its status before
+    anything is launched (no GPU here)."""
+    P = ctypes.c_void_p
+    y, q, s, g, amax = P(4096), P(8192), P(12288), P(16384), P(20480)
+
+    def cfg(fmt=0, block=16, view=0, sr=0, hn=0, T=448.0):
+        return _lib.QuantCfg(fmt, block, view, sr, hn, T, 0, 0)
+
+    def call(name, a, b, c, amx=amax, qq=q, ss=s, yy=y):
+        return getattr(lib, name)(ctypes.byref(a), ctypes.byref(b), yy, 0, ctypes.byref(c), amx, qq, ss, g, None,
+                                  None, None)
+    a, b = op(), op()
+    for name in ("fp4_gemm_fprop_q", "fp4_gemm_dgrad_q"):
+        assert call(name, a, b, cfg(view=1)) == _lib.FP4_EUNSUPPORTED                  # COL view of C
+        assert call(name, a, b, cfg(hn=16)) == _lib.FP4_EUNSUPPORTED                  # rotation
+        assert call(name, a, b, cfg(block=8)) != _lib.FP4_OK                          # bad block
+        assert call(name, a, b, cfg(), qq=None) == _lib.FP4_EINVAL                    # NULL payload
+        assert call(name, a, b, cfg(), ss=None) == _lib.FP4_EINVAL                    # NULL scales
+        assert call(name, a, b, cfg(), qq=P(4100)) == _lib.FP4_EALIGN                 # payload alignment
+        assert call(name, a, b, cfg(), amx=None) == _lib.FP4_EINVAL                   # UE5M3 without amax
+        assert call(name, a, op(rows=72), cfg()) == _lib.FP4_EINVAL                   # N % 16
+        assert call(name, op(k=0), op(k=0), cfg()) == _lib.FP4_EUNSUPPORTED           # K = 0
+        assert call(name, a, op(k=192), cfg()) == _lib.FP4_EINVAL                     # K mismatch
+    assert call("fp4_gemm_dgrad_q", a, op(layout=1), cfg()) == _lib.FP4_EUNSUPPORTED  # weight's forward view
+    assert call("fp4_gemm_fprop_q", a, op(layout=2), cfg()) == _lib.FP4_EUNSUPPORTED  # weight's dgrad view
+
+
+def test_decode_once_entry_points_reject_bad_arguments(lib):
+    """fp4_decode_f16 / fp4_gemm_f16: argument errors return before any launch."""
+    P = ctypes.c_void_p
+    out, a16, b16, c = P(4096), P(8192), P(12288), P(16384)
+    mx = op(fmt=2, block=32)
+    assert lib.fp4_decode_f16(ctypes.byref(mx), out, None) == _lib.FP4_EUNSUPPORTED      # MXFP4 runs natively
+    assert lib.fp4_decode_f16(ctypes.byref(op()), None, None) == _lib.FP4_EINVAL
+    assert lib.fp4_decode_f16(ctypes.byref(op()), P(4104), None) == _lib.FP4_EALIGN
+    assert lib.fp4_decode_f16(None, out, None) == _lib.FP4_EINVAL
+    assert lib.fp4_decode_f16(ctypes.byref(op(k=96)), out, None) == _lib.FP4_EINVAL      # K % 64
+    a, b = op(), op()
+    f = lib.fp4_gemm_f16
+    assert f(ctypes.byref(mx), a16, ctypes.byref(op(fmt=2, block=32)), b16, c, 0, 0, None) == _lib.FP4_EUNSUPPORTED
+    assert f(ctypes.byref(a), None, ctypes.byref(b), b16, c, 0, 0, None) == _lib.FP4_EINVAL
+    assert f(ctypes.byref(a), a16, ctypes.byref(b), P(12296), c, 0, 0, None) == _lib.FP4_EALIGN
+    assert f(ctypes.byref(a), a16, ctypes.byref(b), b16, c, 8, 0, None) == _lib.FP4_EINVAL
+    assert f(ctypes.byref(a), a16, ctypes.byref(op(k=192)), b16, c, 0, 0, None) == _lib.FP4_EINVAL
+    assert f(ctypes.byref(a), a16, ctypes.byref(b), b16, None, 0, 0, None) == _lib.FP4_EINVAL
+    assert f(ctypes.byref(a), a16, ctypes.byref(b), b16, c, 0, 2, None) == _lib.FP4_EINVAL   # canon 0/1
+    assert f(ctypes.byref(op(rows=0)), None, ctypes.byref(b), None, None, 0, 0, None) == _lib.FP4_OK   # empty: no-op
