@@ -113,10 +113,14 @@ __device__ __forceinline__ uint32_t e2m1_sr(float r, uint32_t u16) {
   const float a = fminf(fabsf(r), 6.0f);
   const int k = min(max(__builtin_amdgcn_frexp_expf(a), 1), 3);
   const float t = __builtin_amdgcn_ldexpf(a, 2 - k);
-  const float frac = __builtin_amdgcn_fractf(t);
-  const uint32_t up = (float)u16 < frac * 65536.0f ? 1u : 0u;
+  // floor(t) + up = ceil(t - u16 / 2^16): t - u16 / 2^16 lies in (floor(t) - 1, floor(t) + 1) and
+  // exceeds floor(t) exactly when u16 < 2^16 frac(t). The fused multiply-add rounds once: for
+  // t >= 1 the difference is a multiple of t's quantum below 4, hence exact; for t < 1 only its
+  // sign matters, which rounding keeps.
+  const float v = __builtin_fmaf((float)u16, -1.0f / 65536.0f, t);
+  const uint32_t c = (uint32_t)__builtin_ceilf(v);
   const uint32_t sign = (__float_as_uint(r) >> 28) & 8u;
-  return sign | ((uint32_t)t + 2u * (uint32_t)k - 2u + up);
+  return sign | (c + 2u * (uint32_t)k - 2u);
 }
 
 // ---- Philox-4x32-10 (Salmon et al., SC'11) ----
@@ -131,6 +135,9 @@ __device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t k) {
 }
 
 __device__ __forceinline__ u4 philox4x32_10(u4 c, uint32_t k0, uint32_t k1) {
+  // the round keys are formed here on the scalar unit: hoisted out of the callers' loops, the
+  // twenty of each key schedule would be spilled to vector lanes and read back with v_readlane
+  asm volatile("" : "+s"(k0), "+s"(k1));
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r > 0) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }

@@ -79,6 +79,30 @@ def test_stochastic_e2m1():
     assert np.array_equal(_run(r, 4, u), sr_e2m1(r, u))
 
 
+def test_stochastic_e2m1_decision_boundaries():
+    """The rule rounds up iff the draw u < 2^16 f (strict), f the value's fraction within its
+    codebook interval. Values whose f is exactly k/2^16, one float step above or below that,
+    drawn against u = k - 1, k, k + 1, in every interval and with both signs; and the tiniest
+    magnitudes (f = 2|r|, down to the smallest subnormal) against u = 0, 1, 2, 65535."""
+    rng = np.random.default_rng(7)
+    rs, us = [], []
+    for lo, hi in ((0.0, 0.5), (0.5, 1.0), (1.0, 1.5), (1.5, 2.0), (2.0, 3.0), (3.0, 4.0), (4.0, 6.0)):
+        for k in rng.integers(1, 65535, 256):
+            a = np.float32(lo + (hi - lo) * (int(k) / 65536.0))          # exact: f = k / 2^16
+            for aa in (a, np.nextafter(a, np.float32(np.inf)), np.nextafter(a, np.float32(-np.inf))):
+                for d in (k - 1, k, k + 1):
+                    rs += [aa, -aa]
+                    us += [d, d]
+    for e in range(14, 150):
+        t = np.float32(2.0 ** -e)
+        for d in (0, 1, 2, 65535):
+            rs += [t, -t]
+            us += [d, d]
+    r = np.array(rs, np.float32)
+    u = np.array(us, np.uint16)
+    assert np.array_equal(_run(r, 4, u), sr_e2m1(r, u))
+
+
 def _oracle_code(x: np.ndarray, which: int) -> np.ndarray:
     x = np.asarray(x, np.float32)
     if which == 3:
