@@ -26,10 +26,11 @@
 // stage test (outlier channels fail only the stages that hold them).
 //
 // The per-group float32 add bounds this kernel: 16 v_add_f32 per lane per 32x32x64 MFMA,
-// which the vector ALU issues in about the time the matrix core takes for the MFMA, and
-// the two overlap only in part. The stage loop is therefore kept free of other vector
-// work: fragment addresses are one per-lane base XOR a group constant plus immediate
-// offsets, and the direct-to-LDS loads use a scalar base plus a per-lane offset.
+// which take the vector ALU about twice as long as the matrix core takes for the MFMA, and
+// the two pipes do not overlap. The stage loop is therefore kept free of other vector work:
+// fragment addresses are a per-lane base plus immediate offsets (the interior kernel runs
+// its passing stages in even/odd pairs, so that both LDS buffers are compile-time
+// constants), and the direct-to-LDS loads use a scalar base plus a per-lane offset.
 #include <type_traits>
 
 #include "gemm_common.hpp"
