@@ -71,6 +71,28 @@ def test_mxfp4_outlier_blocks_then_fast_stages(M, N, K):
     assert_f32_bits_equal(got, want, f"outlier blocks {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K,bad", [
+    (128, 256, 256, []), (128, 256, 256, [0]), (128, 128, 768, [1]), (128, 128, 768, [0, 2]),
+    (256, 128, 1280, [1, 2]), (128, 256, 2048, [0, 3, 4, 7]), (128, 128, 2048, [6, 7]),
+    (200, 136, 1344, [0, 5])])
+def test_mxfp4_failing_stages_at_chosen_positions(M, N, K, bad):
+    """The fast stage loop runs passing 256-K stages two at a time (even, odd); a failing
+    stage runs group by group and the loop re-aligns on the next even stage. Stages made to
+    fail at chosen positions (first, last, even, odd, consecutive; one-stage and odd stage
+    counts; a partial last stage and a ragged tile in the last case): one group of each bad
+    stage has a block of A raised by 2^12, past the exponent-gap bound."""
+    rng = np.random.default_rng(M * 3 + N + K + len(bad))
+    qa = random_operand(rng, M, K, OF.E8M0, 32, 1)
+    qb = random_operand(rng, N, K, OF.E8M0, 32, 1)
+    for st in bad:
+        blk = 8 * st + 2 * int(rng.integers(0, min(4, K // 64 - 4 * st)))   # K-block 0 of one of its groups
+        qa.scales[:, blk] = (qa.scales[:, blk].astype(np.int32) + 12).astype(np.uint8)
+    want = _oracle_y(qa, qb)
+    got = fp4.gemm_fprop(qtensor_from_oracle(qa), qtensor_from_oracle(qb))
+    torch.cuda.synchronize()
+    assert_f32_bits_equal(got, want, f"failing stages {bad} {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("fmt,block", [(OF.UE5M3, 16), (OF.E8M0, 32)])
 def test_empty_k_writes_zeros(fmt, block):
     """K = 0: every output is an empty sum, +0 (the output buffer starts non-zero)."""
