@@ -50,7 +50,7 @@ GEMM_SOURCES = {"mxfp4": ["gemm_mx.hip", "gemm_common.hpp", "fp4_device.hpp"],
                 "ue5m3": ["gemm_dec16.hip", "gemm_common.hpp", "fp4_device.hpp"],
                 "e4m3": ["gemm_dec16.hip", "gemm_common.hpp", "fp4_device.hpp"]}
 GEMM_KERNEL = {"mxfp4": "k_gemm_mx", "ue5m3": "k_gemm_dec16", "e4m3": "k_gemm_dec16"}
-GEMM_KERNEL_PRE = "k_gemm_f16"   # --predecode (UE5M3/E4M3)
+GEMM_KERNEL_PRE = "k_gemm_f16_w8"   # --predecode (UE5M3/E4M3 block 16)
 
 
 def log(msg):
@@ -331,7 +331,7 @@ def routes(torch, fp4, Xd, Wd, dYd, args, skip):
         ms_step, gemm_ms = time_step(torch, st, 3, 10)
         tf = flop_gemm / (gemm_ms * 1e-3) / 1e12
         out[route] = {"ms_per_step": round(ms_step, 4), "step_TFLOPs": round(3 * flop_gemm / (ms_step * 1e-3) / 1e12, 1),
-                     "gemm_kernel": "k_gemm_f16" if pre else GEMM_KERNEL[name], "gemm_avg_ms": round(gemm_ms, 4),
+                     "gemm_kernel": GEMM_KERNEL_PRE if pre else GEMM_KERNEL[name], "gemm_avg_ms": round(gemm_ms, 4),
                      "decode_pair_avg_ms": round(float(np.mean([a.elapsed_time(b) for a, b in st.evd])), 4) if pre
                      else None,
                      "gemm_TFLOPs": round(tf, 1), "frac_of_fp4_peak": round(tf / FP4_PEAK_TFLOPS, 4),

@@ -353,6 +353,8 @@ hipError_t run_decode_f16(const GemmOperand& a, int fmt, int block, int64_t K, v
 // global memory into a double-buffered LDS tile with global_load_lds (the same chunk swizzle:
 // chunk c of row r at c ^ ((r >> 1) & 7)); the next group's copy is in flight during the
 // current group's MFMAs and additions. Same MFMAs, additions, rounding modes and epilogue.
+// This form (four waves of 64 x 64, two waves per SIMD) serves block 32; block 16 runs
+// k_gemm_f16_w8 below.
 #ifndef FP4_F16_TILING
 #define FP4_F16_TILING 2, 2, 2, 2
 #endif
@@ -453,8 +455,114 @@ __global__ __launch_bounds__(F16Tiling::NT, 512 / F16Tiling::NT) void k_gemm_f16
   store_tiles<2, 2>(c, M, N, m0 + wm * 64, n0 + wn * 64, acc, ga, gb, canon, epi, 64.0f);   // undo 2^-3 x 2^-3
 }
 
+// Block 16 at four waves per SIMD: 128 x 128 workgroup tiles of 8 waves of 32 x 64 (two
+// 32x32 output tiles per wave sharing each A fragment). Each 16-wide slice's fragments are
+// read just before its MFMAs and each tile's group partial is accumulated slice by slice,
+// ((T0 + T1) + T2) + T3 in K order with nearest-even adds, so that the kernel fits in 128
+// VGPRs. Same staging, swizzle, rounding modes and epilogue as k_gemm_f16.
+using F16TilingW8 = Tiling<4, 2, 1, 2>;
+
+template <bool INTERIOR>
+__global__ __launch_bounds__(F16TilingW8::NT, 4) void k_gemm_f16_w8(const uint8_t* __restrict__ a16,
+                                                                const uint8_t* __restrict__ b16,
+                                                                const float* __restrict__ ga,
+                                                                const float* __restrict__ gb, float* __restrict__ c,
+                                                                int64_t M, int64_t N, int64_t K, int canon, int epi) {
+  using TL = F16TilingW8;
+  constexpr int DROW = 64 * 2;
+  constexpr int DBUF = (TL::BM + TL::BN) * DROW;
+  __shared__ __attribute__((aligned(1024))) uint8_t lD[2 * DBUF];
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w / TL::WN, wn = w % TL::WN;
+  int64_t m0, n0;
+  tile_coords(M, N, TL::BM, TL::BN, m0, n0);
+  const int64_t ngroups = K / 64;
+  const int half = l >> 5;
+  StageLoader<TL::BM, TL::NW> LA;
+  StageLoader<TL::BN, TL::NW> LB;
+  LA.init(a16, M, 4 * K, m0);
+  LB.init(b16, N, 4 * K, n0);
+  auto issue = [&](int64_t gi, int buf) {
+    if (INTERIOR) {
+      LA.issue_interior(gi, lD + buf * DBUF);
+      LB.issue_interior(gi, lD + buf * DBUF + TL::BM * DROW);
+    } else {
+      LA.issue(gi, lD + buf * DBUF);
+      LB.issue(gi, lD + buf * DBUF + TL::BM * DROW);
+    }
+  };
+  uint32_t ra[4], rb[4];
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub) {
+    const uint32_t pos = (uint32_t)((2 * sub + half) ^ ((l >> 1) & 7)) << 4;
+    ra[sub] = (uint32_t)((wm * 32 + (l & 31)) * DROW) + pos;
+    rb[sub] = (uint32_t)((TL::BM + wn * 64 + (l & 31)) * DROW) + pos;
+  }
+  v16f acc[1][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[0][j][r] = 0.0f;
+  if (ngroups > 0) issue(0, 0);
+  wait_vm();
+  __syncthreads();
+  for (int64_t gi = 0; gi < ngroups; ++gi) {
+    const int buf = (int)(gi & 1);
+    if (gi + 1 < ngroups) issue(gi + 1, buf ^ 1);
+    const uint8_t* D = lD + buf * DBUF;
+    v16f G[2];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      const v8h fa = *reinterpret_cast<const v8h*>(D + ra[sub]);
+      const v8h fb0 = *reinterpret_cast<const v8h*>(D + rb[sub]);
+      const v8h fb1 = *reinterpret_cast<const v8h*>(D + rb[sub] + 32 * DROW);
+      v16f T0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, fb0, v16f{}, 0, 0, 0);
+      v16f T1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, fb1, v16f{}, 0, 0, 0);
+      pin(T0);
+      pin(T1);
+      if (sub == 0) {
+        G[0] = T0;
+        G[1] = T1;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          G[0][r] = G[0][r] + T0[r];   // nearest-even (the loop's mode), in K order
+          G[1][r] = G[1][r] + T1[r];
+        }
+      }
+    }
+    pin(G[0]);
+    pin(G[1]);
+    mode_f32_rtz();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      pin(G[j]);
+      pin(acc[0][j]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[0][j][r] = acc[0][j][r] + G[j][r];
+      pin(acc[0][j]);
+    }
+    mode_f32_rne();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) pin(acc[0][j]);
+    wait_vm();
+    __syncthreads();
+  }
+  store_tiles<1, 2>(c, M, N, m0 + wm * 32, n0 + wn * 64, acc, ga, gb, canon, epi, 64.0f);   // undo 2^-3 x 2^-3
+}
+
 template <int B>
 static hipError_t launch_f16(const GemmArgs& g) {
+  if constexpr (B == 16) {
+    using TW = F16TilingW8;
+    const int64_t tw = ((g.M + TW::BM - 1) / TW::BM) * ((g.N + TW::BN - 1) / TW::BN);
+    const bool inter = g.M % TW::BM == 0 && g.N % TW::BN == 0;
+    auto kw = inter ? k_gemm_f16_w8<true> : k_gemm_f16_w8<false>;
+    hipLaunchKernelGGL(kw, dim3((unsigned)tw), dim3(TW::NT), 0, g.stream, reinterpret_cast<const uint8_t*>(g.a16),
+                       reinterpret_cast<const uint8_t*>(g.b16), g.a.g, g.b.g, g.c, g.M, g.N, g.K, g.canon,
+                       epilogue_word(g.hadamard_n, g.a.g_shift, g.b.g_shift));
+    return hipGetLastError();
+  }
   using TL = F16Tiling;
   const int64_t tiles = ((g.M + TL::BM - 1) / TL::BM) * ((g.N + TL::BN - 1) / TL::BN);
   const bool interior = g.M % TL::BM == 0 && g.N % TL::BN == 0;
