@@ -103,24 +103,38 @@ __device__ __forceinline__ uint32_t e2m1_pack8(const float* r) {
 
 // ---- stochastic E2M1 ----
 // With lo <= |r| < hi the neighbouring codebook values, round up iff u16 < 65536 (|r| - lo) /
-// (hi - lo); |r| >= 6 gives 6. Branch-free form: with a = min(|r|, 6) and k the binary
-// exponent of a clamped to [1, 3] (frexp convention, so a in [2, 4) has k = 2 and a in
-// [4, 6] has k = 3), t = a 2^(2-k) is exact and lies in [0, 4). Below 2, t = 2a and floor(t)
-// is the code of lo; in [2, 4) t = a and in [4, 6] t = a / 2, and floor(t) is 2 below that
-// code. So code = floor(t) + 2 (k - 1) + up, where frac(t) = (|r| - lo) / (hi - lo) exactly.
-// a = 6 (any |r| >= 6) gives k = 3, t = 3, frac 0: code 7.
-__device__ __forceinline__ uint32_t e2m1_sr(float r, uint32_t u16) {
-  const float a = fminf(fabsf(r), 6.0f);
-  const int k = min(max(__builtin_amdgcn_frexp_expf(a), 1), 3);
-  const float t = __builtin_amdgcn_ldexpf(a, 2 - k);
-  // floor(t) + up = ceil(t - u16 / 2^16): t - u16 / 2^16 lies in (floor(t) - 1, floor(t) + 1) and
-  // exceeds floor(t) exactly when u16 < 2^16 frac(t). The fused multiply-add rounds once: for
-  // t >= 1 the difference is a multiple of t's quantum below 4, hence exact; for t < 1 only its
-  // sign matters, which rounding keeps.
+// (hi - lo); |r| >= 6 gives 6. Branch-free form: the codebook spacing around |r| is h = 1/2 below
+// 2, 1 in [2, 4) and 2 from 4 on, so 2h = min(max(P, 1), 4) with P = 2^floor(log2 |r|) (the
+// exponent bits of r alone: 0 for zero and subnormals). t = |r| / h is exact, floor(t) h = lo
+// and frac(t) = (|r| - lo) / h. Then floor(t) + up = ceil(t - u16 / 2^16): t - u16 / 2^16 lies in
+// (floor(t) - 1, floor(t) + 1) and exceeds floor(t) exactly when u16 < 2^16 frac(t). The fused
+// multiply-add rounds once: for t >= 1 the difference is a multiple of t's quantum below 4,
+// hence exact; for t < 1 only its sign matters, which rounding keeps.
+// Returns twice the selected codebook value, (floor(t) + up) 2h, with the sign of r: the
+// encoder below halves it exactly (its scale operand 2.0 divides) and maps it to its own code.
+// |r| >= 6 gives 12 or more, which the encoder saturates to 6; so do infinities, and a NaN
+// (whose 2h is 4) encodes as 6 with its sign, the same as min(|r|, 6) would give.
+__device__ __forceinline__ float e2m1_sr_twice(float r, uint32_t u16) {
+  const float h2 = __builtin_amdgcn_fmed3f(__uint_as_float(__float_as_uint(r) & 0x7F800000u), 1.0f, 4.0f);
+  const float t = fabsf(r) * __uint_as_float(0x7F800000u - __float_as_uint(h2));   // |r| 2 / h2, exact
   const float v = __builtin_fmaf((float)u16, -1.0f / 65536.0f, t);
-  const uint32_t c = (uint32_t)__builtin_ceilf(v);
-  const uint32_t sign = (__float_as_uint(r) >> 28) & 8u;
-  return sign | (c + 2u * (uint32_t)k - 2u);
+  return __builtin_copysignf(__builtin_ceilf(v) * h2, r);
+}
+
+// two values from e2m1_sr_twice -> two codes in byte SEL of old (src0 in the low nibble)
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_sr_pack2(uint32_t old, float a2, float b2) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a2, b2, 2.0f, SEL);
+}
+
+// 8 values with their 16-bit draws -> one dword of 8 stochastically rounded codes
+__device__ __forceinline__ uint32_t e2m1_sr_pack8(const float* r, const uint32_t* u) {
+  uint32_t w = 0;
+  w = e2m1_sr_pack2<0>(w, e2m1_sr_twice(r[0], u[0]), e2m1_sr_twice(r[1], u[1]));
+  w = e2m1_sr_pack2<1>(w, e2m1_sr_twice(r[2], u[2]), e2m1_sr_twice(r[3], u[3]));
+  w = e2m1_sr_pack2<2>(w, e2m1_sr_twice(r[4], u[4]), e2m1_sr_twice(r[5], u[5]));
+  w = e2m1_sr_pack2<3>(w, e2m1_sr_twice(r[6], u[6]), e2m1_sr_twice(r[7], u[7]));
+  return w;
 }
 
 // ---- Philox-4x32-10 (Salmon et al., SC'11) ----

@@ -968,7 +968,7 @@ __global__ void k_debug_encode(const float* __restrict__ x, const uint16_t* __re
   else if (which == 1) c = enc_scale3<FMT_UE5M3>(v);
   else if (which == 2) c = enc_scale3<FMT_E4M3>(v);
   else if (which == 3) c = e8m0_code(v);
-  else c = e2m1_sr(v, u16[i]);
+  else c = e2m1_sr_pack2<0>(0u, e2m1_sr_twice(v, u16[i]), 0.0f) & 15u;
   out[i] = (uint8_t)c;
 }
 

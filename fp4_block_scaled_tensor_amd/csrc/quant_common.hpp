@@ -152,10 +152,7 @@ __device__ __forceinline__ void payload(const float* v, float mult, uint64_t i0,
     if constexpr (SR) {
       uint32_t u[8];
       philox_u16x8((i0 >> 3) + w, seed, offset, u);
-      uint32_t word = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) word |= e2m1_sr(r[j], u[j]) << (4 * j);
-      words[w] = word;
+      words[w] = e2m1_sr_pack8(r, u);
     } else {
       words[w] = e2m1_pack8(r);
     }

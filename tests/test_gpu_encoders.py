@@ -103,6 +103,19 @@ def test_stochastic_e2m1_decision_boundaries():
     assert np.array_equal(_run(r, 4, u), sr_e2m1(r, u))
 
 
+def test_stochastic_e2m1_saturation_and_specials():
+    """Magnitudes from 6 up (where the rule gives 6 whatever the draw), the largest float,
+    infinities and NaNs of both signs, zeros and the codebook's top interval, each against
+    the draws 0, 1, 2^15 and 65535."""
+    big = np.array([6.0, np.nextafter(np.float32(6.0), np.float32(np.inf)), 6.5, 7.0, 7.999, 8.0, 11.0, 12.0, 16.0,
+                    1e4, 1e30, 3.4028235e38, np.inf, np.nan, 0.0, 4.0, 5.0, 5.999,
+                    np.nextafter(np.float32(6.0), np.float32(0))], np.float32)
+    r = np.concatenate([big, -big]).astype(np.float32)
+    r = np.repeat(r, 4)
+    u = np.tile(np.array([0, 1, 1 << 15, 65535], np.uint16), r.size // 4)
+    assert np.array_equal(_run(r, 4, u), sr_e2m1(r, u))
+
+
 def _oracle_code(x: np.ndarray, which: int) -> np.ndarray:
     x = np.asarray(x, np.float32)
     if which == 3:
